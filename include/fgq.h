@@ -1,0 +1,186 @@
+/*
+ * fgq.h - C ABI of libfgq: 4-bit asymmetric group-wise (64 elements per
+ * group) compression of weights and KV cache, decode attention over the
+ * compressed cache, and the dequantising weight GEMM of a block of GPU
+ * batches, for AMD Instinct MI355X (gfx950).
+ *
+ * Method (pages on FlexGen, arXiv 2303.06865):
+ *  - FlexGen review on jaehun.me, section "Is 4-bit compression the same as
+ *    integer-arithmetic acceleration?" (paper section 5): weights and KV are
+ *    stored as 4-bit integers and restored to FP16 before compute; groups of
+ *    64 elements; weights grouped along the output channel, KV along the
+ *    hidden dimension; asymmetric, from the group's minimum a and maximum b;
+ *    a constant group needs separate handling.
+ *  - FlexGen review on blog.gzher.com, section 3.4: fine-grained group-wise
+ *    asymmetric quantisation of weights and KV cache, dequantised to FP16
+ *    before computation; the aim is less storage and traffic, not INT4 math.
+ *  - paper-graph-ui FlexGen summary, section 3.4 "Compute Schedule": a block
+ *    is (GPU batch size g) x (number of GPU batches m); one load of a layer's
+ *    weights serves every GPU batch of the block.
+ *
+ * Encoding (the formula is dropped from the pages; the plain min-max reading):
+ *   per group of 64 fp16 values x_i:  a = min x_i, b = max x_i (signed zeros
+ *   folded to +0); if a == b every code is 0 and the step is +0; otherwise
+ *   q_i = roundTiesToEven(((x_i - a) / (b - a)) * 15) clamped to [0, 15], each
+ *   operation a separate IEEE fp32 operation in that order; the group stores
+ *   min = fp16(a) and step = fp16_RNE(fp32((b - a) / 15)).
+ *   Reconstruction: x^ = min + q * step.
+ *
+ * Storage:
+ *   codes  uint8 [rows][cols/2]; byte j holds element 2j in its low nibble and
+ *          element 2j+1 in its high nibble.
+ *   meta   uint32 [rows][cols/64]; low 16 bits fp16 min, high 16 bits fp16 step
+ *          (a little-endian half2 {min, step}).
+ *   0.5625 bytes per element (4-bit code plus 4 bytes of metadata per 64).
+ *
+ * Conventions for every call:
+ *  - Every pointer is caller-owned device memory unless stated otherwise.
+ *    The library never allocates, frees or retains memory and never
+ *    synchronises; scratch space is a caller-provided workspace.
+ *  - Every array must be 16-byte aligned (FGQ_ERR_ALIGN otherwise).
+ *  - Calls are asynchronous and ordered on `stream` (a hipStream_t; NULL is
+ *    the default stream).
+ *  - Arguments are validated on the host before anything is enqueued; on any
+ *    error nothing is enqueued and outputs are untouched.  A failed launch
+ *    returns FGQ_ERR_DEVICE.  fgq_last_error() gives a text for the calling
+ *    thread's last failure.
+ *  - Inputs must be finite (precondition; the result is undefined otherwise).
+ *  - Calls are reentrant; the library holds no mutable global state besides
+ *    the per-thread error text.
+ */
+#ifndef FGQ_H
+#define FGQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FGQ_ABI_VERSION 1
+
+typedef int32_t fgq_status;
+#define FGQ_OK 0
+#define FGQ_ERR_INVALID_ARG -1  /* null pointer or negative size */
+#define FGQ_ERR_SHAPE -2        /* a size breaks a divisibility or range rule */
+#define FGQ_ERR_ALIGN -3        /* an array (or leading dimension) is not 16-byte aligned */
+#define FGQ_ERR_CAPACITY -4     /* KV positions beyond the cache capacity */
+#define FGQ_ERR_WORKSPACE -5    /* workspace missing or smaller than the size query */
+#define FGQ_ERR_DTYPE -6        /* unknown output dtype */
+#define FGQ_ERR_DEVICE -7       /* the HIP runtime rejected a launch */
+#define FGQ_ERR_UNSUPPORTED -8  /* valid but not implemented (e.g. head_dim not 64 or 128) */
+
+/* Output element types. */
+#define FGQ_DTYPE_F32 0
+#define FGQ_DTYPE_F16 1
+
+int32_t fgq_abi_version(void);
+const char *fgq_status_string(fgq_status s);
+/* Text describing the calling thread's most recent failure ("" if none). */
+const char *fgq_last_error(void);
+
+/*
+ * fgq_quantize_g64 - compress an fp16 matrix, groups of 64 along its rows.
+ *   x      fp16 [rows][ld_x], the first `cols` columns are read.
+ *   codes  uint8 [rows][cols/2] out;  meta uint32 [rows][cols/64] out.
+ * For a weight W [K = in][N = out] pass rows=K, cols=N: each group is 64
+ * consecutive output channels at one input index.  For KV rows pass
+ * [tokens][hidden]: each group is 64 consecutive hidden elements.
+ * Requires cols % 64 == 0 and ld_x % 8 == 0, ld_x >= cols.  rows == 0 is a no-op.
+ * Codes and meta equal, bit for bit, the encoding defined above.
+ */
+fgq_status fgq_quantize_g64(const void *x_f16, int64_t rows, int64_t cols, int64_t ld_x,
+                            uint8_t *codes, uint32_t *meta, void *stream);
+
+/*
+ * Compressed KV cache of one layer, head-major:
+ *   k_codes, v_codes  uint8  [batch][heads][capacity][head_dim/2]
+ *   k_meta,  v_meta   uint32 [batch][heads][capacity][head_dim/64]
+ * Groups run along the hidden dimension of one token's K (or V) row; with
+ * head_dim a multiple of 64 a group never straddles two heads.  The caller
+ * allocates the arrays; the library reads and writes them only in calls.
+ */
+typedef struct fgq_kv_cache {
+    uint8_t *k_codes;
+    uint8_t *v_codes;
+    uint32_t *k_meta;
+    uint32_t *v_meta;
+    int32_t batch;
+    int32_t heads;
+    int32_t head_dim;   /* 64 or 128 */
+    int32_t capacity;   /* positions per sequence */
+} fgq_kv_cache;
+
+/*
+ * fgq_kv_append - compress the K and V rows that a decode (or prompt) step
+ * produced and write them at positions [pos, pos + n_new) of every sequence
+ * (the cache persists and grows one token per decode step: paper-graph-ui
+ * FlexGen summary, section 3.4, graph-traversal formulation; FlexGen review on
+ * jaehun.me, "Is 4-bit compression ...": KV grouped along hidden).
+ *   k_new, v_new  fp16 [batch][n_new][heads*head_dim], token-major.
+ * Bit-exact with fgq_quantize_g64 on the same rows.  n_new == 0 or batch == 0
+ * is a no-op.  pos + n_new > capacity -> FGQ_ERR_CAPACITY.
+ */
+fgq_status fgq_kv_append(const fgq_kv_cache *kv, const void *k_new_f16, const void *v_new_f16,
+                         int32_t pos, int32_t n_new, void *stream);
+
+/*
+ * fgq_decode_attn_q4kv - one decode step of attention for every sequence over
+ * the compressed cache: for each (sequence, head)
+ *   s_j = softmax_scale * sum_d q_d * K^_{j,d},  j in [0, kv_len)
+ *   o_d = sum_j softmax(s)_j * V^_{j,d}
+ * with K^, V^ reconstructed on the fly (paper-graph-ui FlexGen summary,
+ * section 3.4 "Computation delegation": decode attention reads the whole
+ * cache and is bound by I/O; FlexGen review on blog.gzher.com, section 3.4).
+ *   q    fp16 [batch][heads*head_dim];  out [batch][heads*head_dim] in out_dtype.
+ *   softmax_scale <= 0 selects 1/sqrt(head_dim).  Every sequence attends the
+ *   same kv_len positions (no mask).  Requires 1 <= kv_len <= capacity.
+ *   ws / ws_bytes: workspace of at least fgq_decode_attn_ws_bytes(...) bytes
+ *   (may be NULL when that is 0): per-split partial softmax states.
+ * The result depends on the split plan only through fp32 rounding.
+ */
+size_t fgq_decode_attn_ws_bytes(int32_t batch, int32_t heads, int32_t head_dim, int32_t kv_len);
+fgq_status fgq_decode_attn_q4kv(const fgq_kv_cache *kv, const void *q_f16, int32_t kv_len,
+                                float softmax_scale, void *out, int32_t out_dtype,
+                                void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * fgq_pack_weight_g64 - one-time re-layout of a compressed weight (codes and
+ * meta as fgq_quantize_g64 writes them for W [K][N]) into the tile order the
+ * GEMM consumes.  Pure permutation: no value changes.
+ *   packed_codes uint32 [K/32][N/64][64][4]: word (kc, g, lane, j) holds the
+ *     codes of W[k][n], n = 64g + 16j + lane%16, k = 32kc + 8(lane/16) + i for
+ *     i = 0..7, code i in nibble [0,4,1,5,2,6,3,7][i] of the word.
+ *   packed_meta  uint32 [K/32][N/64][4][8]: entry (kc, g, kq, t) is the half2
+ *     {step[k], step[k+1]} for t < 4, {min[k], min[k+1]} for t >= 4, with
+ *     k = 32kc + 8kq + 2(t%4), of group g.
+ * Same byte sizes as codes and meta.  Requires K % 32 == 0, N % 64 == 0.
+ */
+fgq_status fgq_pack_weight_g64(const uint8_t *codes, const uint32_t *meta, int64_t K, int64_t N,
+                               uint32_t *packed_codes, uint32_t *packed_meta, void *stream);
+
+/*
+ * fgq_dequant_gemm - Y = X * W^ for one block of m GPU batches of g rows that
+ * share one read of the compressed weight (paper-graph-ui FlexGen summary,
+ * section 3.4 "Compute Schedule"; FlexGen review on jaehun.me, "A block is
+ * the unit of weight reuse": B = g*m).
+ *   x  fp16 [g*m][K], GPU batch j in rows j*g .. j*g+g-1;
+ *   packed_codes / packed_meta from fgq_pack_weight_g64 for W [K][N];
+ *   y  [g*m][N] in y_dtype.
+ * W^ is restored to fp16 (W^ = fp16(min + q*step)) and multiplied on the
+ * fp16 matrix cores with fp32 accumulation.  Requires K % 32 == 0 and
+ * N % 64 == 0; g*m == 0 is a no-op.
+ *   ws / ws_bytes: at least fgq_dequant_gemm_ws_bytes(g*m, K, N) bytes of
+ *   workspace (split-K partial sums; may be NULL when that is 0).
+ */
+size_t fgq_dequant_gemm_ws_bytes(int64_t M, int64_t K, int64_t N);
+fgq_status fgq_dequant_gemm(const void *x_f16, int32_t g, int32_t m, int64_t K, int64_t N,
+                            const uint32_t *packed_codes, const uint32_t *packed_meta,
+                            void *y, int32_t y_dtype, void *ws, size_t ws_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FGQ_H */

@@ -1,0 +1,175 @@
+// extern "C" entry points of libfgq: argument validation on the host (nothing
+// is enqueued when a check fails), then the launches.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+
+#include "common.h"
+
+namespace fgq {
+
+fgq_status launch_quantize(const void *x, int64_t rows, int64_t cols, int64_t ld, uint8_t *codes,
+                           uint32_t *meta, hipStream_t stream);
+fgq_status launch_kv_append(const fgq_kv_cache *kv, const void *k_new, const void *v_new, int32_t pos,
+                            int32_t n_new, hipStream_t stream);
+fgq_status launch_pack_weight(const uint8_t *codes, const uint32_t *meta, int64_t K, int64_t N,
+                              uint32_t *packed_codes, uint32_t *packed_meta, hipStream_t stream);
+size_t attn_ws_bytes(int32_t batch, int32_t heads, int32_t head_dim, int32_t kv_len);
+fgq_status launch_decode_attn(const fgq_kv_cache *kv, const void *q, int32_t kv_len, float scale, void *out,
+                              int32_t out_dtype, void *ws, hipStream_t stream);
+size_t gemm_ws_bytes(int64_t M, int64_t K, int64_t N);
+fgq_status launch_dequant_gemm(const void *x, int64_t M, int64_t K, int64_t N, const uint32_t *pc,
+                               const uint32_t *pm, void *y, int32_t y_dtype, void *ws, hipStream_t stream);
+
+static thread_local char g_err[512];
+
+fgq_status fail(fgq_status s, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+fgq_status check_launch(const char *what) {
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(FGQ_ERR_DEVICE, "%s: %s", what, hipGetErrorString(e));
+    return FGQ_OK;
+}
+
+static fgq_status check_kv(const fgq_kv_cache *kv) {
+    if (!kv) return fail(FGQ_ERR_INVALID_ARG, "kv is NULL");
+    if (kv->batch < 0 || kv->heads < 0 || kv->capacity < 0 || kv->head_dim <= 0)
+        return fail(FGQ_ERR_INVALID_ARG, "negative kv dimension");
+    if (kv->head_dim != 64 && kv->head_dim != 128) {
+        if (kv->head_dim % 64 != 0) return fail(FGQ_ERR_SHAPE, "head_dim %d is not a multiple of 64", kv->head_dim);
+        return fail(FGQ_ERR_UNSUPPORTED, "head_dim %d (64 or 128 supported)", kv->head_dim);
+    }
+    if (!kv->k_codes || !kv->v_codes || !kv->k_meta || !kv->v_meta)
+        return fail(FGQ_ERR_INVALID_ARG, "kv array is NULL");
+    if (!aligned16(kv->k_codes) || !aligned16(kv->v_codes) || !aligned16(kv->k_meta) || !aligned16(kv->v_meta))
+        return fail(FGQ_ERR_ALIGN, "kv arrays must be 16-byte aligned");
+    return FGQ_OK;
+}
+
+}  // namespace fgq
+
+using namespace fgq;
+
+extern "C" {
+
+int32_t fgq_abi_version(void) { return FGQ_ABI_VERSION; }
+
+const char *fgq_status_string(fgq_status s) {
+    switch (s) {
+        case FGQ_OK: return "ok";
+        case FGQ_ERR_INVALID_ARG: return "invalid argument";
+        case FGQ_ERR_SHAPE: return "bad shape";
+        case FGQ_ERR_ALIGN: return "misaligned array";
+        case FGQ_ERR_CAPACITY: return "kv capacity exceeded";
+        case FGQ_ERR_WORKSPACE: return "workspace too small";
+        case FGQ_ERR_DTYPE: return "unsupported dtype";
+        case FGQ_ERR_DEVICE: return "device error";
+        case FGQ_ERR_UNSUPPORTED: return "unsupported configuration";
+        default: return "unknown status";
+    }
+}
+
+const char *fgq_last_error(void) { return g_err; }
+
+fgq_status fgq_quantize_g64(const void *x_f16, int64_t rows, int64_t cols, int64_t ld_x, uint8_t *codes,
+                            uint32_t *meta, void *stream) {
+    g_err[0] = 0;
+    if (rows < 0 || cols < 0) return fail(FGQ_ERR_INVALID_ARG, "negative size");
+    if (cols % 64 != 0) return fail(FGQ_ERR_SHAPE, "cols %lld is not a multiple of 64", (long long)cols);
+    if (ld_x < cols) return fail(FGQ_ERR_SHAPE, "ld_x %lld < cols %lld", (long long)ld_x, (long long)cols);
+    if (rows == 0 || cols == 0) return FGQ_OK;
+    if (!x_f16 || !codes || !meta) return fail(FGQ_ERR_INVALID_ARG, "NULL array");
+    if (ld_x % 8 != 0 || !aligned16(x_f16) || !aligned16(codes) || !aligned16(meta))
+        return fail(FGQ_ERR_ALIGN, "arrays and rows must be 16-byte aligned");
+    return launch_quantize(x_f16, rows, cols, ld_x, codes, meta, static_cast<hipStream_t>(stream));
+}
+
+fgq_status fgq_kv_append(const fgq_kv_cache *kv, const void *k_new_f16, const void *v_new_f16, int32_t pos,
+                         int32_t n_new, void *stream) {
+    g_err[0] = 0;
+    fgq_status s = check_kv(kv);
+    if (s != FGQ_OK) return s;
+    if (pos < 0 || n_new < 0) return fail(FGQ_ERR_INVALID_ARG, "negative pos or n_new");
+    if ((int64_t)pos + n_new > kv->capacity)
+        return fail(FGQ_ERR_CAPACITY, "pos %d + n_new %d > capacity %d", pos, n_new, kv->capacity);
+    if (n_new == 0 || kv->batch == 0 || kv->heads == 0) return FGQ_OK;
+    if (!k_new_f16 || !v_new_f16) return fail(FGQ_ERR_INVALID_ARG, "NULL k_new or v_new");
+    if (!aligned16(k_new_f16) || !aligned16(v_new_f16)) return fail(FGQ_ERR_ALIGN, "k_new/v_new must be 16-byte aligned");
+    return launch_kv_append(kv, k_new_f16, v_new_f16, pos, n_new, static_cast<hipStream_t>(stream));
+}
+
+size_t fgq_decode_attn_ws_bytes(int32_t batch, int32_t heads, int32_t head_dim, int32_t kv_len) {
+    if (batch <= 0 || heads <= 0 || (head_dim != 64 && head_dim != 128) || kv_len <= 0) return 0;
+    return attn_ws_bytes(batch, heads, head_dim, kv_len);
+}
+
+fgq_status fgq_decode_attn_q4kv(const fgq_kv_cache *kv, const void *q_f16, int32_t kv_len, float softmax_scale,
+                                void *out, int32_t out_dtype, void *ws, size_t ws_bytes, void *stream) {
+    g_err[0] = 0;
+    fgq_status s = check_kv(kv);
+    if (s != FGQ_OK) return s;
+    if (out_dtype != FGQ_DTYPE_F32 && out_dtype != FGQ_DTYPE_F16)
+        return fail(FGQ_ERR_DTYPE, "out_dtype %d", out_dtype);
+    if (kv_len < 1) return fail(FGQ_ERR_SHAPE, "kv_len %d < 1", kv_len);
+    if (kv_len > kv->capacity) return fail(FGQ_ERR_CAPACITY, "kv_len %d > capacity %d", kv_len, kv->capacity);
+    if (!std::isfinite(softmax_scale)) return fail(FGQ_ERR_INVALID_ARG, "softmax_scale is not finite");
+    if (kv->batch == 0 || kv->heads == 0) return FGQ_OK;
+    if (!q_f16 || !out) return fail(FGQ_ERR_INVALID_ARG, "NULL q or out");
+    if (!aligned16(q_f16) || !aligned16(out)) return fail(FGQ_ERR_ALIGN, "q/out must be 16-byte aligned");
+    const size_t need = attn_ws_bytes(kv->batch, kv->heads, kv->head_dim, kv_len);
+    if (need > 0) {
+        if (!ws || ws_bytes < need)
+            return fail(FGQ_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws ? ws_bytes : (size_t)0, need);
+        if (!aligned16(ws)) return fail(FGQ_ERR_ALIGN, "workspace must be 16-byte aligned");
+    }
+    const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt((float)kv->head_dim);
+    return launch_decode_attn(kv, q_f16, kv_len, scale, out, out_dtype, ws, static_cast<hipStream_t>(stream));
+}
+
+fgq_status fgq_pack_weight_g64(const uint8_t *codes, const uint32_t *meta, int64_t K, int64_t N,
+                               uint32_t *packed_codes, uint32_t *packed_meta, void *stream) {
+    g_err[0] = 0;
+    if (K < 0 || N < 0) return fail(FGQ_ERR_INVALID_ARG, "negative size");
+    if (K % 32 != 0 || N % 64 != 0) return fail(FGQ_ERR_SHAPE, "K %% 32 and N %% 64 must be 0");
+    if (K == 0 || N == 0) return FGQ_OK;
+    if (!codes || !meta || !packed_codes || !packed_meta) return fail(FGQ_ERR_INVALID_ARG, "NULL array");
+    if (!aligned16(codes) || !aligned16(meta) || !aligned16(packed_codes) || !aligned16(packed_meta))
+        return fail(FGQ_ERR_ALIGN, "arrays must be 16-byte aligned");
+    return launch_pack_weight(codes, meta, K, N, packed_codes, packed_meta, static_cast<hipStream_t>(stream));
+}
+
+size_t fgq_dequant_gemm_ws_bytes(int64_t M, int64_t K, int64_t N) {
+    if (M <= 0 || K < 0 || N <= 0 || K % 32 != 0 || N % 64 != 0) return 0;
+    return gemm_ws_bytes(M, K, N);
+}
+
+fgq_status fgq_dequant_gemm(const void *x_f16, int32_t g, int32_t m, int64_t K, int64_t N,
+                            const uint32_t *packed_codes, const uint32_t *packed_meta, void *y, int32_t y_dtype,
+                            void *ws, size_t ws_bytes, void *stream) {
+    g_err[0] = 0;
+    if (g < 0 || m < 0 || K < 0 || N < 0) return fail(FGQ_ERR_INVALID_ARG, "negative size");
+    if (K % 32 != 0 || N % 64 != 0) return fail(FGQ_ERR_SHAPE, "K %% 32 and N %% 64 must be 0");
+    if (y_dtype != FGQ_DTYPE_F32 && y_dtype != FGQ_DTYPE_F16) return fail(FGQ_ERR_DTYPE, "y_dtype %d", y_dtype);
+    const int64_t M = (int64_t)g * m;
+    if (M > (int64_t)1 << 30) return fail(FGQ_ERR_SHAPE, "g*m too large");
+    if (M == 0 || N == 0) return FGQ_OK;
+    if (!y || (K > 0 && (!x_f16 || !packed_codes || !packed_meta))) return fail(FGQ_ERR_INVALID_ARG, "NULL array");
+    if (!aligned16(y) || (K > 0 && (!aligned16(x_f16) || !aligned16(packed_codes) || !aligned16(packed_meta))))
+        return fail(FGQ_ERR_ALIGN, "arrays must be 16-byte aligned");
+    const size_t need = gemm_ws_bytes(M, K, N);
+    if (need > 0) {
+        if (!ws || ws_bytes < need)
+            return fail(FGQ_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws ? ws_bytes : (size_t)0, need);
+        if (!aligned16(ws)) return fail(FGQ_ERR_ALIGN, "workspace must be 16-byte aligned");
+    }
+    return launch_dequant_gemm(x_f16, M, K, N, packed_codes, packed_meta, y, y_dtype, ws,
+                               static_cast<hipStream_t>(stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,326 @@
+// Decode attention over the 4-bit compressed KV cache (one query per
+// sequence and head, every cached position).
+//
+// What is computed: paper-graph-ui FlexGen summary, section 3.4
+// "Computation delegation" (decode attention reads the whole per-layer cache
+// and is bound by I/O); FlexGen review on blog.gzher.com, section 3.4 (codes
+// are restored before compute).  Per (sequence b, head h):
+//   s_j = scale * sum_d q_d * (min_{j,g(d)} + c_{j,d} * step_{j,g(d)})
+//   o_d = sum_j softmax(s)_j * (min_{j,g(d)} + c_{j,d} * step_{j,g(d)})
+//
+// Design (HBM-bound: 1.125 bytes per cached hidden element, ~4 flops):
+//  * One wavefront owns one (b, h, split) work item; the sequence is split
+//    into n_split ranges when b*h alone would not fill the 256 CUs, and the
+//    partial softmax states (m, l, o) are merged by a second kernel.
+//  * Lane = (token slot, part): a token's 64-byte row of codes (head_dim 128)
+//    is read by 4 lanes with one 16-byte load each, so a wave streams 16
+//    tokens per load instruction, fully coalesced.
+//  * The reconstruction is folded out of the element loop:
+//      q.k^ = sum_g [ min_g * sum_{d in g} q_d  +  step_g * sum_{d in g} q_d c_d ]
+//    and sum q_d c_d uses v_dot2_f32_f16 on pairs of codes placed in the
+//    mantissa of fp16 subnormals (c * 2^-24 or c * 2^-20 after a plain AND),
+//    so one AND and one dot2 handle two elements with exact products.
+//  * P.V is folded the same way: o_d = sum_j p_j min_j + sum_j (p_j step_j) c_{j,d};
+//    two tokens share a dot2 (a byte permute interleaves their codes) and the
+//    fp16 weight p_j*step_j is split into a high and a low fp16 part so the
+//    product keeps ~22 bits.
+//  * Scores of a 64-token chunk are formed first, the chunk max is taken over
+//    the wave, then the exponentials and the P.V pass run with that max: the
+//    running accumulators are rescaled once per chunk, not per token.
+#include "common.h"
+
+namespace fgq {
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2(as_f16x2(a), as_f16x2(b), c, false);
+}
+
+template <int PARTS>
+__device__ __forceinline__ float sum_parts(float v) {
+    // lanes of one token are PARTS consecutive lanes
+    v += __shfl_xor(v, 1, 64);
+    if (PARTS == 4) v += __shfl_xor(v, 2, 64);
+    return v;
+}
+
+template <int PARTS>
+__device__ __forceinline__ float max_slots(float v) {
+#pragma unroll
+    for (int s = PARTS; s < 64; s <<= 1) v = fmaxf(v, __shfl_xor(v, s, 64));
+    return v;
+}
+
+template <int PARTS>
+__device__ __forceinline__ float sum_slots(float v) {
+#pragma unroll
+    for (int s = PARTS; s < 64; s <<= 1) v += __shfl_xor(v, s, 64);
+    return v;
+}
+
+// D = head_dim (64 or 128); CH = token iterations per chunk (even).
+template <int D, int CH>
+__global__ __launch_bounds__(256) void attn_split_kernel(
+    const uint8_t *__restrict__ kc, const uint32_t *__restrict__ km, const uint8_t *__restrict__ vc,
+    const uint32_t *__restrict__ vm, const uint16_t *__restrict__ q, int H, int cap, int L, int n_split,
+    int tok_per_split, int total_items, float sl2, float *__restrict__ ws, void *__restrict__ out,
+    int out_f16) {
+    constexpr int PARTS = D / 32;   // lanes per token row
+    constexpr int TPI = 64 / PARTS; // tokens per wave iteration
+    constexpr int G = D / 64;       // groups per token row
+    constexpr int EPL = 32 / TPI;   // output elements per lane in the final reduction
+    __shared__ float red[4][64 * 33];
+
+    const int lane = threadIdx.x & 63;
+    const int wv = threadIdx.x >> 6;
+    const int item = blockIdx.x * 4 + wv;
+    if (item >= total_items) return;   // wave-uniform
+
+    const int split = item % n_split;
+    const int bh = item / n_split;
+    const int b = bh / H, hh = bh - b * H;
+    const int j0 = split * tok_per_split;
+    const int j1 = min(L, j0 + tok_per_split);
+    const int slot = lane / PARTS, part = lane % PARTS, grp = part >> 1;
+
+    // ---- query: 32 fp16 values of this lane's part, arranged as dot2 pairs
+    const uint4 *qp = reinterpret_cast<const uint4 *>(q + ((size_t)b * H + hh) * D + part * 32);
+    uint32_t qw[16];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint4 t = qp[i];
+        qw[4 * i + 0] = t.x; qw[4 * i + 1] = t.y; qw[4 * i + 2] = t.z; qw[4 * i + 3] = t.w;
+    }
+    // element 8i + j sits in qw[4i + j/2], half j%2.  Pairs for code word i:
+    //   QP[i][0] = (q_{8i+0}, q_{8i+4}), QP[i][1] = (q_{8i+1}, q_{8i+5}),
+    //   QP[i][2] = (q_{8i+2}, q_{8i+6}), QP[i][3] = (q_{8i+3}, q_{8i+7}).
+    uint32_t QP[4][4];
+    float qsum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t a = qw[4 * i + 0], bq = qw[4 * i + 1], c = qw[4 * i + 2], d = qw[4 * i + 3];
+        QP[i][0] = __builtin_amdgcn_perm(c, a, 0x05040100u);   // (a.lo, c.lo)
+        QP[i][1] = __builtin_amdgcn_perm(c, a, 0x07060302u);   // (a.hi, c.hi)
+        QP[i][2] = __builtin_amdgcn_perm(d, bq, 0x05040100u);  // (b.lo, d.lo)
+        QP[i][3] = __builtin_amdgcn_perm(d, bq, 0x07060302u);  // (b.hi, d.hi)
+#pragma unroll
+        for (int h2 = 0; h2 < 4; ++h2) {
+            const f16x2 v = as_f16x2(qw[4 * i + h2]);
+            qsum += (float)v.x + (float)v.y;
+        }
+    }
+
+    const size_t rowbase = (size_t)bh * cap;
+    const uint8_t *kbase = kc + rowbase * (D / 2) + part * 16;
+    const uint8_t *vbase = vc + rowbase * (D / 2) + part * 16;
+    const uint32_t *kmb = km + rowbase * G + grp;
+    const uint32_t *vmb = vm + rowbase * G + grp;
+
+    float m_run = -INFINITY, l_acc = 0.f, macc = 0.f;
+    float o[32];
+#pragma unroll
+    for (int e = 0; e < 32; ++e) o[e] = 0.f;
+
+    for (int c0 = j0; c0 < j1; c0 += CH * TPI) {
+        uint4 K[CH], V[CH];
+        uint32_t KM[CH], VM[CH];
+        bool ok[CH];
+#pragma unroll
+        for (int it = 0; it < CH; ++it) {
+            const int j = c0 + it * TPI + slot;
+            ok[it] = j < j1;
+            const size_t jc = (size_t)(ok[it] ? j : j1 - 1);
+            K[it] = *reinterpret_cast<const uint4 *>(kbase + jc * (D / 2));
+            KM[it] = kmb[jc * G];
+            V[it] = *reinterpret_cast<const uint4 *>(vbase + jc * (D / 2));
+            VM[it] = vmb[jc * G];
+        }
+        // ---- scores
+        float s[CH];
+#pragma unroll
+        for (int it = 0; it < CH; ++it) {
+            const uint32_t w[4] = {K[it].x, K[it].y, K[it].z, K[it].w};
+            float lo = 0.f, hi = 0.f;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const uint32_t w8 = w[i] >> 8;
+                lo = dot2(w[i] & 0x000F000Fu, QP[i][0], lo);
+                hi = dot2(w[i] & 0x00F000F0u, QP[i][1], hi);
+                lo = dot2(w8 & 0x000F000Fu, QP[i][2], lo);
+                hi = dot2(w8 & 0x00F000F0u, QP[i][3], hi);
+            }
+            const float sc = lo * 16777216.0f + hi * 1048576.0f;   // sum_d q_d c_d
+            const float step = h2f((uint16_t)(KM[it] >> 16));
+            const float mn = h2f((uint16_t)(KM[it] & 0xffffu));
+            const float part_s = step * sc + mn * qsum;
+            const float tot = sum_parts<PARTS>(part_s);
+            s[it] = ok[it] ? tot * sl2 : -INFINITY;
+        }
+        float cm = s[0];
+#pragma unroll
+        for (int it = 1; it < CH; ++it) cm = fmaxf(cm, s[it]);
+        cm = max_slots<PARTS>(cm);
+        const float m_new = fmaxf(m_run, cm);
+        const float corr = exp2f(m_run - m_new);
+        m_run = m_new;
+        l_acc *= corr;
+        macc *= corr;
+#pragma unroll
+        for (int e = 0; e < 32; ++e) o[e] *= corr;
+
+        // ---- P.V, two tokens (it, it + CH/2) per dot2
+#pragma unroll
+        for (int pi = 0; pi < CH / 2; ++pi) {
+            const int ia = pi, ib = pi + CH / 2;
+            const float pa = exp2f(s[ia] - m_new), pb = exp2f(s[ib] - m_new);
+            l_acc += pa + pb;
+            const float sa = h2f((uint16_t)(VM[ia] >> 16)), sb = h2f((uint16_t)(VM[ib] >> 16));
+            macc += pa * h2f((uint16_t)(VM[ia] & 0xffffu)) + pb * h2f((uint16_t)(VM[ib] & 0xffffu));
+            const float wa = pa * sa, wb = pb * sb;
+            const _Float16 wa_h = (_Float16)wa, wb_h = (_Float16)wb;
+            const _Float16 wa_l = (_Float16)(wa - (float)wa_h), wb_l = (_Float16)(wb - (float)wb_h);
+            f16x2 whi, wlo;
+            whi.x = wa_h; whi.y = wb_h;
+            wlo.x = wa_l; wlo.y = wb_l;
+            const uint32_t WH = as_u32(whi), WL = as_u32(wlo);
+            const uint32_t A[4] = {V[ia].x, V[ia].y, V[ia].z, V[ia].w};
+            const uint32_t Bv[4] = {V[ib].x, V[ib].y, V[ib].z, V[ib].w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                // X = [A.b0, A.b1, B.b0, B.b1], Y = [A.b2, A.b3, B.b2, B.b3]
+                const uint32_t X = __builtin_amdgcn_perm(Bv[i], A[i], 0x05040100u);
+                const uint32_t Y = __builtin_amdgcn_perm(Bv[i], A[i], 0x07060302u);
+                const uint32_t X8 = X >> 8, Y8 = Y >> 8;
+                const uint32_t pr[8] = {X & 0x000F000Fu, X & 0x00F000F0u, X8 & 0x000F000Fu, X8 & 0x00F000F0u,
+                                        Y & 0x000F000Fu, Y & 0x00F000F0u, Y8 & 0x000F000Fu, Y8 & 0x00F000F0u};
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    o[8 * i + e] = dot2(pr[e], WH, o[8 * i + e]);
+                    o[8 * i + e] = dot2(pr[e], WL, o[8 * i + e]);
+                }
+            }
+        }
+    }
+
+    // ---- reduce the token slots: o (per element) through LDS, l and macc by shuffles
+    float *r = red[wv];
+#pragma unroll
+    for (int e = 0; e < 32; ++e) r[lane * 33 + e] = o[e];
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const float l_tot = sum_slots<PARTS>(l_acc);
+    const float m_tot = sum_slots<PARTS>(macc);
+    float val[EPL];
+#pragma unroll
+    for (int k = 0; k < EPL; ++k) {
+        const int e = slot * EPL + k;
+        float acc = 0.f;
+        for (int s2 = 0; s2 < TPI; ++s2) acc += r[(s2 * PARTS + part) * 33 + e];
+        val[k] = acc * ((e & 1) ? 1048576.0f : 16777216.0f) + m_tot;
+    }
+    const int d0 = part * 32 + slot * EPL;
+    if (n_split == 1) {
+        const float inv = 1.0f / l_tot;
+        const size_t ob = ((size_t)b * H + hh) * D + d0;
+#pragma unroll
+        for (int k = 0; k < EPL; ++k) {
+            if (out_f16)
+                static_cast<_Float16 *>(out)[ob + k] = (_Float16)(val[k] * inv);
+            else
+                static_cast<float *>(out)[ob + k] = val[k] * inv;
+        }
+    } else {
+        float *wrow = ws + ((size_t)bh * n_split + split) * (D + 4);
+#pragma unroll
+        for (int k = 0; k < EPL; ++k) wrow[d0 + k] = val[k];
+        if (lane == 0) {
+            wrow[D] = m_run;
+            wrow[D + 1] = l_tot;
+        }
+    }
+}
+
+// Merge the n_split partial states of each (b, h): one block of D threads.
+template <int D>
+__global__ __launch_bounds__(128) void attn_merge_kernel(const float *__restrict__ ws, int n_split,
+                                                         void *__restrict__ out, int out_f16) {
+    const int bh = blockIdx.x;
+    const int d = threadIdx.x;
+    const float *base = ws + (size_t)bh * n_split * (D + 4);
+    float mx = -INFINITY;
+    for (int i = 0; i < n_split; ++i) mx = fmaxf(mx, base[i * (D + 4) + D]);
+    float num = 0.f, den = 0.f;
+    for (int i = 0; i < n_split; ++i) {
+        const float w = exp2f(base[i * (D + 4) + D] - mx);
+        num += w * base[i * (D + 4) + d];
+        den += w * base[i * (D + 4) + D + 1];
+    }
+    const float v = num / den;
+    if (out_f16)
+        static_cast<_Float16 *>(out)[(size_t)bh * D + d] = (_Float16)v;
+    else
+        static_cast<float *>(out)[(size_t)bh * D + d] = v;
+}
+
+constexpr int kChunkIters = 4;
+
+}  // namespace
+
+struct AttnPlan {
+    int n_split;
+    int tok_per_split;
+};
+
+AttnPlan attn_plan(int32_t batch, int32_t heads, int32_t head_dim, int32_t kv_len) {
+    const int tpi = 64 / (head_dim / 32);
+    const int chunk = kChunkIters * tpi;
+    const int64_t bh = (int64_t)batch * heads;
+    const int64_t target_waves = 8LL * 4 * kNumCU;     // ~8 waves per SIMD in flight
+    int n_split = 1;
+    if (bh > 0 && bh < target_waves) {
+        n_split = (int)((target_waves + bh - 1) / bh);
+        const int max_split = kv_len / 256 > 1 ? kv_len / 256 : 1;   // keep >= 256 tokens per split
+        if (n_split > max_split) n_split = max_split;
+    }
+    int per = (kv_len + n_split - 1) / n_split;
+    per = ((per + chunk - 1) / chunk) * chunk;
+    n_split = (kv_len + per - 1) / per;   // drop empty splits
+    return {n_split, per};
+}
+
+size_t attn_ws_bytes(int32_t batch, int32_t heads, int32_t head_dim, int32_t kv_len) {
+    const AttnPlan p = attn_plan(batch, heads, head_dim, kv_len);
+    if (p.n_split <= 1) return 0;
+    return (size_t)batch * heads * p.n_split * (head_dim + 4) * sizeof(float);
+}
+
+fgq_status launch_decode_attn(const fgq_kv_cache *kv, const void *q, int32_t kv_len, float scale, void *out,
+                              int32_t out_dtype, void *ws, hipStream_t stream) {
+    const AttnPlan p = attn_plan(kv->batch, kv->heads, kv->head_dim, kv_len);
+    const int total = kv->batch * kv->heads * p.n_split;
+    if (kv->batch == 0 || kv->heads == 0) return FGQ_OK;
+    const float sl2 = scale * kLog2e;
+    const int f16 = out_dtype == FGQ_DTYPE_F16;
+    const dim3 grid((unsigned)((total + 3) / 4)), block(256);
+    if (kv->head_dim == 128)
+        attn_split_kernel<128, kChunkIters><<<grid, block, 0, stream>>>(
+            kv->k_codes, kv->k_meta, kv->v_codes, kv->v_meta, static_cast<const uint16_t *>(q), kv->heads,
+            kv->capacity, kv_len, p.n_split, p.tok_per_split, total, sl2, static_cast<float *>(ws), out, f16);
+    else
+        attn_split_kernel<64, kChunkIters><<<grid, block, 0, stream>>>(
+            kv->k_codes, kv->k_meta, kv->v_codes, kv->v_meta, static_cast<const uint16_t *>(q), kv->heads,
+            kv->capacity, kv_len, p.n_split, p.tok_per_split, total, sl2, static_cast<float *>(ws), out, f16);
+    fgq_status s = check_launch("attn_split_kernel");
+    if (s != FGQ_OK || p.n_split == 1) return s;
+    const dim3 mgrid((unsigned)(kv->batch * kv->heads));
+    if (kv->head_dim == 128)
+        attn_merge_kernel<128><<<mgrid, dim3(128), 0, stream>>>(static_cast<const float *>(ws), p.n_split, out, f16);
+    else
+        attn_merge_kernel<64><<<mgrid, dim3(64), 0, stream>>>(static_cast<const float *>(ws), p.n_split, out, f16);
+    return check_launch("attn_merge_kernel");
+}
+
+}  // namespace fgq

@@ -1,0 +1,201 @@
+// Group-wise 4-bit quantiser (64 elements per group) for weights and KV
+// rows, the KV-cache append, and the one-time weight re-layout for the GEMM.
+//
+// Encoding: FlexGen review on jaehun.me, section "Is 4-bit compression the
+// same as integer-arithmetic acceleration?" (paper section 5) - asymmetric
+// min/max groups of 64, weights along the output channel, KV along hidden,
+// constant groups handled apart; FlexGen review on blog.gzher.com, section
+// 3.4.  The formula itself is missing from the pages; the min-max reading
+// q = RNE(((x - a) / (b - a)) * 15) is taken with each step an IEEE fp32
+// operation in that order, so every code and meta word is reproducible bit
+// for bit.
+//
+// Mapping: one group per 8 consecutive lanes, each lane owning 8 elements
+// (one 16-byte load).  The group's min and max are exchanged with DPP-free
+// xor shuffles inside the 8-lane segment; each lane then writes one 32-bit
+// word of codes (8 nibbles) and the segment's first lane writes the meta
+// word.  The division is the correctly rounded one (HIP default).
+#include "common.h"
+
+namespace fgq {
+namespace {
+
+struct GroupOut {
+    uint32_t codes;   // 8 nibbles of this lane
+    uint32_t meta;    // valid in every lane of the segment
+};
+
+// x8: the lane's 8 fp16 values (as raw halves). All 8 lanes of the segment
+// must call this together (shuffles).
+__device__ __forceinline__ GroupOut quantize8(const uint4 raw) {
+#pragma clang fp contract(off)
+    float x[8];
+    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        x[2 * i] = h2f((uint16_t)(w[i] & 0xffffu));
+        x[2 * i + 1] = h2f((uint16_t)(w[i] >> 16));
+    }
+    float a = x[0], b = x[0];
+#pragma unroll
+    for (int i = 1; i < 8; ++i) {
+        a = fminf(a, x[i]);
+        b = fmaxf(b, x[i]);
+    }
+#pragma unroll
+    for (int s = 1; s < 8; s <<= 1) {
+        a = fminf(a, __shfl_xor(a, s, 64));
+        b = fmaxf(b, __shfl_xor(b, s, 64));
+    }
+    a = a + 0.0f;   // -0 -> +0
+    b = b + 0.0f;
+    GroupOut out;
+    const uint32_t min_h = f2h_rne(a);   // exact: a is an fp16 value
+    if (a == b) {
+        out.codes = 0u;
+        out.meta = min_h;
+        return out;
+    }
+    const float d = __fsub_rn(b, a);
+    uint32_t packed = 0u;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const float t = __fsub_rn(x[i], a);
+        const float u = __fdiv_rn(t, d);
+        const float v = __fmul_rn(u, 15.0f);
+        float r = rintf(v);                 // v_rndne_f32: ties to even
+        r = fminf(fmaxf(r, 0.0f), 15.0f);
+        packed |= ((uint32_t)r) << (4 * i);
+    }
+    const float step = __fdiv_rn(d, 15.0f);
+    out.codes = packed;
+    out.meta = min_h | ((uint32_t)f2h_rne(step) << 16);
+    return out;
+}
+
+__global__ __launch_bounds__(256) void quantize_g64_kernel(const uint16_t *__restrict__ x, int64_t rows,
+                                                           int64_t cols, int64_t ld,
+                                                           uint32_t *__restrict__ codes,
+                                                           uint32_t *__restrict__ meta) {
+    const int64_t ngr = cols >> 6;
+    const int64_t total = rows * ngr;
+    const int64_t gid = (int64_t)blockIdx.x * 32 + (threadIdx.x >> 3);
+    const int sub = threadIdx.x & 7;
+    const bool valid = gid < total;
+    const int64_t r = valid ? gid / ngr : 0;
+    const int64_t gi = valid ? gid - r * ngr : 0;
+    uint4 raw = make_uint4(0u, 0u, 0u, 0u);
+    if (valid) raw = *reinterpret_cast<const uint4 *>(x + r * ld + gi * 64 + sub * 8);
+    const GroupOut o = quantize8(raw);
+    if (!valid) return;
+    codes[(r * (cols >> 1) + gi * 32 + sub * 4) >> 2] = o.codes;
+    if (sub == 0) meta[gid] = o.meta;
+}
+
+// One group = 64 hidden elements of one token's K or V row of one head.
+// gid enumerates (which in {K,V}, b, i, head, group-in-head).
+__global__ __launch_bounds__(256) void kv_append_kernel(const uint16_t *__restrict__ k_new,
+                                                        const uint16_t *__restrict__ v_new,
+                                                        fgq_kv_cache kv, int32_t pos, int32_t n_new) {
+    const int gph = kv.head_dim >> 6;                       // groups per head
+    const int64_t per_tensor = (int64_t)kv.batch * n_new * kv.heads * gph;
+    const int64_t gid = (int64_t)blockIdx.x * 32 + (threadIdx.x >> 3);
+    const int sub = threadIdx.x & 7;
+    const bool valid = gid < 2 * per_tensor;
+    const int which = (valid && gid >= per_tensor) ? 1 : 0;
+    int64_t rem = valid ? gid - which * per_tensor : 0;
+    const int gi = (int)(rem % gph);
+    rem /= gph;
+    const int hd = (int)(rem % kv.heads);
+    rem /= kv.heads;
+    const int i = (int)(rem % n_new);
+    const int64_t b = rem / n_new;
+    const int64_t hidden = (int64_t)kv.heads * kv.head_dim;
+    const uint16_t *src = which ? v_new : k_new;
+    uint4 raw = make_uint4(0u, 0u, 0u, 0u);
+    if (valid)
+        raw = *reinterpret_cast<const uint4 *>(src + (b * n_new + i) * hidden + (int64_t)hd * kv.head_dim +
+                                               gi * 64 + sub * 8);
+    const GroupOut o = quantize8(raw);
+    if (!valid) return;
+    const int64_t slot = (b * kv.heads + hd) * kv.capacity + pos + i;
+    uint8_t *cbase = which ? kv.v_codes : kv.k_codes;
+    uint32_t *mbase = which ? kv.v_meta : kv.k_meta;
+    *reinterpret_cast<uint32_t *>(cbase + slot * (kv.head_dim >> 1) + gi * 32 + sub * 4) = o.codes;
+    if (sub == 0) mbase[slot * gph + gi] = o.meta;
+}
+
+// Weight re-layout: one thread per packed code word (kc, g, lane, j).
+__global__ __launch_bounds__(256) void pack_codes_kernel(const uint8_t *__restrict__ codes, int64_t K,
+                                                         int64_t N, uint32_t *__restrict__ packed) {
+    const int64_t words = K * N / 8;
+    const int64_t w = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (w >= words) return;
+    const int j = (int)(w & 3);
+    const int lane = (int)((w >> 2) & 63);
+    const int64_t tile = w >> 8;                 // kc * (N/64) + g
+    const int64_t ng = N >> 6;
+    const int64_t g = tile % ng, kc = tile / ng;
+    const int64_t n = 64 * g + 16 * j + (lane & 15);
+    const int64_t k0 = 32 * kc + 8 * (lane >> 4);
+    const int slot_of[8] = {0, 4, 1, 5, 2, 6, 3, 7};
+    uint32_t out = 0u;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const uint8_t byte = codes[(k0 + i) * (N >> 1) + (n >> 1)];
+        const uint32_t q = (n & 1) ? (byte >> 4) : (byte & 15u);
+        out |= q << (4 * slot_of[i]);
+    }
+    packed[w] = out;
+}
+
+// One thread per packed meta word (kc, g, kq, t).
+__global__ __launch_bounds__(256) void pack_meta_kernel(const uint32_t *__restrict__ meta, int64_t K,
+                                                        int64_t N, uint32_t *__restrict__ packed) {
+    const int64_t words = K * N / 64;
+    const int64_t w = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (w >= words) return;
+    const int t = (int)(w & 7);
+    const int kq = (int)((w >> 3) & 3);
+    const int64_t tile = w >> 5;
+    const int64_t ng = N >> 6;
+    const int64_t g = tile % ng, kc = tile / ng;
+    const int64_t k = 32 * kc + 8 * kq + 2 * (t & 3);
+    const uint32_t m0 = meta[k * ng + g], m1 = meta[(k + 1) * ng + g];
+    packed[w] = (t < 4) ? ((m0 >> 16) | (m1 & 0xffff0000u)) : ((m0 & 0xffffu) | (m1 << 16));
+}
+
+}  // namespace
+
+fgq_status launch_quantize(const void *x, int64_t rows, int64_t cols, int64_t ld, uint8_t *codes,
+                           uint32_t *meta, hipStream_t stream) {
+    const int64_t groups = rows * (cols / 64);
+    if (groups == 0) return FGQ_OK;
+    const int64_t blocks = (groups + 31) / 32;
+    quantize_g64_kernel<<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(
+        static_cast<const uint16_t *>(x), rows, cols, ld, reinterpret_cast<uint32_t *>(codes), meta);
+    return check_launch("quantize_g64_kernel");
+}
+
+fgq_status launch_kv_append(const fgq_kv_cache *kv, const void *k_new, const void *v_new, int32_t pos,
+                            int32_t n_new, hipStream_t stream) {
+    const int64_t groups = 2LL * kv->batch * n_new * kv->heads * (kv->head_dim / 64);
+    if (groups == 0) return FGQ_OK;
+    const int64_t blocks = (groups + 31) / 32;
+    kv_append_kernel<<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(
+        static_cast<const uint16_t *>(k_new), static_cast<const uint16_t *>(v_new), *kv, pos, n_new);
+    return check_launch("kv_append_kernel");
+}
+
+fgq_status launch_pack_weight(const uint8_t *codes, const uint32_t *meta, int64_t K, int64_t N,
+                              uint32_t *packed_codes, uint32_t *packed_meta, hipStream_t stream) {
+    const int64_t cw = K * N / 8, mw = K * N / 64;
+    if (cw == 0) return FGQ_OK;
+    pack_codes_kernel<<<dim3((unsigned)((cw + 255) / 256)), dim3(256), 0, stream>>>(codes, K, N, packed_codes);
+    fgq_status s = check_launch("pack_codes_kernel");
+    if (s != FGQ_OK) return s;
+    pack_meta_kernel<<<dim3((unsigned)((mw + 255) / 256)), dim3(256), 0, stream>>>(meta, K, N, packed_meta);
+    return check_launch("pack_meta_kernel");
+}
+
+}  // namespace fgq

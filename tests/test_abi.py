@@ -1,0 +1,135 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/fgq.h declares, and rejects bad arguments on the host before any
+HIP call (so nothing is enqueued and outputs stay untouched)."""
+import ctypes
+import os
+import subprocess
+
+import pytest
+
+import int4_group_quantized_fgq_amd as fgq
+
+BAD = 0x1001            # a non-null, misaligned address (never dereferenced)
+GOOD = 0x7f0000000000   # a non-null, 16-byte aligned address (never dereferenced)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(fgq.LIB_PATH):
+        pytest.skip("libfgq.so not built")
+    return fgq.load()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = fgq.declared_symbols()
+    assert {"fgq_quantize_g64", "fgq_kv_append", "fgq_decode_attn_q4kv", "fgq_dequant_gemm"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", fgq.LIB_PATH], stdout=subprocess.PIPE, text=True).stdout
+    exported = {l.split()[-1] for l in out.splitlines() if " T " in l}
+    assert set(names) <= exported
+
+
+def test_header_compiles_as_plain_c(tmp_path):
+    src = tmp_path / "t.c"
+    src.write_text('#include "fgq.h"\nint main(void){ fgq_kv_cache kv; (void)kv; return fgq_abi_version() != 1; }\n')
+    inc = os.path.join(os.path.dirname(fgq.HEADER_PATH))
+    subprocess.check_call(["gcc", "-std=c99", "-Wall", "-Werror", "-c", str(src), "-I", inc, "-o",
+                           str(tmp_path / "t.o")])
+
+
+def test_version_and_status_strings(lib):
+    assert fgq.fgq_abi_version() == 1
+    assert fgq.status_string(fgq.FGQ_OK) == "ok"
+    codes = [fgq.FGQ_ERR_INVALID_ARG, fgq.FGQ_ERR_SHAPE, fgq.FGQ_ERR_ALIGN, fgq.FGQ_ERR_CAPACITY,
+             fgq.FGQ_ERR_WORKSPACE, fgq.FGQ_ERR_DTYPE, fgq.FGQ_ERR_DEVICE, fgq.FGQ_ERR_UNSUPPORTED]
+    texts = {fgq.status_string(c) for c in codes}
+    assert len(texts) == len(codes)
+    assert fgq.status_string(12345) == "unknown status"
+
+
+def _status(call):
+    try:
+        call()
+    except fgq.FgqError as e:
+        return e.status
+    return fgq.FGQ_OK
+
+
+def test_quantize_validation(lib):
+    q = fgq.fgq_quantize_g64
+    assert _status(lambda: q(GOOD, 4, 96, 96, GOOD, GOOD, 0)) == fgq.FGQ_ERR_SHAPE
+    assert "multiple of 64" in fgq.last_error()
+    assert _status(lambda: q(GOOD, -1, 64, 64, GOOD, GOOD, 0)) == fgq.FGQ_ERR_INVALID_ARG
+    assert _status(lambda: q(GOOD, 4, 128, 64, GOOD, GOOD, 0)) == fgq.FGQ_ERR_SHAPE
+    assert _status(lambda: q(0, 4, 64, 64, GOOD, GOOD, 0)) == fgq.FGQ_ERR_INVALID_ARG
+    assert _status(lambda: q(BAD, 4, 64, 64, GOOD, GOOD, 0)) == fgq.FGQ_ERR_ALIGN
+    assert _status(lambda: q(GOOD, 4, 64, 68, GOOD, GOOD, 0)) == fgq.FGQ_ERR_ALIGN
+    assert _status(lambda: q(0, 0, 64, 64, 0, 0, 0)) == fgq.FGQ_OK          # empty: no-op
+
+
+def _kv(batch=2, heads=2, head_dim=128, cap=16, ptr=GOOD):
+    return fgq.fgq_kv_cache(ptr, ptr, ptr, ptr, batch, heads, head_dim, cap)
+
+
+def test_kv_append_validation(lib):
+    a = fgq.fgq_kv_append
+    assert _status(lambda: a(_kv(), GOOD, GOOD, 10, 7, 0)) == fgq.FGQ_ERR_CAPACITY
+    assert _status(lambda: a(_kv(), GOOD, GOOD, -1, 1, 0)) == fgq.FGQ_ERR_INVALID_ARG
+    assert _status(lambda: a(_kv(head_dim=96), GOOD, GOOD, 0, 1, 0)) == fgq.FGQ_ERR_SHAPE
+    assert _status(lambda: a(_kv(head_dim=256), GOOD, GOOD, 0, 1, 0)) == fgq.FGQ_ERR_UNSUPPORTED
+    assert _status(lambda: a(_kv(ptr=BAD), GOOD, GOOD, 0, 1, 0)) == fgq.FGQ_ERR_ALIGN
+    assert _status(lambda: a(_kv(ptr=0), GOOD, GOOD, 0, 1, 0)) == fgq.FGQ_ERR_INVALID_ARG
+    assert _status(lambda: a(_kv(), BAD, GOOD, 0, 1, 0)) == fgq.FGQ_ERR_ALIGN
+    assert _status(lambda: a(_kv(), GOOD, GOOD, 16, 0, 0)) == fgq.FGQ_OK      # n_new = 0 at the end: no-op
+    assert _status(lambda: a(_kv(batch=0), 0, 0, 0, 4, 0)) == fgq.FGQ_OK
+    null_kv = ctypes.cast(None, ctypes.POINTER(fgq.fgq_kv_cache))
+    assert lib.fgq_kv_append(null_kv, GOOD, GOOD, 0, 1, None) == fgq.FGQ_ERR_INVALID_ARG
+
+
+def test_attention_validation_and_workspace(lib):
+    d = fgq.fgq_decode_attn_q4kv
+    assert _status(lambda: d(_kv(), GOOD, 0, 0.0, GOOD, 0, 0, 0, 0)) == fgq.FGQ_ERR_SHAPE
+    assert _status(lambda: d(_kv(), GOOD, 17, 0.0, GOOD, 0, 0, 0, 0)) == fgq.FGQ_ERR_CAPACITY
+    assert _status(lambda: d(_kv(), GOOD, 4, 0.0, GOOD, 7, 0, 0, 0)) == fgq.FGQ_ERR_DTYPE
+    assert _status(lambda: d(_kv(), GOOD, 4, float("nan"), GOOD, 0, 0, 0, 0)) == fgq.FGQ_ERR_INVALID_ARG
+    assert _status(lambda: d(_kv(), BAD, 4, 0.0, GOOD, 0, 0, 0, 0)) == fgq.FGQ_ERR_ALIGN
+    # a shape that needs a workspace (few sequences, long context)
+    B, H, D, L = 1, 2, 128, 4096
+    need = fgq.fgq_decode_attn_ws_bytes(B, H, D, L)
+    assert need > 0 and need % 16 == 0
+    kv = _kv(B, H, D, L)
+    assert _status(lambda: d(kv, GOOD, L, 0.0, GOOD, 0, 0, 0, 0)) == fgq.FGQ_ERR_WORKSPACE
+    assert _status(lambda: d(kv, GOOD, L, 0.0, GOOD, 0, GOOD, need - 16, 0)) == fgq.FGQ_ERR_WORKSPACE
+    assert _status(lambda: d(kv, GOOD, L, 0.0, GOOD, 0, BAD, need, 0)) == fgq.FGQ_ERR_ALIGN
+    # many sequences: one split, no workspace
+    assert fgq.fgq_decode_attn_ws_bytes(144, 96, 128, 544) == 0
+    assert fgq.fgq_decode_attn_ws_bytes(0, 96, 128, 544) == 0
+
+
+def test_gemm_validation_and_workspace(lib):
+    gm = fgq.fgq_dequant_gemm
+    assert _status(lambda: gm(GOOD, 4, 1, 48, 64, GOOD, GOOD, GOOD, 0, 0, 0, 0)) == fgq.FGQ_ERR_SHAPE
+    assert _status(lambda: gm(GOOD, 4, 1, 64, 96, GOOD, GOOD, GOOD, 0, 0, 0, 0)) == fgq.FGQ_ERR_SHAPE
+    assert _status(lambda: gm(GOOD, 4, 1, 64, 64, GOOD, GOOD, GOOD, 5, 0, 0, 0)) == fgq.FGQ_ERR_DTYPE
+    assert _status(lambda: gm(GOOD, -4, 1, 64, 64, GOOD, GOOD, GOOD, 0, 0, 0, 0)) == fgq.FGQ_ERR_INVALID_ARG
+    assert _status(lambda: gm(BAD, 4, 1, 64, 64, GOOD, GOOD, GOOD, 0, 0, 0, 0)) == fgq.FGQ_ERR_ALIGN
+    assert _status(lambda: gm(GOOD, 4, 1, 64, 64, 0, GOOD, GOOD, 0, 0, 0, 0)) == fgq.FGQ_ERR_INVALID_ARG
+    assert _status(lambda: gm(0, 0, 4, 64, 64, 0, 0, 0, 0, 0, 0, 0)) == fgq.FGQ_OK   # empty block
+    need = fgq.fgq_dequant_gemm_ws_bytes(144, 12288, 12288)
+    assert need > 0 and need % 16 == 0
+    assert _status(lambda: gm(GOOD, 36, 4, 12288, 12288, GOOD, GOOD, GOOD, 0, GOOD, need - 4, 0)) == \
+        fgq.FGQ_ERR_WORKSPACE
+    pk = fgq.fgq_pack_weight_g64
+    assert _status(lambda: pk(GOOD, GOOD, 48, 64, GOOD, GOOD, 0)) == fgq.FGQ_ERR_SHAPE
+    assert _status(lambda: pk(GOOD, GOOD, 64, 64, BAD, GOOD, 0)) == fgq.FGQ_ERR_ALIGN
+    assert _status(lambda: pk(0, 0, 0, 64, 0, 0, 0)) == fgq.FGQ_OK
+
+
+def test_gemm_workspace_covers_every_workload():
+    import synth
+    for w in synth.WORKLOADS.values():
+        for K, N in w.weights:
+            need = fgq.fgq_dequant_gemm_ws_bytes(w.batch, K, N)
+            assert need % 16 == 0
+            assert need <= 64 * w.batch * N * 4        # at most 64 split-K partial tiles

@@ -1,0 +1,353 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle on the
+same seeded inputs.
+
+Bar: codes and meta bit-exact; attention and GEMM outputs within
+max|gpu - oracle| <= 1e-2 and ||gpu - oracle||_2 / ||oracle||_2 <= 1e-3,
+computed by the oracle on the same codes.  Sizes span several tiles and
+ragged tails; the full-size workloads are checked on sampled outputs that the
+oracle computes one sequence / one column group at a time.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests import gpu_util as gu
+
+try:
+    import torch
+    _HAS_GPU = torch.cuda.is_available()
+except ImportError:   # pragma: no cover
+    _HAS_GPU = False
+
+pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not _HAS_GPU, reason="needs an MI355X GPU")]
+
+W = synth.WORKLOADS
+
+
+def _special_groups():
+    rng = np.random.default_rng(0)
+    rows = []
+    rows.append(np.full(64, 1.5))                           # constant
+    rows.append(np.full(64, -0.0))                          # constant -0
+    z = np.zeros(64); z[:32] = -0.0; z[40] = 2.0; rows.append(z)  # signed zeros at the min
+    rows.append(np.r_[65504.0, -65504.0, rng.standard_normal(62)])
+    rows.append(rng.standard_normal(64) * 2.0 ** -20)      # subnormal fp16 values
+    sub = np.zeros(64); sub[1] = 2.0 ** -24; rows.append(sub)  # step underflows to 0
+    rows.append(np.r_[0.0, 30.0, np.arange(1, 30, 2), np.zeros(64 - 17)])                 # tie ladder G1
+    rows.append(np.r_[-8.0, 7.0, np.arange(-7.5, 7.0, 1.0), np.full(64 - 17, -8.0)])     # tie ladder G2
+    k = rng.integers(0, 16, 64); k[0], k[1] = 0, 15; rows.append((k - 8) * 0.25)          # on-grid
+    rows.append(rng.standard_normal(64) * 1000.0)
+    return np.array(rows).astype(np.float16)
+
+
+def test_quantize_bit_exact_random_and_special():
+    rng = np.random.default_rng(1)
+    x = (rng.standard_normal((333, 64 * 7)) * 3.0).astype(np.float16)
+    sp = _special_groups()                                   # [10][64]
+    x[:10, 64:128] = sp
+    x[20:30, 0:64] = sp
+    gu.note("quantize 333x448 random + special groups")
+    c, m = gu.quantize(x)
+    rc, rm = oracle.quantize_g64(x)
+    assert np.array_equal(c, rc) and np.array_equal(m, rm)
+
+
+def test_quantize_leading_dimension():
+    rng = np.random.default_rng(2)
+    full = rng.standard_normal((37, 256 + 64)).astype(np.float16)
+    gu.note("quantize with ld_x > cols")
+    torch = gu.torch_cuda()
+    xd = gu.to_dev(full)
+    codes = torch.empty((37, 128), dtype=torch.uint8, device="cuda")
+    meta = torch.empty((37, 4), dtype=torch.int32, device="cuda")
+    gu.fgq.fgq_quantize_g64(xd, 37, 256, 320, codes, meta)
+    torch.cuda.synchronize()
+    rc, rm = oracle.quantize_g64(np.ascontiguousarray(full[:, :256]))
+    assert np.array_equal(gu.to_host(codes), rc)
+    assert np.array_equal(gu.to_host(meta, np.uint32), rm)
+
+
+@pytest.mark.parametrize("name,idx", [("tiny", 0), ("opt-6.7b", 0), ("opt-6.7b", 5), ("opt-30b", 4),
+                                      ("opt-175b", 0), ("opt-175b", 4)])
+def test_quantize_bit_exact_workload_weights(name, idx):
+    w = W[name]
+    K, N = w.weights[idx]
+    gu.note("quantize weight %s[%d] %dx%d" % (name, idx, K, N))
+    x = synth.weight(w, idx)
+    c, m = gu.quantize(x)
+    rc, rm = oracle.quantize_g64(x)
+    assert np.array_equal(c, rc), "codes differ"
+    assert np.array_equal(m, rm), "meta differs"
+
+
+def _kv_case(w, nb, steps):
+    """Prompt bulk append then `steps` one-token appends, GPU and oracle."""
+    B, H, D = nb, w.heads, w.head_dim
+    cap = w.prompt + steps
+    dev = gu.DevKV(B, H, D, cap)
+    ref = oracle.KVCache(B, H, D, cap)
+    pk = synth.prompt_kv(w, "k", nb=nb)
+    pv = synth.prompt_kv(w, "v", nb=nb)
+    dev.append(pk, pv, 0)
+    oracle.kv_append(ref, pk, pv, 0)
+    del pk, pv
+    for t in range(1, steps + 1):
+        sk = synth.step_kv(w, "k", t)[:nb]
+        sv = synth.step_kv(w, "v", t)[:nb]
+        dev.append(sk, sv, w.prompt + t - 1)
+        oracle.kv_append(ref, sk, sv, w.prompt + t - 1)
+    return dev, ref
+
+
+@pytest.mark.parametrize("name,nb,steps", [("tiny", 4, 1), ("opt-6.7b", 3, 4), ("long-t3", 2, 2)])
+def test_kv_append_bit_exact(name, nb, steps):
+    w = W[name]
+    gu.note("kv_append %s batch %d steps %d" % (name, nb, steps))
+    dev, ref = _kv_case(w, nb, steps)
+    h = dev.host()
+    for a in ("k_codes", "k_meta", "v_codes", "v_meta"):
+        assert np.array_equal(h[a], getattr(ref, a)), a
+
+
+def test_append_one_by_one_equals_bulk_on_gpu():
+    w = W["opt-6.7b"]
+    nb, L = 2, 40
+    k = synth.prompt_kv(w, "k", nb=nb, nt=L)
+    v = synth.prompt_kv(w, "v", nb=nb, nt=L)
+    gu.note("append one-by-one vs bulk")
+    a = gu.DevKV(nb, w.heads, w.head_dim, L)
+    a.append(k, v, 0)
+    b = gu.DevKV(nb, w.heads, w.head_dim, L)
+    for t in range(L):
+        b.append(np.ascontiguousarray(k[:, t:t + 1]), np.ascontiguousarray(v[:, t:t + 1]), t)
+    ha, hb = a.host(), b.host()
+    for key in ha:
+        assert np.array_equal(ha[key], hb[key]), key
+
+
+def _attn_check(dev, ref, q, L, what, out_f16=False, scale=0.0):
+    gu.note("attention %s kv_len %d" % (what, L))
+    got = dev.attend(q, L, scale, out_f16)
+    exp = oracle.decode_attn(ref, q, L, scale)
+    gu.assert_close(got, exp, what)
+
+
+def test_attention_tiny_all_lengths():
+    w = W["tiny"]
+    dev, ref = _kv_case(w, w.batch, 1)
+    q = synth.step_q(w, 1)
+    for L in (1, 2, 63, 64, 65, 127, 128, 129):
+        _attn_check(dev, ref, q, L, "tiny(D=64)")
+
+
+def test_attention_opt67b_reduced_batch_all_steps():
+    w = W["opt-6.7b"]
+    nb, steps = 3, 32
+    dev, ref = _kv_case(w, nb, steps)
+    for t in (1, 2, 17, 31, 32):
+        q = synth.step_q(w, t)[:nb]
+        _attn_check(dev, ref, q, w.kv_len(t), "opt-6.7b b=3 t=%d" % t)
+
+
+def test_attention_long_context_outliers_and_constant_groups():
+    w = W["long-t3"]
+    nb, steps = 2, 2
+    dev, ref = _kv_case(w, nb, steps)
+    for t in (1, 2):
+        q = synth.step_q(w, t)[:nb]
+        _attn_check(dev, ref, q, w.kv_len(t), "long-t3 b=2 t=%d" % t)
+
+
+def test_attention_fp16_output_and_scale():
+    w = W["opt-6.7b"]
+    nb = 2
+    dev, ref = _kv_case(w, nb, 1)
+    q = synth.step_q(w, 1)[:nb]
+    _attn_check(dev, ref, q, 513, "fp16 out", out_f16=True)
+    _attn_check(dev, ref, q, 300, "scale 0.05", scale=0.05)
+
+
+def _full_size_attention_rows(name, t, samples):
+    w = W[name]
+    B, H, D, cap = w.batch, w.heads, w.head_dim, w.capacity
+    gu.note("full-size attention %s B=%d H=%d L=%d" % (name, B, H, w.kv_len(t)))
+    dev = gu.DevKV(B, H, D, cap)
+    chunk = 8
+    for b0 in range(0, B, chunk):
+        nb = min(chunk, B - b0)
+        sub = gu.fgq.kv_struct(dev.k_codes[b0:b0 + nb], dev.v_codes[b0:b0 + nb], dev.k_meta[b0:b0 + nb],
+                               dev.v_meta[b0:b0 + nb], nb, H, D, cap)
+        kd = gu.to_dev(synth.prompt_kv(w, "k", b0=b0, nb=nb))
+        vd = gu.to_dev(synth.prompt_kv(w, "v", b0=b0, nb=nb))
+        gu.fgq.fgq_kv_append(sub, kd, vd, 0, w.prompt)
+        del kd, vd
+    for s in range(1, t + 1):
+        dev.append(synth.step_kv(w, "k", s), synth.step_kv(w, "v", s), w.prompt + s - 1)
+    q = synth.step_q(w, t)
+    got = dev.attend(q, w.kv_len(t))
+    h = dev.host()
+    for b in samples:
+        ref = oracle.KVCache(1, H, D, cap)
+        oracle.kv_append(ref, synth.prompt_kv(w, "k", b0=b, nb=1), synth.prompt_kv(w, "v", b0=b, nb=1), 0)
+        for s in range(1, t + 1):
+            oracle.kv_append(ref, synth.step_kv(w, "k", s)[b:b + 1], synth.step_kv(w, "v", s)[b:b + 1],
+                             w.prompt + s - 1)
+        for a in ("k_codes", "k_meta", "v_codes", "v_meta"):
+            assert np.array_equal(h[a][b], getattr(ref, a)[0]), (a, b)
+        exp = oracle.decode_attn(ref, q[b:b + 1], w.kv_len(t))
+        gu.assert_close(got[b:b + 1], exp, "%s full-size seq %d" % (name, b))
+
+
+@pytest.mark.parametrize("name,t,samples", [("opt-175b", 3, (0, 77, 143)), ("long-t3", 2, (0, 31))])
+def test_attention_full_size_sampled(name, t, samples):
+    _full_size_attention_rows(name, t, samples)
+
+
+def test_attention_result_does_not_depend_on_batch_split_plan():
+    """The same sequences attended alone (long splits merged) and inside a wide
+    batch (one split) agree within tolerance, and each matches the oracle."""
+    w = W["opt-6.7b"]
+    dev, ref = _kv_case(w, 2, 1)
+    q = synth.step_q(w, 1)[:2]
+    L = w.kv_len(1)
+    gu.note("split-plan independence")
+    wide = gu.DevKV(64, w.heads, w.head_dim, dev.cap)
+    for a in ("k_codes", "k_meta", "v_codes", "v_meta"):
+        getattr(wide, a)[:2].copy_(getattr(dev, a))
+        getattr(wide, a)[2:].copy_(getattr(dev, a)[:1].expand(62, -1, -1, -1))
+    qw = np.concatenate([q, np.repeat(q[:1], 62, axis=0)])
+    a1 = dev.attend(q, L)
+    a2 = wide.attend(qw, L)[:2]
+    exp = oracle.decode_attn(ref, q, L)
+    gu.assert_close(a1, exp, "narrow plan")
+    gu.assert_close(a2, exp, "wide plan")
+    assert gu.fgq.fgq_decode_attn_ws_bytes(2, w.heads, w.head_dim, L) > 0
+    assert gu.fgq.fgq_decode_attn_ws_bytes(64, w.heads, w.head_dim, L) >= 0
+
+
+def test_attention_repeatable_bitwise():
+    w = W["long-t3"]
+    dev, ref = _kv_case(w, 1, 1)
+    q = synth.step_q(w, 1)[:1]
+    gu.note("attention repeatability")
+    a = dev.attend(q, w.kv_len(1))
+    b = dev.attend(q, w.kv_len(1))
+    assert np.array_equal(a, b)
+
+
+# --------------------------------------------------------------------------- GEMM
+
+def _gemm_case(x16, g, m, Wt):
+    K, N = Wt.shape
+    codes, meta = gu.quantize(Wt)
+    rc, rm = oracle.quantize_g64(Wt)
+    assert np.array_equal(codes, rc) and np.array_equal(meta, rm)
+    pc, pm = gu.pack(gu.to_dev(codes), gu.to_dev(meta), K, N)
+    return rc, rm, pc, pm
+
+
+def test_pack_matches_layout_definition():
+    rng = np.random.default_rng(3)
+    Wt = (rng.standard_normal((96, 320)) * 0.02).astype(np.float16)
+    gu.note("pack layout 96x320")
+    codes, meta = oracle.quantize_g64(Wt)
+    pc, pm = gu.pack(gu.to_dev(codes), gu.to_dev(meta), 96, 320)
+    ec, em = gu.pack_reference(codes, meta)
+    assert np.array_equal(gu.to_host(pc, np.uint32), ec)
+    assert np.array_equal(gu.to_host(pm, np.uint32), em)
+
+
+@pytest.mark.parametrize("M,K,N", [(1, 32, 64), (5, 96, 320), (16, 64, 256), (17, 160, 64), (37, 256, 512),
+                                   (144, 128, 192), (145, 96, 128), (300, 64, 64), (4, 0, 64)])
+def test_gemm_ragged_shapes(M, K, N):
+    rng = np.random.default_rng(M * 7 + K + N)
+    Wt = (rng.standard_normal((K, N)) * 0.02).astype(np.float16)
+    X = rng.standard_normal((M, K)).astype(np.float16)
+    gu.note("gemm ragged M=%d K=%d N=%d" % (M, K, N))
+    if K == 0:
+        torch = gu.torch_cuda()
+        pc = torch.empty(16, dtype=torch.int32, device="cuda")
+        y = gu.gemm(X, M, 1, pc, pc, K, N)
+        assert np.all(y == 0)
+        return
+    rc, rm, pc, pm = _gemm_case(X, M, 1, Wt)
+    y = gu.gemm(X, M, 1, pc, pm, K, N)
+    gu.assert_close(y, oracle.dequant_gemm(X, M, 1, rc, rm), "gemm %dx%dx%d" % (M, K, N))
+
+
+@pytest.mark.parametrize("name,idx", [("tiny", 0), ("opt-6.7b", 0), ("opt-6.7b", 4), ("opt-6.7b", 5),
+                                      ("opt-30b", 0)])
+def test_gemm_workload_full(name, idx):
+    w = W[name]
+    K, N = w.weights[idx]
+    gu.note("gemm %s[%d] M=%d K=%d N=%d" % (name, idx, w.batch, K, N))
+    Wt = synth.weight(w, idx)
+    X = synth.gemm_x(w, idx, 1)
+    rc, rm, pc, pm = _gemm_case(X, w.g, w.m, Wt)
+    y = gu.gemm(X, w.g, w.m, pc, pm, K, N)
+    gu.assert_close(y, oracle.dequant_gemm(X, w.g, w.m, rc, rm), "gemm %s[%d]" % (name, idx))
+
+
+@pytest.mark.parametrize("idx", [0, 4, 5])
+def test_gemm_opt175b_sampled_columns(idx):
+    """Bench launch configuration (M = 144 = 36 x 4) at full size; the oracle
+    recomputes three 256-column slices (whole weight groups)."""
+    w = W["opt-175b"]
+    K, N = w.weights[idx]
+    gu.note("gemm opt-175b[%d] M=%d K=%d N=%d" % (idx, w.batch, K, N))
+    Wt = synth.weight(w, idx)
+    X = synth.gemm_x(w, idx, 1)
+    codes, meta = gu.quantize(Wt)
+    del Wt
+    pc, pm = gu.pack(gu.to_dev(codes), gu.to_dev(meta), K, N)
+    y = gu.gemm(X, w.g, w.m, pc, pm, K, N)
+    for n0 in (0, N // 2 + 64, N - 256):
+        sl = slice(n0, n0 + 256)
+        c = np.ascontiguousarray(codes[:, n0 // 2:(n0 + 256) // 2])
+        m = np.ascontiguousarray(meta[:, n0 // 64:(n0 + 256) // 64])
+        exp = oracle.dequant_gemm(X, w.g, w.m, c, m)
+        gu.assert_close(y[:, sl], exp, "opt-175b[%d] cols %d.." % (idx, n0))
+
+
+def test_gemm_block_identity_and_determinism():
+    """Y(g, m) against the m GPU batches run one at a time (within tolerance:
+    the launch plan differs), and bitwise repeatability."""
+    rng = np.random.default_rng(9)
+    K, N, g, m = 1024, 512, 36, 4
+    Wt = (rng.standard_normal((K, N)) * 0.02).astype(np.float16)
+    X = rng.standard_normal((g * m, K)).astype(np.float16)
+    rc, rm, pc, pm = _gemm_case(X, g, m, Wt)
+    gu.note("gemm block identity")
+    y = gu.gemm(X, g, m, pc, pm, K, N)
+    y2 = gu.gemm(X, g, m, pc, pm, K, N)
+    assert np.array_equal(y, y2)
+    parts = np.concatenate([gu.gemm(np.ascontiguousarray(X[j * g:(j + 1) * g]), g, 1, pc, pm, K, N)
+                            for j in range(m)])
+    gu.assert_close(y, parts, "block vs per-batch")
+    gu.assert_close(y, oracle.dequant_gemm(X, g, m, rc, rm), "block vs oracle")
+
+
+def test_gemm_fp16_output():
+    w = W["opt-6.7b"]
+    K, N = w.weights[0]
+    Wt = synth.weight(w, 0)
+    X = synth.gemm_x(w, 0, 2)
+    rc, rm, pc, pm = _gemm_case(X, w.g, w.m, Wt)
+    gu.note("gemm fp16 output")
+    y = gu.gemm(X, w.g, w.m, pc, pm, K, N, y_f16=True)
+    exp = oracle.dequant_gemm(X, w.g, w.m, rc, rm)
+    # fp16 rounding of |Y| up to ~8 adds up to 2^-11 relative on top of the fp32 bar
+    gu.assert_close(y, exp, "gemm fp16 out")
+
+
+def test_gpu_rejects_capacity_overflow_without_writing():
+    w = W["tiny"]
+    dev = gu.DevKV(2, w.heads, w.head_dim, 8)
+    k = np.ones((2, 3, w.hidden), np.float16)
+    gu.note("capacity error")
+    with pytest.raises(gu.fgq.FgqError) as e:
+        dev.append(k, k, 6)
+    assert e.value.status == gu.fgq.FGQ_ERR_CAPACITY
+    h = dev.host()
+    assert all(np.all(v == 0) for v in h.values())
