@@ -62,7 +62,7 @@ __device__ __forceinline__ float sum_slots(float v) {
 
 // D = head_dim (64 or 128); CH = token iterations per chunk (even).
 template <int D, int CH>
-__global__ __launch_bounds__(256) void attn_split_kernel(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void attn_split_kernel(
     const uint8_t *__restrict__ kc, const uint32_t *__restrict__ km, const uint8_t *__restrict__ vc,
     const uint32_t *__restrict__ vm, const uint16_t *__restrict__ q, int H, int cap, int L, int n_split,
     int tok_per_split, int total_items, float sl2, float *__restrict__ ws, void *__restrict__ out,
@@ -123,25 +123,29 @@ __global__ __launch_bounds__(256) void attn_split_kernel(
 #pragma unroll
     for (int e = 0; e < 32; ++e) o[e] = 0.f;
 
-    for (int c0 = j0; c0 < j1; c0 += CH * TPI) {
+    struct Chunk {
         uint4 K[CH], V[CH];
         uint32_t KM[CH], VM[CH];
-        bool ok[CH];
+    };
+    // Loads of one chunk of CH*TPI tokens (positions past j1 re-read the
+    // last valid row; their probabilities are zero).
+    auto load = [&](int c0, Chunk &d) {
 #pragma unroll
         for (int it = 0; it < CH; ++it) {
             const int j = c0 + it * TPI + slot;
-            ok[it] = j < j1;
-            const size_t jc = (size_t)(ok[it] ? j : j1 - 1);
-            K[it] = *reinterpret_cast<const uint4 *>(kbase + jc * (D / 2));
-            KM[it] = kmb[jc * G];
-            V[it] = *reinterpret_cast<const uint4 *>(vbase + jc * (D / 2));
-            VM[it] = vmb[jc * G];
+            const size_t jc = (size_t)(j < j1 ? j : j1 - 1);
+            d.K[it] = *reinterpret_cast<const uint4 *>(kbase + jc * (D / 2));
+            d.KM[it] = kmb[jc * G];
+            d.V[it] = *reinterpret_cast<const uint4 *>(vbase + jc * (D / 2));
+            d.VM[it] = vmb[jc * G];
         }
+    };
+    auto process = [&](int c0, const Chunk &d) {
         // ---- scores
         float s[CH];
 #pragma unroll
         for (int it = 0; it < CH; ++it) {
-            const uint32_t w[4] = {K[it].x, K[it].y, K[it].z, K[it].w};
+            const uint32_t w[4] = {d.K[it].x, d.K[it].y, d.K[it].z, d.K[it].w};
             float lo = 0.f, hi = 0.f;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -152,23 +156,27 @@ __global__ __launch_bounds__(256) void attn_split_kernel(
                 hi = dot2(w8 & 0x00F000F0u, QP[i][3], hi);
             }
             const float sc = lo * 16777216.0f + hi * 1048576.0f;   // sum_d q_d c_d
-            const float step = h2f((uint16_t)(KM[it] >> 16));
-            const float mn = h2f((uint16_t)(KM[it] & 0xffffu));
+            const float step = h2f((uint16_t)(d.KM[it] >> 16));
+            const float mn = h2f((uint16_t)(d.KM[it] & 0xffffu));
             const float part_s = step * sc + mn * qsum;
             const float tot = sum_parts<PARTS>(part_s);
-            s[it] = ok[it] ? tot * sl2 : -INFINITY;
+            s[it] = (c0 + it * TPI + slot < j1) ? tot * sl2 : -INFINITY;
         }
         float cm = s[0];
 #pragma unroll
         for (int it = 1; it < CH; ++it) cm = fmaxf(cm, s[it]);
         cm = max_slots<PARTS>(cm);
-        const float m_new = fmaxf(m_run, cm);
-        const float corr = exp2f(m_run - m_new);
-        m_run = m_new;
-        l_acc *= corr;
-        macc *= corr;
+        // the running max only moves now and then: rescale only when it does
+        // (m_run and cm are the same in every lane, so the branch is uniform)
+        if (cm > m_run) {
+            const float corr = exp2f(m_run - cm);
+            m_run = cm;
+            l_acc *= corr;
+            macc *= corr;
 #pragma unroll
-        for (int e = 0; e < 32; ++e) o[e] *= corr;
+            for (int e = 0; e < 32; ++e) o[e] *= corr;
+        }
+        const float m_new = m_run;
 
         // ---- P.V, two tokens (it, it + CH/2) per dot2
 #pragma unroll
@@ -176,8 +184,8 @@ __global__ __launch_bounds__(256) void attn_split_kernel(
             const int ia = pi, ib = pi + CH / 2;
             const float pa = exp2f(s[ia] - m_new), pb = exp2f(s[ib] - m_new);
             l_acc += pa + pb;
-            const float sa = h2f((uint16_t)(VM[ia] >> 16)), sb = h2f((uint16_t)(VM[ib] >> 16));
-            macc += pa * h2f((uint16_t)(VM[ia] & 0xffffu)) + pb * h2f((uint16_t)(VM[ib] & 0xffffu));
+            const float sa = h2f((uint16_t)(d.VM[ia] >> 16)), sb = h2f((uint16_t)(d.VM[ib] >> 16));
+            macc += pa * h2f((uint16_t)(d.VM[ia] & 0xffffu)) + pb * h2f((uint16_t)(d.VM[ib] & 0xffffu));
             const float wa = pa * sa, wb = pb * sb;
             const _Float16 wa_h = (_Float16)wa, wb_h = (_Float16)wb;
             const _Float16 wa_l = (_Float16)(wa - (float)wa_h), wb_l = (_Float16)(wb - (float)wb_h);
@@ -185,8 +193,8 @@ __global__ __launch_bounds__(256) void attn_split_kernel(
             whi.x = wa_h; whi.y = wb_h;
             wlo.x = wa_l; wlo.y = wb_l;
             const uint32_t WH = as_u32(whi), WL = as_u32(wlo);
-            const uint32_t A[4] = {V[ia].x, V[ia].y, V[ia].z, V[ia].w};
-            const uint32_t Bv[4] = {V[ib].x, V[ib].y, V[ib].z, V[ib].w};
+            const uint32_t A[4] = {d.V[ia].x, d.V[ia].y, d.V[ia].z, d.V[ia].w};
+            const uint32_t Bv[4] = {d.V[ib].x, d.V[ib].y, d.V[ib].z, d.V[ib].w};
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 // X = [A.b0, A.b1, B.b0, B.b1], Y = [A.b2, A.b3, B.b2, B.b3]
@@ -202,6 +210,22 @@ __global__ __launch_bounds__(256) void attn_split_kernel(
                 }
             }
         }
+    };
+
+    // Two register buffers: the loads of the next chunk are in flight while
+    // the current one is processed.
+    constexpr int STEP = CH * TPI;
+    Chunk bufA, bufB;
+    int c0 = j0;
+    if (c0 < j1) load(c0, bufA);
+    while (c0 < j1) {
+        if (c0 + STEP < j1) load(c0 + STEP, bufB);
+        process(c0, bufA);
+        c0 += STEP;
+        if (c0 >= j1) break;
+        if (c0 + STEP < j1) load(c0 + STEP, bufA);
+        process(c0, bufB);
+        c0 += STEP;
     }
 
     // ---- reduce the token slots: o (per element) through LDS, l and macc by shuffles
