@@ -38,18 +38,31 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
     return __builtin_amdgcn_fdot2(as_f16x2(a), as_f16x2(b), c, false);
 }
 
+// DPP lane shuffles (a VALU operand modifier, no LDS round trip).
+// quad_perm [1,0,3,2] = xor 1, [2,3,0,1] = xor 2; row_ror:n rotates the 16
+// lanes of a row by n.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+constexpr int kQuadXor1 = 0xB1, kQuadXor2 = 0x4E, kRowRor4 = 0x124, kRowRor8 = 0x128;
+
+// Sum over the PARTS consecutive lanes of one token.
 template <int PARTS>
 __device__ __forceinline__ float sum_parts(float v) {
-    // lanes of one token are PARTS consecutive lanes
-    v += __shfl_xor(v, 1, 64);
-    if (PARTS == 4) v += __shfl_xor(v, 2, 64);
+    v += dpp<kQuadXor1>(v);
+    if (PARTS == 4) v += dpp<kQuadXor2>(v);
     return v;
 }
 
+// Max over all token slots of the wave (the parts of a token hold equal values).
 template <int PARTS>
 __device__ __forceinline__ float max_slots(float v) {
-#pragma unroll
-    for (int s = PARTS; s < 64; s <<= 1) v = fmaxf(v, __shfl_xor(v, s, 64));
+    if (PARTS == 2) v = fmaxf(v, dpp<kQuadXor2>(v));
+    v = fmaxf(v, dpp<kRowRor4>(v));
+    v = fmaxf(v, dpp<kRowRor8>(v));
+    v = fmaxf(v, __shfl_xor(v, 16, 64));
+    v = fmaxf(v, __shfl_xor(v, 32, 64));
     return v;
 }
 
@@ -59,6 +72,9 @@ __device__ __forceinline__ float sum_slots(float v) {
     for (int s = PARTS; s < 64; s <<= 1) v += __shfl_xor(v, s, 64);
     return v;
 }
+
+// 2^x on the transcendental unit (x <= 0 here; tiny results may flush to 0).
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // D = head_dim (64 or 128); CH = token iterations per chunk (even).
 template <int D, int CH>
@@ -169,7 +185,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
         // the running max only moves now and then: rescale only when it does
         // (m_run and cm are the same in every lane, so the branch is uniform)
         if (cm > m_run) {
-            const float corr = exp2f(m_run - cm);
+            const float corr = fast_exp2(m_run - cm);
             m_run = cm;
             l_acc *= corr;
             macc *= corr;
@@ -182,7 +198,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
 #pragma unroll
         for (int pi = 0; pi < CH / 2; ++pi) {
             const int ia = pi, ib = pi + CH / 2;
-            const float pa = exp2f(s[ia] - m_new), pb = exp2f(s[ib] - m_new);
+            const float pa = fast_exp2(s[ia] - m_new), pb = fast_exp2(s[ib] - m_new);
             l_acc += pa + pb;
             const float sa = h2f((uint16_t)(d.VM[ia] >> 16)), sb = h2f((uint16_t)(d.VM[ib] >> 16));
             macc += pa * h2f((uint16_t)(d.VM[ia] & 0xffffu)) + pb * h2f((uint16_t)(d.VM[ib] & 0xffffu));

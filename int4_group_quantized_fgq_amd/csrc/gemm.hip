@@ -13,17 +13,17 @@
 //  * a workgroup is 8 waves (512 output channels, two waves per SIMD) and
 //    shares the X rows of each K chunk through LDS;
 //  * every operand reaches LDS through gfx950's direct global->LDS loads
-//    (global_load_lds_dwordx4) into a ring of 8 one-chunk slots (32 k each:
-//    the X rows, each wave's packed code words and its group metadata), so 7
-//    chunks are in flight while one is multiplied, with one barrier per chunk
-//    and no register spent on prefetching;
+//    (global_load_lds_dwordx4) into a ring of 4 slots of two 32-k chunks
+//    each (the X rows, each wave's packed code words and its group
+//    metadata), so 3 slots are in flight while one is multiplied, with one
+//    barrier per slot and no register spent on prefetching;
 //  * the packed weight layout puts the 8 k-values of one output channel in
 //    one 32-bit word, in the nibble order that AND/OR with the fp16 magic
 //    numbers 0x6400 (1024 + q) and 0x5400 (64 + q) turn into two values per
 //    op; a packed subtract and a packed FMA give two fp16 W^ values, and the
 //    next chunk is dequantised in the shadow of the current chunk's MFMAs;
-//  * X rows sit in LDS with a 16-byte-slot XOR swizzle (slot ^ (row/4)%4),
-//    so the 16 rows of an A fragment read hit distinct banks;
+//  * X rows sit in LDS with a 16-byte-slot XOR swizzle, so the rows of an A
+//    fragment read hit distinct banks;
 //  * K is split across workgroups when the N/512 workgroups cannot fill the
 //    CUs; fp32 partial tiles are summed in split order by a second kernel.
 #include <cmath>
@@ -36,7 +36,8 @@ namespace {
 
 constexpr int kWaves = 8;                  // waves (weight groups) per workgroup
 constexpr int kThreads = 64 * kWaves;
-constexpr int kRing = 8;                   // LDS chunk slots: kRing-1 chunks in flight
+constexpr int kSC = 2;                     // 32-k chunks per LDS ring slot (one barrier per slot)
+constexpr int kRing = 8 / kSC;             // ring slots: kRing-1 slots in flight
 
 // Direct global->LDS load of 16 bytes per lane: lane i's bytes land at
 // lds_ptr + 16*i (lds_ptr must be the same in every lane).  Written as inline
@@ -68,20 +69,33 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
-// Wait until at most `chunks` chunks of this wave's loads are outstanding;
-// a wave issues `cnt` (2, 3 or 4) load instructions per chunk.
-template <int CHUNKS>
-__device__ __forceinline__ void wait_chunks(int cnt) {
-    if (cnt == 2) wait_vmcnt<2 * CHUNKS>();
-    else if (cnt == 3) wait_vmcnt<3 * CHUNKS>();
-    else wait_vmcnt<4 * CHUNKS>();
+// Wait until at most `SLOTS` ring slots of this wave's loads are
+// outstanding; a wave issues `cnt` (2..7) load instructions per slot.
+template <int SLOTS>
+__device__ __forceinline__ void wait_slots(int cnt) {
+    switch (cnt) {
+        case 2: wait_vmcnt<2 * SLOTS>(); break;
+        case 3: wait_vmcnt<3 * SLOTS>(); break;
+        case 4: wait_vmcnt<4 * SLOTS>(); break;
+        case 5: wait_vmcnt<5 * SLOTS>(); break;
+        case 6: wait_vmcnt<6 * SLOTS>(); break;
+        default: wait_vmcnt<7 * SLOTS>(); break;
+    }
 }
+
+// 16-byte slot swizzle of the X rows in LDS: element (row, slot c) is stored
+// at slot c ^ xswz(row).  For the 16 rows of one A-fragment read (one slot
+// column each), any 8 consecutive rows then cover all eight 16-byte pieces
+// of a 128-byte bank cycle and the 16 rows cover all sixteen pieces of a
+// 256-byte cycle, so the read is free of bank conflicts.
+__device__ __forceinline__ int xswz(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
 
 template <int MT>
 struct Cfg {
-    static constexpr int XBYTES = MT * 1024;           // MT*16 rows x 64 bytes (one 32-k chunk)
-    static constexpr int BBYTES = kWaves * 1024;       // packed codes, 1 KB per wave
-    static constexpr int MBYTES = kWaves * 128;        // packed meta, 128 B per wave
+    static constexpr int XCHUNK = MT * 1024;           // MT*16 rows x 64 bytes (one 32-k chunk)
+    static constexpr int XBYTES = kSC * XCHUNK;
+    static constexpr int BBYTES = kWaves * kSC * 1024; // packed codes, 1 KB per wave and chunk
+    static constexpr int MBYTES = kWaves * kSC * 128;  // packed meta, 128 B per wave and chunk
     static constexpr int SLOT = XBYTES + BBYTES + MBYTES;
     static constexpr int LDS = kRing * SLOT;
 };
@@ -107,10 +121,11 @@ void dq_gemm_kernel(const uint16_t *__restrict__ x, int M, int64_t K, int64_t N,
     int64_t c_end = c_begin + chunks_per_split;
     if (c_end > nchunks) c_end = nchunks;
 
-    // X blocks (16 rows x 64 B) of a chunk are spread over the waves:
+    // X blocks (16 rows x 64 B) of a slot are spread over the waves:
     // block b is loaded by wave b % kWaves.
-    const int nx = MT / kWaves + (wv < MT % kWaves ? 1 : 0);
-    const int cnt = nx + 2;                      // load instructions per chunk for this wave
+    constexpr int XBLK = MT * kSC;
+    const int nx = XBLK / kWaves + (wv < XBLK % kWaves ? 1 : 0);
+    const int cnt = nx + kSC + 1;                // load instructions per slot for this wave
 
     f32x4 acc[MT][4];
 #pragma unroll
@@ -120,35 +135,54 @@ void dq_gemm_kernel(const uint16_t *__restrict__ x, int M, int64_t K, int64_t N,
 
     const int arow = lane & 15, akq = lane >> 4;
 
-    // Issue this wave's direct-to-LDS loads of chunk kc into ring slot `slot`.
-    // Chunks past c_end (the tail of the ring) and rows past M are clamped to
-    // valid addresses; those values are never used for a stored output.
-    auto issue = [&](int64_t kc, int slot) {
-        if (kc >= c_end) kc = c_end - 1;
+    // Issue this wave's direct-to-LDS loads of the kSC chunks that start at
+    // chunk kc into ring slot `slot`.  Chunks past c_end (the tail of the
+    // ring) and rows past M are clamped to valid addresses; those values are
+    // never used for a stored output.
+    auto issue = [&](int64_t kc0, int slot) {
         uint8_t *base = lds + slot * C::SLOT;
 #pragma unroll
-        for (int t = 0; t < (MT + kWaves - 1) / kWaves; ++t) {
+        for (int t = 0; t < (XBLK + kWaves - 1) / kWaves; ++t) {
             const int blk = t * kWaves + wv;
-            if (blk < MT) {
-                const int row = blk * 16 + (lane >> 2);
-                const int c16 = (lane & 3) ^ ((row >> 2) & 3);     // swizzled source column
+            if (blk < XBLK) {
+                const int ch = blk / MT, rb = blk - ch * MT;
+                int64_t kc = kc0 + ch;
+                if (kc >= c_end) kc = c_end - 1;
+                const int row = rb * 16 + (lane >> 2);
+                const int c16 = (lane & 3) ^ xswz(row);            // swizzled source column
                 const int grow = (m0 + row < M) ? m0 + row : M - 1;
                 dma16(x + (int64_t)grow * K + kc * 32 + c16 * 8, base + blk * 1024);
             }
         }
-        const int64_t tile = kc * ng + gl;
-        dma16(pc + (tile * 64 + lane) * 4, base + C::XBYTES + wv * 1024);
-        if (lane < 8) dma16(pm + tile * 32 + lane * 4, base + C::XBYTES + C::BBYTES + wv * 128);
+#pragma unroll
+        for (int ch = 0; ch < kSC; ++ch) {
+            int64_t kc = kc0 + ch;
+            if (kc >= c_end) kc = c_end - 1;
+            const int64_t tile = kc * ng + gl;
+            dma16(pc + (tile * 64 + lane) * 4, base + C::XBYTES + (wv * kSC + ch) * 1024);
+        }
+        if (lane < 8 * kSC) {
+            int64_t kc = kc0 + (lane >> 3);
+            if (kc >= c_end) kc = c_end - 1;
+            const int64_t tile = kc * ng + gl;
+            dma16(pm + tile * 32 + (lane & 7) * 4, base + C::XBYTES + C::BBYTES + wv * kSC * 128);
+        }
     };
+
+    // The fp16 magic numbers live in VGPRs so that the AND/OR pairs below
+    // become single v_and_or_b32 (a VOP3 operand may not be a literal here).
+    uint32_t mag1024, mag64;
+    asm volatile("v_mov_b32 %0, 0x64006400" : "=v"(mag1024));
+    asm volatile("v_mov_b32 %0, 0x54005400" : "=v"(mag64));
 
     // Packed codes + (step, min) pairs of one chunk -> B fragment j.
     auto dequant_j = [&](const uint4 cw, const uint4 ms, const uint4 mm, int j) -> f16x8 {
         const uint32_t W[4] = {cw.x, cw.y, cw.z, cw.w};
         const uint32_t w = W[j], w8 = w >> 8;
-        const uint32_t p0 = (w & 0x000F000Fu) | 0x64006400u;    // 1024 + q (k0, k1)
-        const uint32_t p1 = (w & 0x00F000F0u) | 0x54005400u;    // 64 + q   (k2, k3)
-        const uint32_t p2 = (w8 & 0x000F000Fu) | 0x64006400u;   // 1024 + q (k4, k5)
-        const uint32_t p3 = (w8 & 0x00F000F0u) | 0x54005400u;   // 64 + q   (k6, k7)
+        const uint32_t p0 = (w & 0x000F000Fu) | mag1024;    // 1024 + q (k0, k1)
+        const uint32_t p1 = (w & 0x00F000F0u) | mag64;      // 64 + q   (k2, k3)
+        const uint32_t p2 = (w8 & 0x000F000Fu) | mag1024;   // 1024 + q (k4, k5)
+        const uint32_t p3 = (w8 & 0x00F000F0u) | mag64;     // 64 + q   (k6, k7)
         const f16x2 c01 = as_f16x2(p0) - f16x2{(_Float16)1024.0f, (_Float16)1024.0f};
         const f16x2 c23 = as_f16x2(p1) - f16x2{(_Float16)64.0f, (_Float16)64.0f};
         const f16x2 c45 = as_f16x2(p2) - f16x2{(_Float16)1024.0f, (_Float16)1024.0f};
@@ -159,63 +193,87 @@ void dq_gemm_kernel(const uint16_t *__restrict__ x, int M, int64_t K, int64_t N,
         const f16x2 w67 = __builtin_elementwise_fma(c67, as_f16x2(ms.w), as_f16x2(mm.w));
         return f16x8{w01.x, w01.y, w23.x, w23.y, w45.x, w45.y, w67.x, w67.y};
     };
-    // B words of ring slot `slot` for this wave; keep == 0 turns them into a
-    // zero weight (step 0, min 0), used for a chunk past the end of the split.
-    auto load_b = [&](int slot, uint32_t keep, uint4 &cw, uint4 &ms, uint4 &mm) {
+    // B words of chunk `ch` of ring slot `slot` for this wave.  A chunk past
+    // the end of the split (its data is a clamped copy) gets step 0 and min 0,
+    // so its W^ is zero and it adds nothing (a uniform branch: the chunk index
+    // is the same in every lane).
+    auto load_b = [&](int slot, int ch, bool valid, uint4 &cw, uint4 &ms, uint4 &mm) {
         const uint8_t *base = lds + slot * C::SLOT;
-        cw = *reinterpret_cast<const uint4 *>(base + C::XBYTES + wv * 1024 + lane * 16);
-        const uint8_t *mb = base + C::XBYTES + C::BBYTES + wv * 128 + akq * 32;
+        cw = *reinterpret_cast<const uint4 *>(base + C::XBYTES + (wv * kSC + ch) * 1024 + lane * 16);
+        const uint8_t *mb = base + C::XBYTES + C::BBYTES + (wv * kSC + ch) * 128 + akq * 32;
         ms = *reinterpret_cast<const uint4 *>(mb);
         mm = *reinterpret_cast<const uint4 *>(mb + 16);
-        ms.x &= keep; ms.y &= keep; ms.z &= keep; ms.w &= keep;
-        mm.x &= keep; mm.y &= keep; mm.z &= keep; mm.w &= keep;
+        if (!valid) {
+            ms = make_uint4(0u, 0u, 0u, 0u);
+            mm = ms;
+        }
     };
-    auto a_frag = [&](int slot, int i) {
+    auto a_frag = [&](int slot, int ch, int i) {
         const int row = i * 16 + arow;
-        return *reinterpret_cast<const f16x8 *>(lds + slot * C::SLOT + row * 64 + ((akq ^ ((row >> 2) & 3)) * 16));
+        return *reinterpret_cast<const f16x8 *>(lds + slot * C::SLOT + ch * C::XCHUNK + row * 64 +
+                                                ((akq ^ xswz(row)) * 16));
     };
 
-    const int64_t nmine = c_end - c_begin;       // chunks of this split (>= 1 when the loop runs)
-    f16x8 bcur[4], bnext[4];
+    const int64_t nmine = c_end - c_begin;       // chunks of this split
+    const int64_t nslots = (nmine + kSC - 1) / kSC;
+    // B fragments: bf[ch % 2] feeds chunk ch of a slot while bf[(ch+1) % 2]
+    // receives the next chunk's; with an even number of chunks per slot the
+    // roles swap statically and no register copy is needed.
+    static_assert(kSC % 2 == 0, "B fragment double buffer assumes an even number of chunks per slot");
+    f16x8 bf[2][4];
     if (nmine > 0) {
 #pragma unroll
-        for (int r = 0; r < kRing - 1; ++r) issue(c_begin + r, r);
-        wait_chunks<kRing - 2>(cnt);             // this wave's B words of the first chunk
+        for (int r = 0; r < kRing - 1; ++r) issue(c_begin + (int64_t)r * kSC, r);
+        wait_slots<kRing - 2>(cnt);              // this wave's B words of the first slot
         uint4 cw, ms, mm;
-        load_b(0, 0xFFFFFFFFu, cw, ms, mm);
+        load_b(0, 0, true, cw, ms, mm);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) bcur[j] = dequant_j(cw, ms, mm, j);
+        for (int j = 0; j < 4; ++j) bf[0][j] = dequant_j(cw, ms, mm, j);
     }
-    for (int64_t it = 0; it < nmine; ++it) {
-        const int slot = (int)(it % kRing);
-        wait_chunks<kRing - 3>(cnt);             // chunks it and it+1 of this wave have landed
-        lds_barrier();                           // ... for every wave; slot it-1 is free again
-        issue(c_begin + it + kRing - 1, (int)((it + kRing - 1) % kRing));
-        // MFMAs of chunk it, m-tile by m-tile; the A fragment of the next
-        // m-tile is read first and, after the first m-tiles, one n-tile of the
-        // next chunk's B fragments is dequantised; the scheduling fences keep
-        // the VALU work and the LDS latency under the matrix-core time.
-        uint4 cw, ms, mm;
-        load_b((int)((it + 1) % kRing), it + 1 < nmine ? 0xFFFFFFFFu : 0u, cw, ms, mm);
-        f16x8 a_cur = a_frag(slot, 0);
+    for (int64_t st = 0; st < nslots; ++st) {
+        const int slot = (int)(st % kRing);
+        const int nslot = (int)((st + 1) % kRing);
+        wait_slots<kRing - 3>(cnt);              // slots st and st+1 of this wave have landed
+        lds_barrier();                           // ... for every wave; slot st-1 is free again
 #pragma unroll
-        for (int i = 0; i < MT; ++i) {
-            f16x8 a_nxt;
-            if (i + 1 < MT) a_nxt = a_frag(slot, i + 1);
+        for (int ch = 0; ch < kSC; ++ch) {
+            // MFMAs of one chunk, m-tile by m-tile.  A fragments are read two
+            // m-tiles ahead; in the first chunk of the slot, the loads refilling
+            // the freed slot are issued once the first MFMAs are in flight;
+            // after each of the first m-tiles one n-tile of the next chunk's B
+            // fragments is dequantised.  The scheduling fences keep that order,
+            // so the address arithmetic, the VALU dequant and the LDS latency
+            // sit under the matrix-core time.
+            const int64_t chunk = st * kSC + ch;
+            uint4 cw, ms, mm;
+            if (ch + 1 < kSC)
+                load_b(slot, ch + 1, chunk + 1 < nmine, cw, ms, mm);
+            else
+                load_b(nslot, 0, chunk + 1 < nmine, cw, ms, mm);
+            const f16x8(&bcur)[4] = bf[ch % 2];
+            f16x8(&bnext)[4] = bf[(ch + 1) % 2];
+            f16x8 a0 = a_frag(slot, ch, 0);
+            f16x8 a1 = a_frag(slot, ch, MT > 1 ? 1 : 0);
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_cur, bcur[j], acc[i][j], 0, 0, 0);
-            if (MT >= 4) {
-                if (i < 4) bnext[i] = dequant_j(cw, ms, mm, i);
-            } else if (i == MT - 1) {
+            for (int i = 0; i < MT; ++i) {
+                f16x8 a2;
+                if (i + 2 < MT) a2 = a_frag(slot, ch, i + 2);
 #pragma unroll
-                for (int j = 0; j < 4; ++j) bnext[j] = dequant_j(cw, ms, mm, j);
+                for (int j = 0; j < 4; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, bcur[j], acc[i][j], 0, 0, 0);
+                if (ch == 0 && i == 0)
+                    issue(c_begin + (st + kRing - 1) * kSC, (int)((st + kRing - 1) % kRing));
+                if (MT >= 4) {
+                    if (i < 4) bnext[i] = dequant_j(cw, ms, mm, i);
+                } else if (i == MT - 1) {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) bnext[j] = dequant_j(cw, ms, mm, j);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                a0 = a1;
+                if (i + 2 < MT) a1 = a2;
             }
-            __builtin_amdgcn_sched_barrier(0);
-            if (i + 1 < MT) a_cur = a_nxt;
         }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) bcur[j] = bnext[j];
     }
     wait_vmcnt<0>();     // no load may still be writing LDS when the workgroup ends
 
@@ -299,9 +357,10 @@ struct GemmPlan {
 
 // Split-K plan.  One 8-wave workgroup per CU (the LDS ring takes most of
 // the CU's 160 KB).  The time of a plan is modelled as (workgroups per CU) x
-// (chunks per split) x (time of one 32-k chunk of one workgroup, ~0.8 us at
-// 144 rows) plus writing and re-reading the fp32 partial tiles (~5 TB/s) and
-// one extra launch for the reduction.
+// (chunks per split x time of one 32-k chunk, ~0.88 us at 144 rows, plus the
+// ring fill and epilogue) plus writing and re-reading the fp32 partial tiles
+// and one extra launch for the reduction; the constants are fitted to split
+// sweeps on MI355X over the OPT-shaped weights.
 GemmPlan gemm_plan(int64_t M, int64_t K, int64_t N) {
     GemmPlan p{};
     const int64_t mt_needed = (M + 15) / 16;
@@ -310,16 +369,17 @@ GemmPlan gemm_plan(int64_t M, int64_t K, int64_t N) {
     p.nblocks = ((N / 64) + kWaves - 1) / kWaves;
     const int64_t nchunks = K / 32;
     const int64_t base = p.nblocks * (p.mblocks > 0 ? p.mblocks : 1);
-    const double chunk_us = 0.1 + 0.7 * p.mt / 9.0;
-    const double bytes_per_us = 5.0e6;
+    const double chunk_us = 0.1 + 0.78 * p.mt / 9.0;    // one 32-k chunk of one workgroup
+    const double ramp_us = 4.0;                          // ring fill and epilogue of a workgroup
+    const double bytes_per_us = 3.0e6;                   // partial tile write + read, ~6 TB/s each
     double best = 1e300;
     int best_ks = 1;
     for (int ks = 1; ks <= 64; ++ks) {
         const int64_t cps = (nchunks + ks - 1) / ks;
         if (ks > 1 && (cps * (ks - 1) >= nchunks || cps < 8)) break;   // empty or too short splits
         const double per_cu = std::ceil((double)base * ks / kNumCU);
-        const double t = per_cu * (double)cps * chunk_us +
-                         (ks > 1 ? (double)(ks + 1) * (double)M * (double)N * 4.0 / bytes_per_us + 4.0 : 0.0);
+        const double t = per_cu * ((double)cps * chunk_us + ramp_us) +
+                         (ks > 1 ? (double)ks * (double)M * (double)N * 4.0 / bytes_per_us + 3.0 : 0.0);
         if (t < best) { best = t; best_ks = ks; }
     }
     int64_t cps = (nchunks + best_ks - 1) / best_ks;
