@@ -169,8 +169,9 @@ fgq_status fgq_pack_weight_g64(const uint8_t *codes, const uint32_t *meta, int64
  *   packed_codes / packed_meta from fgq_pack_weight_g64 for W [K][N];
  *   y  [g*m][N] in y_dtype.
  * W^ is restored to fp16 (W^ = fp16(min + q*step)) and multiplied on the
- * fp16 matrix cores with fp32 accumulation.  Requires K % 32 == 0 and
- * N % 64 == 0; g*m == 0 is a no-op.
+ * fp16 matrix cores with fp32 accumulation.  Requires K % 32 == 0,
+ * N % 64 == 0, K <= 2^23 and N <= 2^28 (FGQ_ERR_SHAPE otherwise); g*m == 0
+ * is a no-op.
  *   ws / ws_bytes: at least fgq_dequant_gemm_ws_bytes(g*m, K, N) bytes of
  *   workspace (split-K partial sums; may be NULL when that is 0).
  */

@@ -158,6 +158,7 @@ fgq_status fgq_dequant_gemm(const void *x_f16, int32_t g, int32_t m, int64_t K, 
     if (y_dtype != FGQ_DTYPE_F32 && y_dtype != FGQ_DTYPE_F16) return fail(FGQ_ERR_DTYPE, "y_dtype %d", y_dtype);
     const int64_t M = (int64_t)g * m;
     if (M > (int64_t)1 << 30) return fail(FGQ_ERR_SHAPE, "g*m too large");
+    if (K > (int64_t)1 << 23 || N > (int64_t)1 << 28) return fail(FGQ_ERR_SHAPE, "K > 2^23 or N > 2^28");
     if (M == 0 || N == 0) return FGQ_OK;
     if (!y || (K > 0 && (!x_f16 || !packed_codes || !packed_meta))) return fail(FGQ_ERR_INVALID_ARG, "NULL array");
     if (!aligned16(y) || (K > 0 && (!aligned16(x_f16) || !aligned16(packed_codes) || !aligned16(packed_meta))))

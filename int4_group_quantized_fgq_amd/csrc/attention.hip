@@ -76,6 +76,14 @@ __device__ __forceinline__ float sum_slots(float v) {
 // 2^x on the transcendental unit (x <= 0 here; tiny results may flush to 0).
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// 16-byte streaming load: the cache rows are read once per step, so the
+// loads are marked nontemporal (they do not displace other data in the
+// caches), which streams measurably faster than plain loads on MI355X.
+__device__ __forceinline__ uint4 stream_load16(const uint8_t *p) {
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+    return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
 // D = head_dim (64 or 128); CH = token iterations per chunk (even).
 template <int D, int CH>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void attn_split_kernel(
@@ -150,10 +158,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
         for (int it = 0; it < CH; ++it) {
             const int j = c0 + it * TPI + slot;
             const size_t jc = (size_t)(j < j1 ? j : j1 - 1);
-            d.K[it] = *reinterpret_cast<const uint4 *>(kbase + jc * (D / 2));
-            d.KM[it] = kmb[jc * G];
-            d.V[it] = *reinterpret_cast<const uint4 *>(vbase + jc * (D / 2));
-            d.VM[it] = vmb[jc * G];
+            d.K[it] = stream_load16(kbase + jc * (D / 2));
+            d.KM[it] = __builtin_nontemporal_load(kmb + jc * G);
+            d.V[it] = stream_load16(vbase + jc * (D / 2));
+            d.VM[it] = __builtin_nontemporal_load(vmb + jc * G);
         }
     };
     auto process = [&](int c0, const Chunk &d) {

@@ -39,20 +39,28 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kSC = 2;                     // 32-k chunks per LDS ring slot (one barrier per slot)
 constexpr int kRing = 8 / kSC;             // ring slots: kRing-1 slots in flight
 
-// Direct global->LDS load of 16 bytes per lane: lane i's bytes land at
-// lds_ptr + 16*i (lds_ptr must be the same in every lane).  Written as inline
-// assembly so the compiler does not track it as an LDS store: it would
-// otherwise drain every load in flight (s_waitcnt vmcnt(0)) before each LDS
-// read of the ring, since it cannot prove that the slot being filled differs
-// from the slots being read.  The kernel waits for exactly the chunks it
-// needs with explicit vmcnt counts instead.  M0 (the LDS base of the load)
+// LDS byte address of a pointer into a __shared__ array.
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
+}
+
+// Direct global->LDS load of 16 bytes per lane from sbase + voff (sbase is
+// wave-uniform and lives in SGPRs, voff is the lane's 32-bit byte offset);
+// lane i's bytes land at LDS address lds + 16*i (lds wave-uniform).  Written
+// as inline assembly so the compiler does not track it as an LDS store: it
+// would otherwise drain every load in flight (s_waitcnt vmcnt(0)) before each
+// LDS read of the ring, since it cannot prove that the slot being filled
+// differs from the slots being read.  The kernel waits for exactly the chunks
+// it needs with explicit vmcnt counts instead.  M0 (the LDS base of the load)
 // is used by nothing else in this kernel.
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void dma16(const void *gptr, const void *lds_ptr) {
-    const uint32_t la = __builtin_amdgcn_readfirstlane(
-        (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)lds_ptr);
-    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "s"(la) : "memory", "m0");
+__device__ __forceinline__ void dma16(const void *sbase, uint32_t voff, uint32_t lds) {
+    // readfirstlane keeps the LDS address in an SGPR also inside a lane-masked
+    // branch, where the compiler may otherwise hold the uniform value in a VGPR.
+    const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds);
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(m0v)
+                 : "memory", "m0");
 }
 #pragma clang diagnostic pop
 
@@ -84,11 +92,11 @@ __device__ __forceinline__ void wait_slots(int cnt) {
 }
 
 // 16-byte slot swizzle of the X rows in LDS: element (row, slot c) is stored
-// at slot c ^ xswz(row).  For the 16 rows of one A-fragment read (one slot
-// column each), any 8 consecutive rows then cover all eight 16-byte pieces
-// of a 128-byte bank cycle and the 16 rows cover all sixteen pieces of a
-// 256-byte cycle, so the read is free of bank conflicts.
-__device__ __forceinline__ int xswz(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
+// at slot c ^ xswz(row).  Among any 8 consecutive rows of an A-fragment read
+// (one slot column each), the four rows of equal parity get four different
+// slots, so the 8 lanes of one 128-byte bank cycle hit distinct banks.  The
+// swizzle repeats every 8 rows, so it is the same for every 16-row m-tile.
+__device__ __forceinline__ int xswz(int row) { return (row >> 1) & 3; }
 
 template <int MT>
 struct Cfg {
@@ -107,25 +115,57 @@ void dq_gemm_kernel(const uint16_t *__restrict__ x, int M, int64_t K, int64_t N,
                     float *__restrict__ part, void *__restrict__ y, int y_f16, int ksplit) {
     using C = Cfg<MT>;
     __shared__ __attribute__((aligned(1024))) uint8_t lds[C::LDS];
+    const uint32_t lds0 = lds_addr(lds);
 
     const int lane = threadIdx.x & 63;
-    const int wv = threadIdx.x >> 6;
+    const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+
+    // Workgroups are dealt to the 8 XCDs round-robin in launch order.  Remap
+    // the launch index so that each XCD gets a contiguous run of tiles in
+    // (column block fastest, then split) order: the tiles of one split share
+    // their X slice, which then stays in that XCD's L2 instead of being
+    // fetched by every XCD.
+    const int nbx = gridDim.x, nby = gridDim.y;
+    const int total = nbx * nby * gridDim.z;
+    const int lin = blockIdx.x + nbx * (blockIdx.y + nby * blockIdx.z);
+    const int xcd = lin & 7, per = total >> 3, extra = total & 7;
+    const int tile = xcd * per + (xcd < extra ? xcd : extra) + (lin >> 3);
+    const int bx = tile % nbx, by = (tile / nbx) % nby, bz = tile / (nbx * nby);
+
     const int64_t ng = N >> 6;
-    const int64_t g = (int64_t)blockIdx.x * kWaves + wv;
+    const int64_t g = (int64_t)bx * kWaves + wv;
     const bool gvalid = g < ng;
     const int64_t gl = gvalid ? g : ng - 1;      // clamped group for loads
-    const int split = blockIdx.y;
-    const int m0 = blockIdx.z * MT * 16;
-    const int64_t nchunks = K >> 5;
-    const int64_t c_begin = (int64_t)split * chunks_per_split;
-    int64_t c_end = c_begin + chunks_per_split;
+    const int split = by;
+    const int m0 = bz * MT * 16;
+    // Chunk indices fit in 32 bits (K <= 2^23), so their compares stay scalar.
+    const int nchunks = (int)(K >> 5);
+    const int c_begin = split * chunks_per_split;
+    int c_end = c_begin + chunks_per_split;
     if (c_end > nchunks) c_end = nchunks;
 
     // X blocks (16 rows x 64 B) of a slot are spread over the waves:
     // block b is loaded by wave b % kWaves.
     constexpr int XBLK = MT * kSC;
+    constexpr int XT = (XBLK + kWaves - 1) / kWaves;
     const int nx = XBLK / kWaves + (wv < XBLK % kWaves ? 1 : 0);
     const int cnt = nx + kSC + 1;                // load instructions per slot for this wave
+
+    // Loop-invariant lane offsets of the loads (the per-chunk part of every
+    // address is wave-uniform and stays in SGPRs).  X rows past M are
+    // clamped to row M-1; those rows are never stored.
+    const uint16_t *xm = x + (int64_t)m0 * K;
+    uint32_t xoff[XT];
+#pragma unroll
+    for (int t = 0; t < XT; ++t) {
+        const int blk = t * kWaves + wv;
+        const int rb = blk % MT;
+        const int row = rb * 16 + (lane >> 2);
+        const int64_t grow = (m0 + row < M) ? row : M - 1 - m0;
+        xoff[t] = (uint32_t)(grow * K * 2 + (((lane & 3) ^ xswz(row)) * 16));
+    }
+    const uint32_t coff = (uint32_t)lane * 16;
+    const uint32_t moff = (uint32_t)((lane >> 3) * ng * 128 + (lane & 7) * 16);
 
     f32x4 acc[MT][4];
 #pragma unroll
@@ -134,39 +174,33 @@ void dq_gemm_kernel(const uint16_t *__restrict__ x, int M, int64_t K, int64_t N,
         for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     const int arow = lane & 15, akq = lane >> 4;
+    const int aoff = arow * 64 + ((akq ^ xswz(arow)) * 16);
 
     // Issue this wave's direct-to-LDS loads of the kSC chunks that start at
-    // chunk kc into ring slot `slot`.  Chunks past c_end (the tail of the
-    // ring) and rows past M are clamped to valid addresses; those values are
-    // never used for a stored output.
-    auto issue = [&](int64_t kc0, int slot) {
-        uint8_t *base = lds + slot * C::SLOT;
+    // chunk kc0 into ring slot `slot`.  Chunks past c_end (the tail of the
+    // ring) are clamped to the last chunk of the split; a chunk past c_end is
+    // never multiplied.
+    auto issue = [&](int kc0, int slot) {
+        const uint32_t sb = lds0 + slot * C::SLOT;
 #pragma unroll
-        for (int t = 0; t < (XBLK + kWaves - 1) / kWaves; ++t) {
+        for (int t = 0; t < XT; ++t) {
             const int blk = t * kWaves + wv;
             if (blk < XBLK) {
-                const int ch = blk / MT, rb = blk - ch * MT;
-                int64_t kc = kc0 + ch;
+                int kc = kc0 + blk / MT;
                 if (kc >= c_end) kc = c_end - 1;
-                const int row = rb * 16 + (lane >> 2);
-                const int c16 = (lane & 3) ^ xswz(row);            // swizzled source column
-                const int grow = (m0 + row < M) ? m0 + row : M - 1;
-                dma16(x + (int64_t)grow * K + kc * 32 + c16 * 8, base + blk * 1024);
+                dma16(xm + (int64_t)kc * 32, xoff[t], sb + blk * 1024);
             }
         }
 #pragma unroll
         for (int ch = 0; ch < kSC; ++ch) {
-            int64_t kc = kc0 + ch;
+            int kc = kc0 + ch;
             if (kc >= c_end) kc = c_end - 1;
-            const int64_t tile = kc * ng + gl;
-            dma16(pc + (tile * 64 + lane) * 4, base + C::XBYTES + (wv * kSC + ch) * 1024);
+            dma16(pc + ((int64_t)kc * ng + gl) * 256, coff, sb + C::XBYTES + (wv * kSC + ch) * 1024);
         }
-        if (lane < 8 * kSC) {
-            int64_t kc = kc0 + (lane >> 3);
-            if (kc >= c_end) kc = c_end - 1;
-            const int64_t tile = kc * ng + gl;
-            dma16(pm + tile * 32 + (lane & 7) * 4, base + C::XBYTES + C::BBYTES + wv * kSC * 128);
-        }
+        const int kc = kc0 < c_end ? kc0 : c_end - 1;
+        const int left = c_end - kc;
+        const int nmeta = 8 * (left < kSC ? left : kSC);
+        if (lane < nmeta) dma16(pm + ((int64_t)kc * ng + gl) * 32, moff, sb + C::XBYTES + C::BBYTES + wv * kSC * 128);
     };
 
     // The fp16 magic numbers live in VGPRs so that the AND/OR pairs below
@@ -175,103 +209,109 @@ void dq_gemm_kernel(const uint16_t *__restrict__ x, int M, int64_t K, int64_t N,
     asm volatile("v_mov_b32 %0, 0x64006400" : "=v"(mag1024));
     asm volatile("v_mov_b32 %0, 0x54005400" : "=v"(mag64));
 
-    // Packed codes + (step, min) pairs of one chunk -> B fragment j.
-    auto dequant_j = [&](const uint4 cw, const uint4 ms, const uint4 mm, int j) -> f16x8 {
+    // Half h (0..7) of the dequantisation of one chunk's B fragments: n-tile
+    // j = h/2, k-values 0..3 (h even) or 4..7 (h odd) of the packed word.
+    // The code pairs become 1024 + q and 64 + q in fp16 through AND/OR with
+    // the magic numbers; a packed subtract and a packed FMA give the fp16 W^.
+    auto dequant_half = [&](const uint4 cw, const uint4 ms, const uint4 mm, int h, u32x4(&b)[4]) {
+        const int j = h >> 1;
         const uint32_t W[4] = {cw.x, cw.y, cw.z, cw.w};
-        const uint32_t w = W[j], w8 = w >> 8;
-        const uint32_t p0 = (w & 0x000F000Fu) | mag1024;    // 1024 + q (k0, k1)
-        const uint32_t p1 = (w & 0x00F000F0u) | mag64;      // 64 + q   (k2, k3)
-        const uint32_t p2 = (w8 & 0x000F000Fu) | mag1024;   // 1024 + q (k4, k5)
-        const uint32_t p3 = (w8 & 0x00F000F0u) | mag64;     // 64 + q   (k6, k7)
-        const f16x2 c01 = as_f16x2(p0) - f16x2{(_Float16)1024.0f, (_Float16)1024.0f};
-        const f16x2 c23 = as_f16x2(p1) - f16x2{(_Float16)64.0f, (_Float16)64.0f};
-        const f16x2 c45 = as_f16x2(p2) - f16x2{(_Float16)1024.0f, (_Float16)1024.0f};
-        const f16x2 c67 = as_f16x2(p3) - f16x2{(_Float16)64.0f, (_Float16)64.0f};
-        const f16x2 w01 = __builtin_elementwise_fma(c01, as_f16x2(ms.x), as_f16x2(mm.x));
-        const f16x2 w23 = __builtin_elementwise_fma(c23, as_f16x2(ms.y), as_f16x2(mm.y));
-        const f16x2 w45 = __builtin_elementwise_fma(c45, as_f16x2(ms.z), as_f16x2(mm.z));
-        const f16x2 w67 = __builtin_elementwise_fma(c67, as_f16x2(ms.w), as_f16x2(mm.w));
-        return f16x8{w01.x, w01.y, w23.x, w23.y, w45.x, w45.y, w67.x, w67.y};
+        const uint32_t w = (h & 1) ? W[j] >> 8 : W[j];
+        const uint32_t s0 = (h & 1) ? ms.z : ms.x, s1 = (h & 1) ? ms.w : ms.y;
+        const uint32_t n0 = (h & 1) ? mm.z : mm.x, n1 = (h & 1) ? mm.w : mm.y;
+        const uint32_t p0 = (w & 0x000F000Fu) | mag1024;
+        const uint32_t p1 = (w & 0x00F000F0u) | mag64;
+        const f16x2 c0 = as_f16x2(p0) - f16x2{(_Float16)1024.0f, (_Float16)1024.0f};
+        const f16x2 c1 = as_f16x2(p1) - f16x2{(_Float16)64.0f, (_Float16)64.0f};
+        const f16x2 w0 = __builtin_elementwise_fma(c0, as_f16x2(s0), as_f16x2(n0));
+        const f16x2 w1 = __builtin_elementwise_fma(c1, as_f16x2(s1), as_f16x2(n1));
+        const uint32_t u0 = __builtin_bit_cast(uint32_t, w0), u1 = __builtin_bit_cast(uint32_t, w1);
+        // An empty use pins the values here: the next chunk may be past the
+        // end of the split, and without it the compiler sinks this work past
+        // that test, out of the MFMA shadow.
+        asm volatile("" ::"v"(u0), "v"(u1));
+        b[j][(h & 1) * 2] = u0;
+        b[j][(h & 1) * 2 + 1] = u1;
     };
-    // B words of chunk `ch` of ring slot `slot` for this wave.  A chunk past
-    // the end of the split (its data is a clamped copy) gets step 0 and min 0,
-    // so its W^ is zero and it adds nothing (a uniform branch: the chunk index
-    // is the same in every lane).
-    auto load_b = [&](int slot, int ch, bool valid, uint4 &cw, uint4 &ms, uint4 &mm) {
+    // Packed code words and (step, min) pairs of chunk `ch` of ring slot `slot`.
+    auto load_b = [&](int slot, int ch, uint4 &cw, uint4 &ms, uint4 &mm) {
         const uint8_t *base = lds + slot * C::SLOT;
         cw = *reinterpret_cast<const uint4 *>(base + C::XBYTES + (wv * kSC + ch) * 1024 + lane * 16);
         const uint8_t *mb = base + C::XBYTES + C::BBYTES + (wv * kSC + ch) * 128 + akq * 32;
         ms = *reinterpret_cast<const uint4 *>(mb);
         mm = *reinterpret_cast<const uint4 *>(mb + 16);
-        if (!valid) {
-            ms = make_uint4(0u, 0u, 0u, 0u);
-            mm = ms;
-        }
     };
     auto a_frag = [&](int slot, int ch, int i) {
-        const int row = i * 16 + arow;
-        return *reinterpret_cast<const f16x8 *>(lds + slot * C::SLOT + ch * C::XCHUNK + row * 64 +
-                                                ((akq ^ xswz(row)) * 16));
+        return *reinterpret_cast<const f16x8 *>(lds + slot * C::SLOT + ch * C::XCHUNK + i * 1024 + aoff);
     };
 
-    const int64_t nmine = c_end - c_begin;       // chunks of this split
-    const int64_t nslots = (nmine + kSC - 1) / kSC;
+    const int nmine = c_end - c_begin;           // chunks of this split
+    const int nslots = (nmine + kSC - 1) / kSC;
     // B fragments: bf[ch % 2] feeds chunk ch of a slot while bf[(ch+1) % 2]
     // receives the next chunk's; with an even number of chunks per slot the
     // roles swap statically and no register copy is needed.
     static_assert(kSC % 2 == 0, "B fragment double buffer assumes an even number of chunks per slot");
-    f16x8 bf[2][4];
+    u32x4 bf[2][4];
     if (nmine > 0) {
 #pragma unroll
-        for (int r = 0; r < kRing - 1; ++r) issue(c_begin + (int64_t)r * kSC, r);
-        wait_slots<kRing - 2>(cnt);              // this wave's B words of the first slot
+        for (int r = 0; r < kRing - 1; ++r) issue(c_begin + r * kSC, r);
+        wait_slots<kRing - 2>(cnt);              // this wave's loads of the first slot
         uint4 cw, ms, mm;
-        load_b(0, 0, true, cw, ms, mm);
+        load_b(0, 0, cw, ms, mm);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) bf[0][j] = dequant_j(cw, ms, mm, j);
+        for (int h = 0; h < 8; ++h) dequant_half(cw, ms, mm, h, bf[0]);
     }
-    for (int64_t st = 0; st < nslots; ++st) {
-        const int slot = (int)(st % kRing);
-        const int nslot = (int)((st + 1) % kRing);
-        wait_slots<kRing - 3>(cnt);              // slots st and st+1 of this wave have landed
-        lds_barrier();                           // ... for every wave; slot st-1 is free again
+    // The ring is unrolled so that every slot offset is an immediate.
+    for (int s0 = 0; s0 < nslots; s0 += kRing) {
 #pragma unroll
-        for (int ch = 0; ch < kSC; ++ch) {
-            // MFMAs of one chunk, m-tile by m-tile.  A fragments are read two
-            // m-tiles ahead; in the first chunk of the slot, the loads refilling
-            // the freed slot are issued once the first MFMAs are in flight;
-            // after each of the first m-tiles one n-tile of the next chunk's B
-            // fragments is dequantised.  The scheduling fences keep that order,
-            // so the address arithmetic, the VALU dequant and the LDS latency
-            // sit under the matrix-core time.
-            const int64_t chunk = st * kSC + ch;
-            uint4 cw, ms, mm;
-            if (ch + 1 < kSC)
-                load_b(slot, ch + 1, chunk + 1 < nmine, cw, ms, mm);
-            else
-                load_b(nslot, 0, chunk + 1 < nmine, cw, ms, mm);
-            const f16x8(&bcur)[4] = bf[ch % 2];
-            f16x8(&bnext)[4] = bf[(ch + 1) % 2];
-            f16x8 a0 = a_frag(slot, ch, 0);
-            f16x8 a1 = a_frag(slot, ch, MT > 1 ? 1 : 0);
+        for (int r = 0; r < kRing; ++r) {
+            const int st = s0 + r;
+            if (st >= nslots) break;
+            wait_slots<kRing - 2>(cnt);          // slot st of this wave has landed
+            lds_barrier();                       // ... for every wave; slot st-1 is free again
 #pragma unroll
-            for (int i = 0; i < MT; ++i) {
-                f16x8 a2;
-                if (i + 2 < MT) a2 = a_frag(slot, ch, i + 2);
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, bcur[j], acc[i][j], 0, 0, 0);
-                if (ch == 0 && i == 0)
-                    issue(c_begin + (st + kRing - 1) * kSC, (int)((st + kRing - 1) % kRing));
-                if (MT >= 4) {
-                    if (i < 4) bnext[i] = dequant_j(cw, ms, mm, i);
-                } else if (i == MT - 1) {
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) bnext[j] = dequant_j(cw, ms, mm, j);
+            for (int ch = 0; ch < kSC; ++ch) {
+                // MFMAs of one chunk, m-tile by m-tile.  A fragments are read
+                // two m-tiles ahead; in the first chunk of the slot, the loads
+                // refilling the freed slot are issued once the first MFMAs are
+                // in flight; the next chunk's B fragments are dequantised in
+                // eight halves spread over the m-tiles, each half interleaved
+                // with the MFMAs so the VALU work runs in their shadow.
+                if (st * kSC + ch >= nmine) break;
+                uint4 cw, ms, mm;
+                if (ch + 1 < kSC) {
+                    load_b(r, ch + 1, cw, ms, mm);
+                } else {
+                    // B words of the next slot are this wave's own loads: its
+                    // vmcnt is enough, the barrier comes with that slot.
+                    wait_slots<kRing - 2>(cnt);
+                    load_b((r + 1) % kRing, 0, cw, ms, mm);
                 }
-                __builtin_amdgcn_sched_barrier(0);
-                a0 = a1;
-                if (i + 2 < MT) a1 = a2;
+                const u32x4(&bcur)[4] = bf[ch % 2];
+                u32x4(&bnext)[4] = bf[(ch + 1) % 2];
+                f16x8 a0 = a_frag(r, ch, 0);
+                f16x8 a1 = a_frag(r, ch, MT > 1 ? 1 : 0);
+#pragma unroll
+                for (int i = 0; i < MT; ++i) {
+                    f16x8 a2;
+                    if (i + 2 < MT) a2 = a_frag(r, ch, i + 2);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                            a0, __builtin_bit_cast(f16x8, bcur[j]), acc[i][j], 0, 0, 0);
+                    if (ch == 0 && i == 0) issue(c_begin + (st + kRing - 1) * kSC, (r + kRing - 1) % kRing);
+#pragma unroll
+                    for (int h = 0; h < 8; ++h)
+                        if ((h * MT) / 8 == i) dequant_half(cw, ms, mm, h, bnext);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+                        __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);   // then two VALU ops
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                    a0 = a1;
+                    if (i + 2 < MT) a1 = a2;
+                }
             }
         }
     }
@@ -399,6 +439,8 @@ fgq_status launch_dequant_gemm(const void *x, int64_t M, int64_t K, int64_t N, c
                                const uint32_t *pm, void *y, int32_t y_dtype, void *ws, hipStream_t stream) {
     if (M == 0 || N == 0) return FGQ_OK;
     const GemmPlan p = gemm_plan(M, K, N);
+    if (p.mblocks > 65535 || (double)p.nblocks * p.ksplit * p.mblocks >= 2147483648.0)
+        return fail(FGQ_ERR_SHAPE, "dequant GEMM grid too large (M=%lld N=%lld)", (long long)M, (long long)N);
     const int f16 = y_dtype == FGQ_DTYPE_F16;
     const dim3 grid((unsigned)p.nblocks, (unsigned)p.ksplit, (unsigned)p.mblocks);
     const uint16_t *xh = static_cast<const uint16_t *>(x);
