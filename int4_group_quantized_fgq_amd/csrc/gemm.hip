@@ -98,27 +98,40 @@ __device__ __forceinline__ void wait_slots(int cnt) {
 // swizzle repeats every 8 rows, so it is the same for every 16-row m-tile.
 __device__ __forceinline__ int xswz(int row) { return (row >> 1) & 3; }
 
-template <int MT>
+// Ring and LDS layout of a workgroup with MT m-tiles and KP k-phases: the
+// 8 waves are CG = 8/KP column groups x KP phases; phase p multiplies the
+// chunks p, p+KP, ... of every slot, and the phases' accumulators are summed
+// through LDS at the end.
+template <int MT, int KP>
 struct Cfg {
+    static constexpr int CG = kWaves / KP;             // column groups (64 channels each)
+    static constexpr int LC = kSC / KP;                // chunks per wave and slot
     static constexpr int XCHUNK = MT * 1024;           // MT*16 rows x 64 bytes (one 32-k chunk)
     static constexpr int XBYTES = kSC * XCHUNK;
-    static constexpr int BBYTES = kWaves * kSC * 1024; // packed codes, 1 KB per wave and chunk
-    static constexpr int MBYTES = kWaves * kSC * 128;  // packed meta, 128 B per wave and chunk
+    static constexpr int BBYTES = kWaves * LC * 1024;  // packed codes, 1 KB per wave and chunk
+    static constexpr int MBYTES = kWaves * LC * 128;   // packed meta, 128 B per wave and chunk
     static constexpr int SLOT = XBYTES + BBYTES + MBYTES;
-    static constexpr int LDS = kRing * SLOT;
+    static constexpr int RING = kRing * SLOT;
+    static constexpr int RED = (KP - 1) * CG * MT * 4 * 64 * 16;   // accumulators of phases 1..KP-1
+    static constexpr int LDS = RING > RED ? RING : RED;
+    static_assert(kSC % KP == 0, "every phase takes the same number of chunks of a slot");
+    static_assert((kRing * LC) % 2 == 0, "B fragment double buffer needs an even chunk count per ring turn");
+    static_assert(LDS <= 160 * 1024, "LDS budget");
 };
 
-template <int MT>
+template <int MT, int KP>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void dq_gemm_kernel(const uint16_t *__restrict__ x, int M, int64_t K, int64_t N,
                     const uint32_t *__restrict__ pc, const uint32_t *__restrict__ pm, int chunks_per_split,
                     float *__restrict__ part, void *__restrict__ y, int y_f16, int ksplit) {
-    using C = Cfg<MT>;
+    using C = Cfg<MT, KP>;
+    constexpr int CG = C::CG, LC = C::LC;
     __shared__ __attribute__((aligned(1024))) uint8_t lds[C::LDS];
     const uint32_t lds0 = lds_addr(lds);
 
     const int lane = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int cg = wv % CG, phase = wv / CG;
 
     // Workgroups are dealt to the 8 XCDs round-robin in launch order.  Remap
     // the launch index so that each XCD gets a contiguous run of tiles in
@@ -133,7 +146,7 @@ void dq_gemm_kernel(const uint16_t *__restrict__ x, int M, int64_t K, int64_t N,
     const int bx = tile % nbx, by = (tile / nbx) % nby, bz = tile / (nbx * nby);
 
     const int64_t ng = N >> 6;
-    const int64_t g = (int64_t)bx * kWaves + wv;
+    const int64_t g = (int64_t)bx * CG + cg;
     const bool gvalid = g < ng;
     const int64_t gl = gvalid ? g : ng - 1;      // clamped group for loads
     const int split = by;
@@ -149,7 +162,7 @@ void dq_gemm_kernel(const uint16_t *__restrict__ x, int M, int64_t K, int64_t N,
     constexpr int XBLK = MT * kSC;
     constexpr int XT = (XBLK + kWaves - 1) / kWaves;
     const int nx = XBLK / kWaves + (wv < XBLK % kWaves ? 1 : 0);
-    const int cnt = nx + kSC + 1;                // load instructions per slot for this wave
+    const int cnt = nx + LC + 1;                 // load instructions per slot for this wave
 
     // Loop-invariant lane offsets of the loads (the per-chunk part of every
     // address is wave-uniform and stays in SGPRs).  X rows past M are
@@ -165,7 +178,7 @@ void dq_gemm_kernel(const uint16_t *__restrict__ x, int M, int64_t K, int64_t N,
         xoff[t] = (uint32_t)(grow * K * 2 + (((lane & 3) ^ xswz(row)) * 16));
     }
     const uint32_t coff = (uint32_t)lane * 16;
-    const uint32_t moff = (uint32_t)((lane >> 3) * ng * 128 + (lane & 7) * 16);
+    const uint32_t moff = (uint32_t)((lane >> 3) * KP * ng * 128 + (lane & 7) * 16);
 
     f32x4 acc[MT][4];
 #pragma unroll
@@ -174,12 +187,13 @@ void dq_gemm_kernel(const uint16_t *__restrict__ x, int M, int64_t K, int64_t N,
         for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     const int arow = lane & 15, akq = lane >> 4;
-    const int aoff = arow * 64 + ((akq ^ xswz(arow)) * 16);
+    const int aoff = phase * C::XCHUNK + arow * 64 + ((akq ^ xswz(arow)) * 16);
 
-    // Issue this wave's direct-to-LDS loads of the kSC chunks that start at
-    // chunk kc0 into ring slot `slot`.  Chunks past c_end (the tail of the
-    // ring) are clamped to the last chunk of the split; a chunk past c_end is
-    // never multiplied.
+    // Issue this wave's direct-to-LDS loads for the slot of kSC chunks that
+    // starts at chunk kc0: its share of the X blocks and the code words and
+    // metadata of its own chunks kc0 + phase + lc*KP.  Chunks past c_end (the
+    // tail of the ring) are clamped to the last chunk of the split; a chunk
+    // past c_end is never multiplied.
     auto issue = [&](int kc0, int slot) {
         const uint32_t sb = lds0 + slot * C::SLOT;
 #pragma unroll
@@ -191,16 +205,17 @@ void dq_gemm_kernel(const uint16_t *__restrict__ x, int M, int64_t K, int64_t N,
                 dma16(xm + (int64_t)kc * 32, xoff[t], sb + blk * 1024);
             }
         }
+        const int k1 = kc0 + phase;              // this wave's first chunk of the slot
 #pragma unroll
-        for (int ch = 0; ch < kSC; ++ch) {
-            int kc = kc0 + ch;
+        for (int lc = 0; lc < LC; ++lc) {
+            int kc = k1 + lc * KP;
             if (kc >= c_end) kc = c_end - 1;
-            dma16(pc + ((int64_t)kc * ng + gl) * 256, coff, sb + C::XBYTES + (wv * kSC + ch) * 1024);
+            dma16(pc + ((int64_t)kc * ng + gl) * 256, coff, sb + C::XBYTES + (wv * LC + lc) * 1024);
         }
-        const int kc = kc0 < c_end ? kc0 : c_end - 1;
-        const int left = c_end - kc;
-        const int nmeta = 8 * (left < kSC ? left : kSC);
-        if (lane < nmeta) dma16(pm + ((int64_t)kc * ng + gl) * 32, moff, sb + C::XBYTES + C::BBYTES + wv * kSC * 128);
+        const int kc = k1 < c_end ? k1 : c_end - 1;
+        const int left = (c_end - kc + KP - 1) / KP;     // own chunks left from kc on (>= 1)
+        const int nmeta = 8 * (left < LC ? left : LC);
+        if (lane < nmeta) dma16(pm + ((int64_t)kc * ng + gl) * 32, moff, sb + C::XBYTES + C::BBYTES + wv * LC * 128);
     };
 
     // The fp16 magic numbers live in VGPRs so that the AND/OR pairs below
@@ -233,33 +248,46 @@ void dq_gemm_kernel(const uint16_t *__restrict__ x, int M, int64_t K, int64_t N,
         b[j][(h & 1) * 2] = u0;
         b[j][(h & 1) * 2 + 1] = u1;
     };
-    // Packed code words and (step, min) pairs of chunk `ch` of ring slot `slot`.
-    auto load_b = [&](int slot, int ch, uint4 &cw, uint4 &ms, uint4 &mm) {
+    // Packed code words and (step, min) pairs of this wave's chunk lc of ring
+    // slot `slot`.
+    auto load_b = [&](int slot, int lc, uint4 &cw, uint4 &ms, uint4 &mm) {
         const uint8_t *base = lds + slot * C::SLOT;
-        cw = *reinterpret_cast<const uint4 *>(base + C::XBYTES + (wv * kSC + ch) * 1024 + lane * 16);
-        const uint8_t *mb = base + C::XBYTES + C::BBYTES + (wv * kSC + ch) * 128 + akq * 32;
+        cw = *reinterpret_cast<const uint4 *>(base + C::XBYTES + (wv * LC + lc) * 1024 + lane * 16);
+        const uint8_t *mb = base + C::XBYTES + C::BBYTES + (wv * LC + lc) * 128 + akq * 32;
         ms = *reinterpret_cast<const uint4 *>(mb);
         mm = *reinterpret_cast<const uint4 *>(mb + 16);
     };
-    auto a_frag = [&](int slot, int ch, int i) {
-        return *reinterpret_cast<const f16x8 *>(lds + slot * C::SLOT + ch * C::XCHUNK + i * 1024 + aoff);
+    // A fragment of m-tile i of this wave's chunk lc of ring slot `slot`.
+    auto a_frag = [&](int slot, int lc, int i) {
+        return *reinterpret_cast<const f16x8 *>(lds + slot * C::SLOT + lc * KP * C::XCHUNK + i * 1024 + aoff);
     };
 
     const int nmine = c_end - c_begin;           // chunks of this split
     const int nslots = (nmine + kSC - 1) / kSC;
-    // B fragments: bf[ch % 2] feeds chunk ch of a slot while bf[(ch+1) % 2]
-    // receives the next chunk's; with an even number of chunks per slot the
-    // roles swap statically and no register copy is needed.
-    static_assert(kSC % 2 == 0, "B fragment double buffer assumes an even number of chunks per slot");
+    // B fragments: bf[n % 2] feeds this wave's n-th chunk of a ring turn
+    // while bf[(n+1) % 2] receives the next one's; with an even number of
+    // chunks per ring turn the roles swap statically, with no register copy.
     u32x4 bf[2][4];
+    // A fragments stream through two registers, PD m-tiles ahead of the
+    // MFMAs, across chunk and slot boundaries.  The barrier that makes slot
+    // st+1 visible (every wave's loads of it have landed) and frees slot st
+    // (every wave's LDS reads of it are complete) is taken inside the last
+    // chunk of slot st, just before the first read of slot st+1, while PD
+    // m-tiles of MFMAs with operands already in registers remain: the LDS
+    // latency after the barrier hides behind them.
+    constexpr int PD = MT >= 2 ? 2 : 1;
+    f16x8 a0, a1;
     if (nmine > 0) {
 #pragma unroll
         for (int r = 0; r < kRing - 1; ++r) issue(c_begin + r * kSC, r);
         wait_slots<kRing - 2>(cnt);              // this wave's loads of the first slot
+        lds_barrier();                           // ... and every wave's
         uint4 cw, ms, mm;
         load_b(0, 0, cw, ms, mm);
 #pragma unroll
         for (int h = 0; h < 8; ++h) dequant_half(cw, ms, mm, h, bf[0]);
+        a0 = a_frag(0, 0, 0);
+        if (PD == 2) a1 = a_frag(0, 0, 1);
     }
     // The ring is unrolled so that every slot offset is an immediate.
     for (int s0 = 0; s0 < nslots; s0 += kRing) {
@@ -267,57 +295,111 @@ void dq_gemm_kernel(const uint16_t *__restrict__ x, int M, int64_t K, int64_t N,
         for (int r = 0; r < kRing; ++r) {
             const int st = s0 + r;
             if (st >= nslots) break;
-            wait_slots<kRing - 2>(cnt);          // slot st of this wave has landed
-            lds_barrier();                       // ... for every wave; slot st-1 is free again
 #pragma unroll
-            for (int ch = 0; ch < kSC; ++ch) {
-                // MFMAs of one chunk, m-tile by m-tile.  A fragments are read
-                // two m-tiles ahead; in the first chunk of the slot, the loads
-                // refilling the freed slot are issued once the first MFMAs are
-                // in flight; the next chunk's B fragments are dequantised in
-                // eight halves spread over the m-tiles, each half interleaved
-                // with the MFMAs so the VALU work runs in their shadow.
-                if (st * kSC + ch >= nmine) break;
+            for (int lc = 0; lc < LC; ++lc) {
+                // MFMAs of one chunk, m-tile by m-tile.  With the first chunk
+                // of the slot, the loads refilling slot st-1 are issued once
+                // the first MFMAs are in flight; the next chunk's B fragments
+                // are dequantised in eight halves spread over the m-tiles,
+                // each half interleaved with the MFMAs so the VALU work runs
+                // in their shadow.  A wave only leaves this loop early in the
+                // last slot, which takes no barrier.
+                if (st * kSC + phase + lc * KP >= nmine) break;
+                // The next chunk's B words: in this slot, or (last chunk of
+                // the slot) this wave's own loads of the next slot, for which
+                // its vmcnt is enough.  Slot st+1 is only certain to have
+                // landed once this slot's refill is issued (at most kRing-2
+                // slots outstanding after it), so in a slot's first chunk
+                // that load waits for the refill and the dequantisation
+                // starts one m-tile later.
+                const bool last = lc + 1 == LC;
+                const bool late = last && lc == 0;
                 uint4 cw, ms, mm;
-                if (ch + 1 < kSC) {
-                    load_b(r, ch + 1, cw, ms, mm);
-                } else {
-                    // B words of the next slot are this wave's own loads: its
-                    // vmcnt is enough, the barrier comes with that slot.
+                if (!last) {
+                    load_b(r, lc + 1, cw, ms, mm);
+                } else if (!late) {
                     wait_slots<kRing - 2>(cnt);
                     load_b((r + 1) % kRing, 0, cw, ms, mm);
                 }
-                const u32x4(&bcur)[4] = bf[ch % 2];
-                u32x4(&bnext)[4] = bf[(ch + 1) % 2];
-                f16x8 a0 = a_frag(r, ch, 0);
-                f16x8 a1 = a_frag(r, ch, MT > 1 ? 1 : 0);
+                const int bi = (r * LC + lc) % 2;
+                const u32x4(&bcur)[4] = bf[bi];
+                u32x4(&bnext)[4] = bf[bi ^ 1];
 #pragma unroll
                 for (int i = 0; i < MT; ++i) {
-                    f16x8 a2;
-                    if (i + 2 < MT) a2 = a_frag(r, ch, i + 2);
+                    const int f = i + PD;                // fragment to prefetch
+                    f16x8 an;
+                    if (f < MT) {
+                        an = a_frag(r, lc, f);
+                    } else if (!last) {
+                        an = a_frag(r, lc + 1, f - MT);
+                    } else {
+                        if (f == MT && st + 1 < nslots) {
+                            wait_slots<kRing - 2>(cnt);  // slot st+1 of this wave has landed
+                            lds_barrier();
+                        }
+                        an = a_frag((r + 1) % kRing, 0, f - MT);
+                    }
 #pragma unroll
                     for (int j = 0; j < 4; ++j)
                         acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
                             a0, __builtin_bit_cast(f16x8, bcur[j]), acc[i][j], 0, 0, 0);
-                    if (ch == 0 && i == 0) issue(c_begin + (st + kRing - 1) * kSC, (r + kRing - 1) % kRing);
+                    if (lc == 0 && i == 0) {
+                        issue(c_begin + (st + kRing - 1) * kSC, (r + kRing - 1) % kRing);
+                        if (late) {
+                            wait_slots<kRing - 2>(cnt);
+                            load_b((r + 1) % kRing, 0, cw, ms, mm);
+                        }
+                    }
 #pragma unroll
-                    for (int h = 0; h < 8; ++h)
-                        if ((h * MT) / 8 == i) dequant_half(cw, ms, mm, h, bnext);
+                    for (int h = 0; h < 8; ++h) {
+                        const int at = (late && MT > 1) ? 1 + (h * (MT - 1)) / 8 : (h * MT) / 8;
+                        if (at == i) dequant_half(cw, ms, mm, h, bnext);
+                    }
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
                         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
                         __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);   // then two VALU ops
                     }
                     __builtin_amdgcn_sched_barrier(0);
-                    a0 = a1;
-                    if (i + 2 < MT) a1 = a2;
+                    if (PD == 2) {
+                        a0 = a1;
+                        a1 = an;
+                    } else {
+                        a0 = an;
+                    }
                 }
             }
         }
     }
-    wait_vmcnt<0>();     // no load may still be writing LDS when the workgroup ends
+    wait_vmcnt<0>();     // no load may still be writing LDS when the ring is reused or the workgroup ends
 
-    if (!gvalid) return;
+    if constexpr (KP > 1) {
+        // Sum the phases in LDS, in phase order: phases 1..KP-1 park their
+        // accumulators (lane-major, so reads and writes are conflict-free),
+        // phase 0 adds them.
+        f32x4 *red = reinterpret_cast<f32x4 *>(lds);
+        lds_barrier();                           // every wave is done with the ring
+        if (phase > 0) {
+            f32x4 *mine = red + (size_t)((phase - 1) * CG + cg) * MT * 4 * 64 + lane;
+#pragma unroll
+            for (int i = 0; i < MT; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) mine[(i * 4 + j) * 64] = acc[i][j];
+        }
+        lds_barrier();
+        if (phase == 0) {
+#pragma unroll
+            for (int p = 1; p < KP; ++p) {
+                const f32x4 *other = red + (size_t)((p - 1) * CG + cg) * MT * 4 * 64 + lane;
+#pragma unroll
+                for (int i = 0; i < MT; ++i)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) acc[i][j] += other[(i * 4 + j) * 64];
+            }
+        }
+    }
+
+    if (!gvalid || phase != 0) return;
     // ---- store: lane holds rows 4*(lane/16)+r, column lane%16 of each 16x16 tile
     const int crow = (lane >> 4) * 4, ccol = lane & 15;
     const int64_t col0 = g * 64 + ccol;
@@ -380,9 +462,12 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *__restr
 }
 
 template <int MT>
-void launch_mt(dim3 grid, hipStream_t stream, const uint16_t *x, int M, int64_t K, int64_t N, const uint32_t *pc,
-               const uint32_t *pm, int cps, float *part, void *y, int f16, int ksplit) {
-    dq_gemm_kernel<MT><<<grid, dim3(kThreads), 0, stream>>>(x, M, K, N, pc, pm, cps, part, y, f16, ksplit);
+void launch_mt(int kp, dim3 grid, hipStream_t stream, const uint16_t *x, int M, int64_t K, int64_t N,
+               const uint32_t *pc, const uint32_t *pm, int cps, float *part, void *y, int f16, int ksplit) {
+    if (kp == 2)
+        dq_gemm_kernel<MT, 2><<<grid, dim3(kThreads), 0, stream>>>(x, M, K, N, pc, pm, cps, part, y, f16, ksplit);
+    else
+        dq_gemm_kernel<MT, 1><<<grid, dim3(kThreads), 0, stream>>>(x, M, K, N, pc, pm, cps, part, y, f16, ksplit);
 }
 
 }  // namespace
@@ -390,38 +475,48 @@ void launch_mt(dim3 grid, hipStream_t stream, const uint16_t *x, int M, int64_t 
 struct GemmPlan {
     int mt;              // 16-row tiles per M block
     int mblocks;
-    int64_t nblocks;     // workgroups along N
+    int kp;              // k-phases inside a workgroup (1 or 2)
+    int64_t nblocks;     // workgroups along N (each 64 * 8 / kp channels)
     int ksplit;
     int chunks_per_split;
 };
 
-// Split-K plan.  One 8-wave workgroup per CU (the LDS ring takes most of
-// the CU's 160 KB).  The time of a plan is modelled as (workgroups per CU) x
-// (chunks per split x time of one 32-k chunk, ~0.88 us at 144 rows, plus the
-// ring fill and epilogue) plus writing and re-reading the fp32 partial tiles
-// and one extra launch for the reduction; the constants are fitted to split
-// sweeps on MI355X over the OPT-shaped weights.
+// Work split.  One 8-wave workgroup per CU (the LDS ring takes most of the
+// CU's 160 KB).  K is shared out first between the kp phases of a workgroup
+// (summed in LDS), then between ksplit workgroups (fp32 partial tiles summed
+// by a second kernel).  The time of a plan is modelled as (workgroups per CU)
+// x (chunks per wave x time of one 32-k chunk, ~0.88 us at 144 rows, plus the
+// ring fill, the phase sum and the epilogue) plus writing and re-reading the
+// partial tiles and one extra launch; the constants are fitted to sweeps on
+// MI355X over the OPT-shaped weights.
 GemmPlan gemm_plan(int64_t M, int64_t K, int64_t N) {
     GemmPlan p{};
     const int64_t mt_needed = (M + 15) / 16;
     p.mt = (int)(mt_needed < 9 ? (mt_needed < 1 ? 1 : mt_needed) : 9);
     p.mblocks = (int)((M + 16 * p.mt - 1) / (16 * p.mt));
-    p.nblocks = ((N / 64) + kWaves - 1) / kWaves;
+    const int64_t ng = N / 64;
     const int64_t nchunks = K / 32;
-    const int64_t base = p.nblocks * (p.mblocks > 0 ? p.mblocks : 1);
-    const double chunk_us = 0.1 + 0.78 * p.mt / 9.0;    // one 32-k chunk of one workgroup
+    const double chunk_us = 0.1 + 0.78 * p.mt / 9.0;    // one 32-k chunk of one wave
     const double ramp_us = 4.0;                          // ring fill and epilogue of a workgroup
+    const double phase_us = 1.5;                         // LDS sum of the phases
     const double bytes_per_us = 3.0e6;                   // partial tile write + read, ~6 TB/s each
     double best = 1e300;
-    int best_ks = 1;
-    for (int ks = 1; ks <= 64; ++ks) {
-        const int64_t cps = (nchunks + ks - 1) / ks;
-        if (ks > 1 && (cps * (ks - 1) >= nchunks || cps < 8)) break;   // empty or too short splits
-        const double per_cu = std::ceil((double)base * ks / kNumCU);
-        const double t = per_cu * ((double)cps * chunk_us + ramp_us) +
-                         (ks > 1 ? (double)ks * (double)M * (double)N * 4.0 / bytes_per_us + 3.0 : 0.0);
-        if (t < best) { best = t; best_ks = ks; }
+    int best_ks = 1, best_kp = 1;
+    for (int kp = 1; kp <= 2; ++kp) {
+        const int64_t cols = kWaves / kp;
+        const int64_t base = ((ng + cols - 1) / cols) * (p.mblocks > 0 ? p.mblocks : 1);
+        for (int ks = 1; ks <= 64; ++ks) {
+            const int64_t cps = (nchunks + ks - 1) / ks;
+            if (ks > 1 && (cps * (ks - 1) >= nchunks || cps < 8 * kp)) break;   // empty or too short splits
+            const double per_cu = std::ceil((double)base * ks / kNumCU);
+            const double per_wave = std::ceil((double)cps / kp);
+            const double t = per_cu * (per_wave * chunk_us + ramp_us + (kp > 1 ? phase_us : 0.0)) +
+                             (ks > 1 ? (double)ks * (double)M * (double)N * 4.0 / bytes_per_us + 3.0 : 0.0);
+            if (t < best) { best = t; best_ks = ks; best_kp = kp; }
+        }
     }
+    p.kp = best_kp;
+    p.nblocks = (ng + kWaves / p.kp - 1) / (kWaves / p.kp);
     int64_t cps = (nchunks + best_ks - 1) / best_ks;
     if (cps < 1) cps = 1;
     p.chunks_per_split = (int)cps;
@@ -445,16 +540,17 @@ fgq_status launch_dequant_gemm(const void *x, int64_t M, int64_t K, int64_t N, c
     const dim3 grid((unsigned)p.nblocks, (unsigned)p.ksplit, (unsigned)p.mblocks);
     const uint16_t *xh = static_cast<const uint16_t *>(x);
     float *part = static_cast<float *>(ws);
+    const int cps = p.chunks_per_split, ks = p.ksplit, kp = p.kp;
     switch (p.mt) {
-        case 1: launch_mt<1>(grid, stream, xh, (int)M, K, N, pc, pm, p.chunks_per_split, part, y, f16, p.ksplit); break;
-        case 2: launch_mt<2>(grid, stream, xh, (int)M, K, N, pc, pm, p.chunks_per_split, part, y, f16, p.ksplit); break;
-        case 3: launch_mt<3>(grid, stream, xh, (int)M, K, N, pc, pm, p.chunks_per_split, part, y, f16, p.ksplit); break;
-        case 4: launch_mt<4>(grid, stream, xh, (int)M, K, N, pc, pm, p.chunks_per_split, part, y, f16, p.ksplit); break;
-        case 5: launch_mt<5>(grid, stream, xh, (int)M, K, N, pc, pm, p.chunks_per_split, part, y, f16, p.ksplit); break;
-        case 6: launch_mt<6>(grid, stream, xh, (int)M, K, N, pc, pm, p.chunks_per_split, part, y, f16, p.ksplit); break;
-        case 7: launch_mt<7>(grid, stream, xh, (int)M, K, N, pc, pm, p.chunks_per_split, part, y, f16, p.ksplit); break;
-        case 8: launch_mt<8>(grid, stream, xh, (int)M, K, N, pc, pm, p.chunks_per_split, part, y, f16, p.ksplit); break;
-        default: launch_mt<9>(grid, stream, xh, (int)M, K, N, pc, pm, p.chunks_per_split, part, y, f16, p.ksplit); break;
+        case 1: launch_mt<1>(kp, grid, stream, xh, (int)M, K, N, pc, pm, cps, part, y, f16, ks); break;
+        case 2: launch_mt<2>(kp, grid, stream, xh, (int)M, K, N, pc, pm, cps, part, y, f16, ks); break;
+        case 3: launch_mt<3>(kp, grid, stream, xh, (int)M, K, N, pc, pm, cps, part, y, f16, ks); break;
+        case 4: launch_mt<4>(kp, grid, stream, xh, (int)M, K, N, pc, pm, cps, part, y, f16, ks); break;
+        case 5: launch_mt<5>(kp, grid, stream, xh, (int)M, K, N, pc, pm, cps, part, y, f16, ks); break;
+        case 6: launch_mt<6>(kp, grid, stream, xh, (int)M, K, N, pc, pm, cps, part, y, f16, ks); break;
+        case 7: launch_mt<7>(kp, grid, stream, xh, (int)M, K, N, pc, pm, cps, part, y, f16, ks); break;
+        case 8: launch_mt<8>(kp, grid, stream, xh, (int)M, K, N, pc, pm, cps, part, y, f16, ks); break;
+        default: launch_mt<9>(kp, grid, stream, xh, (int)M, K, N, pc, pm, cps, part, y, f16, ks); break;
     }
     fgq_status s = check_launch("dq_gemm_kernel");
     if (s != FGQ_OK || p.ksplit == 1) return s;

@@ -258,8 +258,13 @@ def test_pack_matches_layout_definition():
     assert np.array_equal(gu.to_host(pm, np.uint32), em)
 
 
+# The last three take two k-phases per workgroup: an odd chunk count with no
+# split (33 x 544), an odd per-split chunk count with 8 splits and a last
+# workgroup holding one valid column group (145 x 4128 x 1088), and 17 splits
+# whose last one has a single chunk, so one phase has no work (150 x 8224).
 @pytest.mark.parametrize("M,K,N", [(1, 32, 64), (5, 96, 320), (16, 64, 256), (17, 160, 64), (37, 256, 512),
-                                   (144, 128, 192), (145, 96, 128), (300, 64, 64), (4, 0, 64)])
+                                   (144, 128, 192), (145, 96, 128), (300, 64, 64), (4, 0, 64),
+                                   (33, 544, 320), (145, 4128, 1088), (150, 8224, 576)])
 def test_gemm_ragged_shapes(M, K, N):
     rng = np.random.default_rng(M * 7 + K + N)
     Wt = (rng.standard_normal((K, N)) * 0.02).astype(np.float16)
@@ -310,15 +315,17 @@ def test_gemm_opt175b_sampled_columns(idx):
         gu.assert_close(y[:, sl], exp, "opt-175b[%d] cols %d.." % (idx, n0))
 
 
-def test_gemm_block_identity_and_determinism():
+@pytest.mark.parametrize("K,N", [(1024, 512), (4128, 1088)])
+def test_gemm_block_identity_and_determinism(K, N):
     """Y(g, m) against the m GPU batches run one at a time (within tolerance:
-    the launch plan differs), and bitwise repeatability."""
+    the launch plan differs), and bitwise repeatability (the second shape
+    sums two k-phases per workgroup and eight K splits)."""
     rng = np.random.default_rng(9)
-    K, N, g, m = 1024, 512, 36, 4
+    g, m = 36, 4
     Wt = (rng.standard_normal((K, N)) * 0.02).astype(np.float16)
     X = rng.standard_normal((g * m, K)).astype(np.float16)
     rc, rm, pc, pm = _gemm_case(X, g, m, Wt)
-    gu.note("gemm block identity")
+    gu.note("gemm block identity K=%d N=%d" % (K, N))
     y = gu.gemm(X, g, m, pc, pm, K, N)
     y2 = gu.gemm(X, g, m, pc, pm, K, N)
     assert np.array_equal(y, y2)
