@@ -5,8 +5,8 @@ One step = one decode step of one OPT-shaped layer for the whole block of
 B = g*m sequences, entirely in HBM:
   fgq_kv_append (the step's K and V rows into the compressed cache)
   fgq_decode_attn_q4kv (attend over prompt + t positions)
-  fgq_dequant_gemm x 6 (Wq, Wk, Wv, Wout, W1, W2 of the layer, one weight read
-  per block).
+  fgq_dequant_gemm x 4 (Wq|Wk|Wv as one [h][3h] matrix, since the three
+  projections share their input; Wout; W1; W2), one weight read per block.
 Decode step t cycles through 1..32 (the pages' 32 generated tokens), so the
 attended length runs from prompt+1 to prompt+32.  Inputs are seeded synthetic
 draws (synth), already resident in HBM when the timed region starts.
@@ -52,7 +52,103 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-seqs", type=int, default=4)
     ap.add_argument("--cpu-sample-cols", type=int, default=256)
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run 10 plain device copies of MIB MiB (HBM counter calibration under rocprofv3)")
+    ap.add_argument("--summarize-pmc", nargs=4, metavar=("KERNEL_FETCH", "KERNEL_WRITE", "COPY_FETCH", "COPY_WRITE"),
+                    help="only summarise four rocprofv3 --pmc output folders (FETCH_SIZE / WRITE_SIZE of the "
+                         "bench and of --calibrate-copy) into the HBM-traffic profile text")
+    ap.add_argument("--kernel", default="dq_gemm_kernel", help="kernel summarised by --summarize-pmc")
+    ap.add_argument("--summarize-trace", metavar="DIR",
+                    help="only summarise a rocprofv3 --kernel-trace --stats output folder of this bench: the "
+                         "kernel statistics and the steady-state duration of every launch of a step")
     return ap.parse_args()
+
+
+# Source files whose text defines each timed kernel: a committed counter
+# summary applies only while their hash is unchanged.
+KERNEL_SOURCES = {
+    "dq_gemm_kernel": ("gemm.hip", "common.h"),
+    "attn_split_kernel": ("attention.hip", "common.h"),
+}
+
+
+def source_hash(kernel: str) -> str:
+    """SHA-256 of the kernel's source code with // comments, trailing blanks
+    and empty lines removed (a comment edit does not invalidate a measurement)."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(ROOT, "int4_group_quantized_fgq_amd", "csrc", f)) as fh:
+            for line in fh:
+                code = line.split("//", 1)[0].rstrip()
+                if code:
+                    h.update((code + "\n").encode())
+    return h.hexdigest()
+
+
+def committed_traffic(kernel: str, config: str):
+    """HBM bytes per launch measured by rocprofv3 counters (a 'traffic-json:'
+    line of a summary under profiles/), or None when there is none for this
+    kernel and workload or the kernel's source has changed since."""
+    import glob
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.md"))):
+        with open(path) as fh:
+            for line in fh:
+                if line.startswith("traffic-json: "):
+                    d = json.loads(line[len("traffic-json: "):])
+                    if d.get("kernel") == kernel and d.get("config") == config and \
+                            d.get("source_sha256") == source_hash(kernel):
+                        return d
+    return None
+
+
+def read_pmc(folder: str, counter: str):
+    """{dispatch id: (kernel name, summed counter value)} from a rocprofv3 --pmc CSV folder."""
+    import csv
+    import glob
+    out = {}
+    files = glob.glob(os.path.join(folder, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit("no counter_collection.csv under " + folder)
+    for f in files:
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                if r["Counter_Name"] != counter:
+                    continue
+                d = int(r["Dispatch_Id"])
+                name, v = out.get(d, (r["Kernel_Name"], 0.0))
+                out[d] = (name, v + float(r["Counter_Value"]))
+    return out
+
+
+def summarize_pmc(args):
+    """Text of the HBM-traffic profile: counter KiB per dispatch of the kernel,
+    scaled by what the same counters read for a copy of known size."""
+    kf, kw, cf, cw = args.summarize_pmc
+    copy_bytes = None
+    fac = {}
+    for counter, folder in (("FETCH_SIZE", cf), ("WRITE_SIZE", cw)):
+        vals = [v for name, v in read_pmc(folder, counter).values() if "opy" in name or "elementwise" in name]
+        big = max(vals)   # the copy dispatches (fills and small helpers read less)
+        per = [v for v in vals if v > 0.5 * big]
+        copy_bytes = args.calibrate_copy * 2 ** 20 if args.calibrate_copy else None
+        fac[counter] = copy_bytes / (np.mean(per) * 1024.0) if copy_bytes else None
+    res = {}
+    for counter, folder in (("FETCH_SIZE", kf), ("WRITE_SIZE", kw)):
+        vals = [v for name, v in read_pmc(folder, counter).values() if args.kernel in name]
+        res[counter] = (len(vals), float(np.mean(vals)) if vals else 0.0)
+    return fac, res
+
+
+def calibrate_copy(torch, mib: int) -> None:
+    a = torch.empty(mib * 2 ** 18, dtype=torch.float32, device="cuda").uniform_()
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(10):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_mib": mib, "copies": 10, "bytes_read_per_copy": mib * 2 ** 20,
+                      "bytes_written_per_copy": mib * 2 ** 20}), flush=True)
 
 
 class Layer:
@@ -70,17 +166,29 @@ class Layer:
             sub = fgq.kv_struct(self.k_codes[b0:b0 + nb], self.v_codes[b0:b0 + nb], self.k_meta[b0:b0 + nb],
                                 self.v_meta[b0:b0 + nb], nb, H, D, cap)
             fgq.fgq_kv_append(sub, kd, vd, 0, w.prompt)
-        self.packed = []
-        for (K, N), (pc, pm) in zip(w.weights, host_weights):
-            self.packed.append((pc.clone(), pm.clone()))
+        self.packed = [(pc.clone(), pm.clone()) for pc, pm in host_weights]
+
+
+def launch_plan(w):
+    """The step's GEMM launches as (name, K, N, weight indices).  Weights whose
+    projections read the same input (Wq, Wk, Wv of an OPT layer: the first
+    three square matrices) are concatenated along N into one launch; groups of
+    64 output channels never straddle two matrices, so the fused matrix's
+    codes and metadata are the three matrices' side by side."""
+    ws = list(w.weights)
+    if len(ws) == 6 and ws[0] == ws[1] == ws[2] and ws[0][0] == ws[0][1]:
+        K = ws[0][0]
+        return [("qkv", K, 3 * K, (0, 1, 2)), ("out", ws[3][0], ws[3][1], (3,)),
+                ("ffn1", ws[4][0], ws[4][1], (4,)), ("ffn2", ws[5][0], ws[5][1], (5,))]
+    return [("w%d" % i, K, N, (i,)) for i, (K, N) in enumerate(ws)]
 
 
 def build_weights(torch, fgq, w):
     """Quantise and pack every weight of the layer once (offline step)."""
     out = []
-    for i, (K, N) in enumerate(w.weights):
+    for name, K, N, idx in launch_plan(w):
         t0 = time.time()
-        wd = torch.from_numpy(synth.weight(w, i)).to("cuda")
+        wd = torch.cat([torch.from_numpy(synth.weight(w, i)).to("cuda") for i in idx], dim=1).contiguous()
         codes = torch.empty((K, N // 2), dtype=torch.uint8, device="cuda")
         meta = torch.empty((K, N // 64), dtype=torch.int32, device="cuda")
         fgq.fgq_quantize_g64(wd, K, N, N, codes, meta)
@@ -90,7 +198,7 @@ def build_weights(torch, fgq, w):
         torch.cuda.synchronize()
         del wd, codes, meta
         out.append((pc, pm))
-        log("weight %d (%dx%d) quantised+packed in %.1fs" % (i, K, N, time.time() - t0))
+        log("weight %s (%dx%d) quantised+packed in %.1fs" % (name, K, N, time.time() - t0))
     return out
 
 
@@ -147,8 +255,105 @@ def cpu_baseline(w, args):
     }
 
 
+def short_name(kernel_name: str) -> str:
+    n = kernel_name.replace("(anonymous namespace)::", "").replace("void ", "")
+    return n.split("(")[0].replace("fgq::", "").strip()
+
+
+def summarize_trace(folder: str, w, steps: int) -> None:
+    """Markdown: rocprofv3's kernel statistics, then the mean duration of each
+    launch of a step over the last `steps` steps (a step starts with the KV
+    append; the split-K reduction is listed with the GEMM launch it ends)."""
+    import csv
+    import glob
+
+    def one(pattern):
+        f = glob.glob(os.path.join(folder, "**", pattern), recursive=True)
+        if not f:
+            raise SystemExit("no %s under %s" % (pattern, folder))
+        with open(f[0]) as fh:
+            return list(csv.DictReader(fh))
+
+    stats = one("*kernel_stats.csv")
+    print("| kernel | calls | average us | total ms | % of GPU time |")
+    print("|---|---|---|---|---|")
+    for r in stats[:12]:
+        print("| %s | %s | %.1f | %.2f | %.1f |" % (short_name(r["Name"]), r["Calls"], float(r["AverageNs"]) / 1e3,
+                                                  float(r["TotalDurationNs"]) / 1e6, float(r["Percentage"])))
+    trace = sorted(one("*kernel_trace.csv"), key=lambda r: int(r["Start_Timestamp"]))
+    names = ["append", "attention"] + ["gemm_" + p[0] for p in launch_plan(w)]
+    stepl = []
+    cur = None
+    for r in trace:
+        n = short_name(r["Kernel_Name"])
+        d = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+        if n.startswith("kv_append_kernel") and int(r["Grid_Size_X"]) == w.batch * w.hidden // 4:
+            cur = {"ops": [], "kernels": {}}
+            stepl.append(cur)
+            cur["ops"].append(["append", d])
+        elif cur is None:
+            continue
+        elif n.startswith("attn_split_kernel"):
+            cur["ops"].append(["attention", d])
+        elif n.startswith("attn_merge_kernel"):
+            cur["ops"][-1][1] += d
+        elif n.startswith("dq_gemm_kernel"):
+            cur["ops"].append([names[len(cur["ops"])] if len(cur["ops"]) < len(names) else "?", d])
+        elif n.startswith("splitk_reduce_kernel"):
+            cur["ops"][-1][1] += d
+    good = [st for st in stepl if [o[0] for o in st["ops"]] == names][-steps:]
+    print()
+    print("Steady state, mean of the last %d steps (us per launch; a GEMM launch includes its split-K "
+          "reduction, attention its merge):" % len(good))
+    print()
+    print("| launch | us |")
+    print("|---|---|")
+    tot = 0.0
+    for i, nm in enumerate(names):
+        v = float(np.mean([st["ops"][i][1] for st in good])) if good else float("nan")
+        tot += v
+        print("| %s | %.1f |" % (nm, v))
+    print("| step (sum) | %.1f |" % tot)
+
+
+def algorithmic_bytes_per_launch(kernel: str, w, n_steps: int = 0) -> float:
+    """Mean algorithmic HBM bytes of one launch of the kernel over the first
+    n_steps bench steps (0: one full cycle of decode steps)."""
+    if kernel == "dq_gemm_kernel":
+        plan = launch_plan(w)
+        return float(np.mean([acc.gemm_bytes(w.batch, K, N) for _, K, N, _ in plan]))
+    ts = [i % w.steps + 1 for i in range(n_steps or w.steps)]
+    return float(np.mean([acc.attention_bytes(w.batch, w.hidden, w.kv_len(t)) for t in ts]))
+
+
 def main():
     args = parse()
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace, synth.WORKLOADS[args.config], args.steps)
+        return
+    if args.summarize_pmc:
+        w = synth.WORKLOADS[args.config]
+        fac, res = summarize_pmc(args)
+        n_f, fetch_kib = res["FETCH_SIZE"]
+        n_w, write_kib = res["WRITE_SIZE"]
+        per_launch = fetch_kib * 1024.0 * fac["FETCH_SIZE"] + write_kib * 1024.0 * fac["WRITE_SIZE"]
+        alg = algorithmic_bytes_per_launch(args.kernel, w, args.warmup + args.steps)
+        d = {"kernel": args.kernel, "config": w.name, "source_sha256": source_hash(args.kernel),
+             "dispatches": [n_f, n_w], "fetch_kib_per_dispatch": round(fetch_kib, 1),
+             "write_kib_per_dispatch": round(write_kib, 1), "fetch_factor": round(fac["FETCH_SIZE"], 4),
+             "write_factor": round(fac["WRITE_SIZE"], 4), "bytes_per_launch": round(per_launch),
+             "algorithmic_bytes_per_launch": round(alg), "ratio": round(per_launch / alg, 4)}
+        print("| counter | dispatches | KiB per dispatch | copy calibration factor | bytes per launch |")
+        print("|---|---|---|---|---|")
+        print("| FETCH_SIZE | %d | %.1f | %.4f | %.4g |" % (n_f, fetch_kib, fac["FETCH_SIZE"],
+                                                           fetch_kib * 1024 * fac["FETCH_SIZE"]))
+        print("| WRITE_SIZE | %d | %.1f | %.4f | %.4g |" % (n_w, write_kib, fac["WRITE_SIZE"],
+                                                           write_kib * 1024 * fac["WRITE_SIZE"]))
+        print()
+        print("HBM traffic per launch %.4g B; algorithmic %.4g B; ratio %.3f" % (per_launch, alg, per_launch / alg))
+        print()
+        print("traffic-json: " + json.dumps(d))
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (the kernels shard by "
               "sequence/head and by weight column; see DESIGN.md). Run with --gpus 1.", file=sys.stderr)
@@ -160,12 +365,16 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     torch.cuda.set_device(0)
+    if args.calibrate_copy:
+        calibrate_copy(torch, args.calibrate_copy)
+        return
     w = synth.WORKLOADS[args.config]
     B, H, D, h = w.batch, w.heads, w.head_dim, w.hidden
     M = B
 
     # ---------------- setup (untimed): weights, caches, per-step inputs
     t_setup = time.time()
+    plan = launch_plan(w)
     weights = build_weights(torch, fgq, w)
     per_layer = acc.packed_bytes(sum(K * N for K, N in w.weights)) + \
         2 * acc.packed_bytes(B * h * w.capacity)
@@ -181,13 +390,13 @@ def main():
             "k": torch.from_numpy(synth.step_kv(w, "k", t)).to("cuda"),
             "v": torch.from_numpy(synth.step_kv(w, "v", t)).to("cuda"),
             "q": torch.from_numpy(synth.step_q(w, t)).to("cuda"),
-            "x": [torch.from_numpy(synth.gemm_x(w, i, t)).to("cuda") for i in range(len(w.weights))],
+            "x": [torch.from_numpy(synth.gemm_x(w, idx[0], t)).to("cuda") for _, _, _, idx in plan],
         }
         steps_in.append(d)
     attn_out = torch.empty((B, h), dtype=torch.float32, device="cuda")
-    ys = [torch.empty((M, N), dtype=torch.float32, device="cuda") for _, N in w.weights]
+    ys = [torch.empty((M, N), dtype=torch.float32, device="cuda") for _, _, N, _ in plan]
     attn_ws_b = max(fgq.fgq_decode_attn_ws_bytes(B, H, D, L) for L in range(w.prompt + 1, w.capacity + 1))
-    gemm_ws_b = max([fgq.fgq_dequant_gemm_ws_bytes(M, K, N) for K, N in w.weights] + [0])
+    gemm_ws_b = max([fgq.fgq_dequant_gemm_ws_bytes(M, K, N) for _, K, N, _ in plan] + [0])
     attn_ws = torch.empty(max(attn_ws_b, 16), dtype=torch.uint8, device="cuda")
     gemm_ws = torch.empty(max(gemm_ws_b, 16), dtype=torch.uint8, device="cuda")
     torch.cuda.synchronize()
@@ -195,7 +404,7 @@ def main():
 
     stream = torch.cuda.current_stream()
     sh = stream.cuda_stream
-    ops = ["append", "attention"] + ["gemm%d" % i for i in range(len(w.weights))]
+    ops = ["append", "attention"] + ["gemm_" + p[0] for p in plan]
 
     def run_step(i, ev=None):
         t = i % w.steps + 1
@@ -210,7 +419,7 @@ def main():
                                  attn_ws_b, sh)
         if ev is not None:
             ev[2].record(stream)
-        for wi, (K, N) in enumerate(w.weights):
+        for wi, (_, K, N, _) in enumerate(plan):
             pc, pm = L.packed[wi]
             fgq.fgq_dequant_gemm(d["x"][wi], w.g, w.m, K, N, pc, pm, ys[wi], fgq.FGQ_DTYPE_F32, gemm_ws,
                                  gemm_ws_b, sh)
@@ -221,7 +430,7 @@ def main():
         run_step(i)
     torch.cuda.synchronize()
 
-    n_ev = 3 + len(w.weights)
+    n_ev = 3 + len(plan)
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(args.steps)]
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)
@@ -239,8 +448,8 @@ def main():
     for ev in events:
         op_ms["append"] += ev[0].elapsed_time(ev[1])
         op_ms["attention"] += ev[1].elapsed_time(ev[2])
-        for wi in range(len(w.weights)):
-            op_ms["gemm%d" % wi] += ev[2 + wi].elapsed_time(ev[3 + wi])
+        for wi, p in enumerate(plan):
+            op_ms["gemm_" + p[0]] += ev[2 + wi].elapsed_time(ev[3 + wi])
 
     # ---------------- accounting
     K_steps = args.steps
@@ -249,8 +458,8 @@ def main():
     attn_flops = sum(acc.attention_flops(B, h, w.kv_len(t)) for t in ts)
     app_bytes = K_steps * acc.append_bytes(B, h)
     gemm_flops = K_steps * acc.layer_gemm_flops(M, w.weights)
-    gemm_bytes = K_steps * sum(acc.gemm_bytes(M, K, N) for K, N in w.weights)
-    gemm_ms = sum(op_ms["gemm%d" % i] for i in range(len(w.weights)))
+    gemm_bytes = K_steps * sum(acc.gemm_bytes(M, K, N) for _, K, N, _ in plan)
+    gemm_ms = sum(op_ms["gemm_" + p[0]] for p in plan)
     attn_gbs = attn_bytes / (op_ms["attention"] * 1e-3) / 1e9
     gemm_tflops = gemm_flops / (gemm_ms * 1e-3) / 1e12 if gemm_ms > 0 else 0.0
     ms_per_step = total_ms / K_steps
@@ -263,10 +472,10 @@ def main():
                       "frac_hbm_peak": attn_gbs / HBM_PEAK_GBS,
                       "TFLOP_per_s": attn_flops / (op_ms["attention"] * 1e-3) / 1e12},
     }
-    for i, (K, N) in enumerate(w.weights):
-        ms = op_ms["gemm%d" % i]
+    for name, K, N, _ in plan:
+        ms = op_ms["gemm_" + name]
         f = K_steps * acc.gemm_flops(M, K, N)
-        kernels["gemm%d_%dx%d" % (i, K, N)] = {
+        kernels["gemm_%s_%dx%d" % (name, K, N)] = {
             "us_per_launch": 1e3 * ms / K_steps,
             "TFLOP_per_s": f / (ms * 1e-3) / 1e12,
             "frac_mfma_peak": f / (ms * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS,
@@ -274,14 +483,22 @@ def main():
         }
 
     if w.weights and gemm_ms >= op_ms["attention"]:
-        roof = {"bound": "mfma", "kernel": "dq_gemm_kernel (all %d weight GEMMs of the step)" % len(w.weights),
+        kname = "dq_gemm_kernel"
+        roof = {"bound": "mfma", "kernel": kname + " (all %d weight GEMM launches of the step)" % len(plan),
                 "achieved": gemm_tflops, "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": gemm_tflops / MFMA_F16_PEAK_TFLOPS, "traffic": None,
-                "algorithmic_per_launch": "2*M*K*N flops, M=%d" % M}
+                "algorithmic_per_launch": "2*M*K*N flops, M=%d; mean algorithmic bytes per launch %.4g" %
+                                          (M, algorithmic_bytes_per_launch(kname, w))}
     else:
-        roof = {"bound": "hbm", "kernel": "attn_split_kernel", "achieved": attn_gbs, "peak": HBM_PEAK_GBS,
+        kname = "attn_split_kernel"
+        roof = {"bound": "hbm", "kernel": kname, "achieved": attn_gbs, "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": attn_gbs / HBM_PEAK_GBS, "traffic": None,
-                "algorithmic_per_launch": "1.125*hidden*kv_len bytes per sequence (+q, out)"}
+                "algorithmic_per_launch": "1.125*hidden*kv_len bytes per sequence (+q, out); mean %.4g" %
+                                          algorithmic_bytes_per_launch(kname, w)}
+    tr = committed_traffic(kname, w.name)
+    if tr is not None:
+        roof["traffic"] = tr["bytes_per_launch"]
+        roof["traffic_source"] = "rocprofv3 FETCH_SIZE + WRITE_SIZE per launch, copy-calibrated (profiles/)"
 
     result = {
         "metric": METRIC,
@@ -298,7 +515,8 @@ def main():
         "data": "synthetic (seeded Philox draws: KV and activations N(0,1), weights N(0,0.02))",
         "config": {"workload": w.name, "batch_g_x_m": "%dx%d" % (w.g, w.m), "global_batch": B,
                    "heads": H, "head_dim": D, "hidden": h, "prompt": w.prompt, "decode_steps": w.steps,
-                   "weights": ["%dx%d" % kn for kn in w.weights], "layer_instances": R,
+                   "weights": ["%dx%d" % kn for kn in w.weights],
+                   "gemm_launches": ["%s %dx%d" % (p[0], p[1], p[2]) for p in plan], "layer_instances": R,
                    "parallelism": "single GPU"},
         "roofline": roof,
         "hbm_roofline_attention": {"achieved": attn_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",

@@ -10,22 +10,26 @@
 //  * a wave owns one weight group column (64 output channels = 4 MFMA
 //    n-tiles) and every row of its M block (up to 9 m-tiles = 144 rows), so
 //    one dequantised B fragment feeds up to 9 MFMAs;
-//  * a workgroup is 8 waves (512 output channels, two waves per SIMD) and
-//    shares the X rows of each K chunk through LDS;
+//  * a workgroup is 8 waves (two per SIMD): 8/KP column groups times KP
+//    k-phases (KP = 1 or 2); the phases multiply alternate chunks of K and
+//    are summed through LDS at the end, and all waves share the X rows of
+//    each K chunk through LDS;
 //  * every operand reaches LDS through gfx950's direct global->LDS loads
-//    (global_load_lds_dwordx4) into a ring of 4 slots of two 32-k chunks
-//    each (the X rows, each wave's packed code words and its group
-//    metadata), so 3 slots are in flight while one is multiplied, with one
-//    barrier per slot and no register spent on prefetching;
+//    (global_load_lds_dwordx4, scalar base + loop-invariant lane offset, so
+//    no vector ALU work) into a ring of 4 slots of two 32-k chunks each (the
+//    X rows, each wave's packed code words and its group metadata), 3 slots
+//    in flight while one is multiplied, one barrier per slot;
 //  * the packed weight layout puts the 8 k-values of one output channel in
 //    one 32-bit word, in the nibble order that AND/OR with the fp16 magic
 //    numbers 0x6400 (1024 + q) and 0x5400 (64 + q) turn into two values per
 //    op; a packed subtract and a packed FMA give two fp16 W^ values, and the
-//    next chunk is dequantised in the shadow of the current chunk's MFMAs;
-//  * X rows sit in LDS with a 16-byte-slot XOR swizzle, so the rows of an A
+//    next chunk is dequantised between the current chunk's MFMAs;
+//  * A fragments stream two m-tiles ahead across chunk and slot boundaries;
+//    X rows sit in LDS with a 16-byte-slot XOR swizzle, so the rows of an A
 //    fragment read hit distinct banks;
-//  * K is split across workgroups when the N/512 workgroups cannot fill the
-//    CUs; fp32 partial tiles are summed in split order by a second kernel.
+//  * K is further split across workgroups when the column blocks cannot fill
+//    the CUs; fp32 partial tiles are summed in split order by a second
+//    kernel.
 #include <cmath>
 #include <type_traits>
 
