@@ -16,15 +16,15 @@
 //    each K chunk through LDS;
 //  * every operand reaches LDS through gfx950's direct global->LDS loads
 //    (global_load_lds_dwordx4, scalar base + loop-invariant lane offset, so
-//    no vector ALU work) into a ring of 4 slots of two 32-k chunks each (the
-//    X rows, each wave's packed code words and its group metadata), 3 slots
-//    in flight while one is multiplied, one barrier per slot;
+//    no vector ALU work) into a ring of two-chunk slots (the X rows, each
+//    wave's packed code words and its group metadata) as deep as the LDS
+//    allows, all but one slot in flight, one barrier per slot;
 //  * the packed weight layout puts the 8 k-values of one output channel in
 //    one 32-bit word, in the nibble order that AND/OR with the fp16 magic
 //    numbers 0x6400 (1024 + q) and 0x5400 (64 + q) turn into two values per
 //    op; a packed subtract and a packed FMA give two fp16 W^ values, and the
 //    next chunk is dequantised between the current chunk's MFMAs;
-//  * A fragments stream two m-tiles ahead across chunk and slot boundaries;
+//  * A fragments stream three m-tiles ahead across chunk and slot boundaries;
 //    X rows sit in LDS with a 16-byte-slot XOR swizzle, so the rows of an A
 //    fragment read hit distinct banks;
 //  * K is further split across workgroups when the column blocks cannot fill
@@ -41,7 +41,7 @@ namespace {
 constexpr int kWaves = 8;                  // waves (weight groups) per workgroup
 constexpr int kThreads = 64 * kWaves;
 constexpr int kSC = 2;                     // 32-k chunks per LDS ring slot (one barrier per slot)
-constexpr int kRing = 8 / kSC;             // ring slots: kRing-1 slots in flight
+constexpr int kLdsBudget = 152 * 1024;     // LDS bytes the ring may take (of 160 KB)
 
 // LDS byte address of a pointer into a __shared__ array.
 __device__ __forceinline__ uint32_t lds_addr(const void *p) {
@@ -115,11 +115,16 @@ struct Cfg {
     static constexpr int BBYTES = kWaves * LC * 1024;  // packed codes, 1 KB per wave and chunk
     static constexpr int MBYTES = kWaves * LC * 128;   // packed meta, 128 B per wave and chunk
     static constexpr int SLOT = XBYTES + BBYTES + MBYTES;
-    static constexpr int RING = kRing * SLOT;
+    // Ring slots: as many as the LDS budget holds (up to 8), NR-1 in flight.
+    static constexpr int NR = kLdsBudget / SLOT < 8 ? kLdsBudget / SLOT : 8;
+    // Slots per unrolled loop turn: the B double buffer alternates per chunk,
+    // so a turn must hold an even number of this wave's chunks.
+    static constexpr int UNROLL = (NR * LC) % 2 ? 2 * NR : NR;
+    static constexpr int RING = NR * SLOT;
     static constexpr int RED = (KP - 1) * CG * MT * 4 * 64 * 16;   // accumulators of phases 1..KP-1
     static constexpr int LDS = RING > RED ? RING : RED;
     static_assert(kSC % KP == 0, "every phase takes the same number of chunks of a slot");
-    static_assert((kRing * LC) % 2 == 0, "B fragment double buffer needs an even chunk count per ring turn");
+    static_assert(NR >= 3, "ring too shallow");
     static_assert(LDS <= 160 * 1024, "LDS budget");
 };
 
@@ -129,7 +134,7 @@ void dq_gemm_kernel(const uint16_t *__restrict__ x, int M, int64_t K, int64_t N,
                     const uint32_t *__restrict__ pc, const uint32_t *__restrict__ pm, int chunks_per_split,
                     float *__restrict__ part, void *__restrict__ y, int y_f16, int ksplit) {
     using C = Cfg<MT, KP>;
-    constexpr int CG = C::CG, LC = C::LC;
+    constexpr int CG = C::CG, LC = C::LC, NR = C::NR;
     __shared__ __attribute__((aligned(1024))) uint8_t lds[C::LDS];
     const uint32_t lds0 = lds_addr(lds);
 
@@ -272,32 +277,32 @@ void dq_gemm_kernel(const uint16_t *__restrict__ x, int M, int64_t K, int64_t N,
     // while bf[(n+1) % 2] receives the next one's; with an even number of
     // chunks per ring turn the roles swap statically, with no register copy.
     u32x4 bf[2][4];
-    // A fragments stream through two registers, PD m-tiles ahead of the
+    // A fragments stream through PD registers, PD m-tiles ahead of the
     // MFMAs, across chunk and slot boundaries.  The barrier that makes slot
     // st+1 visible (every wave's loads of it have landed) and frees slot st
     // (every wave's LDS reads of it are complete) is taken inside the last
     // chunk of slot st, just before the first read of slot st+1, while PD
     // m-tiles of MFMAs with operands already in registers remain: the LDS
     // latency after the barrier hides behind them.
-    constexpr int PD = MT >= 2 ? 2 : 1;
-    f16x8 a0, a1;
+    constexpr int PD = MT >= 3 ? 3 : MT;
+    f16x8 ap[PD];                                // ap[d]: fragment d m-tiles ahead
     if (nmine > 0) {
 #pragma unroll
-        for (int r = 0; r < kRing - 1; ++r) issue(c_begin + r * kSC, r);
-        wait_slots<kRing - 2>(cnt);              // this wave's loads of the first slot
+        for (int r = 0; r < NR - 1; ++r) issue(c_begin + r * kSC, r);
+        wait_slots<NR - 2>(cnt);                 // this wave's loads of the first slot
         lds_barrier();                           // ... and every wave's
         uint4 cw, ms, mm;
         load_b(0, 0, cw, ms, mm);
 #pragma unroll
         for (int h = 0; h < 8; ++h) dequant_half(cw, ms, mm, h, bf[0]);
-        a0 = a_frag(0, 0, 0);
-        if (PD == 2) a1 = a_frag(0, 0, 1);
+#pragma unroll
+        for (int d = 0; d < PD; ++d) ap[d] = a_frag(0, 0, d);
     }
     // The ring is unrolled so that every slot offset is an immediate.
-    for (int s0 = 0; s0 < nslots; s0 += kRing) {
+    for (int s0 = 0; s0 < nslots; s0 += C::UNROLL) {
 #pragma unroll
-        for (int r = 0; r < kRing; ++r) {
-            const int st = s0 + r;
+        for (int u = 0; u < C::UNROLL; ++u) {
+            const int st = s0 + u, r = u % NR;
             if (st >= nslots) break;
 #pragma unroll
             for (int lc = 0; lc < LC; ++lc) {
@@ -312,7 +317,7 @@ void dq_gemm_kernel(const uint16_t *__restrict__ x, int M, int64_t K, int64_t N,
                 // The next chunk's B words: in this slot, or (last chunk of
                 // the slot) this wave's own loads of the next slot, for which
                 // its vmcnt is enough.  Slot st+1 is only certain to have
-                // landed once this slot's refill is issued (at most kRing-2
+                // landed once this slot's refill is issued (at most NR-2
                 // slots outstanding after it), so in a slot's first chunk
                 // that load waits for the refill and the dequantisation
                 // starts one m-tile later.
@@ -322,10 +327,10 @@ void dq_gemm_kernel(const uint16_t *__restrict__ x, int M, int64_t K, int64_t N,
                 if (!last) {
                     load_b(r, lc + 1, cw, ms, mm);
                 } else if (!late) {
-                    wait_slots<kRing - 2>(cnt);
-                    load_b((r + 1) % kRing, 0, cw, ms, mm);
+                    wait_slots<NR - 2>(cnt);
+                    load_b((r + 1) % NR, 0, cw, ms, mm);
                 }
-                const int bi = (r * LC + lc) % 2;
+                const int bi = (u * LC + lc) % 2;
                 const u32x4(&bcur)[4] = bf[bi];
                 u32x4(&bnext)[4] = bf[bi ^ 1];
 #pragma unroll
@@ -338,20 +343,20 @@ void dq_gemm_kernel(const uint16_t *__restrict__ x, int M, int64_t K, int64_t N,
                         an = a_frag(r, lc + 1, f - MT);
                     } else {
                         if (f == MT && st + 1 < nslots) {
-                            wait_slots<kRing - 2>(cnt);  // slot st+1 of this wave has landed
+                            wait_slots<NR - 2>(cnt);  // slot st+1 of this wave has landed
                             lds_barrier();
                         }
-                        an = a_frag((r + 1) % kRing, 0, f - MT);
+                        an = a_frag((r + 1) % NR, 0, f - MT);
                     }
 #pragma unroll
                     for (int j = 0; j < 4; ++j)
                         acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                            a0, __builtin_bit_cast(f16x8, bcur[j]), acc[i][j], 0, 0, 0);
+                            ap[0], __builtin_bit_cast(f16x8, bcur[j]), acc[i][j], 0, 0, 0);
                     if (lc == 0 && i == 0) {
-                        issue(c_begin + (st + kRing - 1) * kSC, (r + kRing - 1) % kRing);
+                        issue(c_begin + (st + NR - 1) * kSC, (r + NR - 1) % NR);
                         if (late) {
-                            wait_slots<kRing - 2>(cnt);
-                            load_b((r + 1) % kRing, 0, cw, ms, mm);
+                            wait_slots<NR - 2>(cnt);
+                            load_b((r + 1) % NR, 0, cw, ms, mm);
                         }
                     }
 #pragma unroll
@@ -365,12 +370,9 @@ void dq_gemm_kernel(const uint16_t *__restrict__ x, int M, int64_t K, int64_t N,
                         __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);   // then two VALU ops
                     }
                     __builtin_amdgcn_sched_barrier(0);
-                    if (PD == 2) {
-                        a0 = a1;
-                        a1 = an;
-                    } else {
-                        a0 = an;
-                    }
+#pragma unroll
+                    for (int d = 0; d + 1 < PD; ++d) ap[d] = ap[d + 1];
+                    ap[PD - 1] = an;
                 }
             }
         }
