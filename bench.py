@@ -48,7 +48,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=32)
     ap.add_argument("--config", default="opt-175b", choices=sorted(synth.WORKLOADS))
     ap.add_argument("--rotate", type=int, default=0,
-                    help="layer instances cycled through (0: enough to exceed the 256 MB last-level cache)")
+                    help="layer instances cycled through (0: at least 3, and enough to exceed the 256 MB "
+                         "last-level cache three times over)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-seqs", type=int, default=4)
     ap.add_argument("--cpu-sample-cols", type=int, default=256)
@@ -138,6 +139,39 @@ def summarize_pmc(args):
         vals = [v for name, v in read_pmc(folder, counter).values() if args.kernel in name]
         res[counter] = (len(vals), float(np.mean(vals)) if vals else 0.0)
     return fac, res
+
+
+def measured_ceilings(torch) -> dict:
+    """Achievable rates on this GPU next to the spec peaks: a 1 GiB device
+    copy (HBM read + write) and a library fp16 GEMM (hipBLASLt, 8192^3)."""
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a = torch.empty(2 ** 28, dtype=torch.float32, device="cuda").uniform_()
+    b = torch.empty_like(a)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(10):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    copy_gbs = 10 * 2 * a.numel() * 4 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del a, b
+    n = 8192
+    x = torch.randn(n, n, device="cuda").half()
+    y = torch.randn(n, n, device="cuda").half()
+    z = x @ y
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(10):
+        z = x @ y
+    e1.record()
+    torch.cuda.synchronize()
+    gemm_tf = 10 * 2.0 * n ** 3 / (e0.elapsed_time(e1) * 1e-3) / 1e12
+    del x, y, z
+    torch.cuda.empty_cache()
+    return {"device_copy_GB_per_s": round(copy_gbs, 1), "hipblaslt_f16_gemm_8192_TFLOP_per_s": round(gemm_tf, 1),
+            "spec_hbm_GB_per_s": HBM_PEAK_GBS, "spec_mfma_f16_TFLOP_per_s": MFMA_F16_PEAK_TFLOPS,
+            "gpu": torch.cuda.get_device_name(0), "hip": torch.version.hip}
 
 
 def calibrate_copy(torch, mib: int) -> None:
@@ -378,7 +412,7 @@ def main():
     weights = build_weights(torch, fgq, w)
     per_layer = acc.packed_bytes(sum(K * N for K, N in w.weights)) + \
         2 * acc.packed_bytes(B * h * w.capacity)
-    R = args.rotate or max(1, min(4, int(np.ceil(3 * 256e6 / per_layer))))
+    R = args.rotate or max(3, min(8, int(np.ceil(3 * 256e6 / per_layer))))
     layers = []
     for inst in range(R):
         layers.append(Layer(torch, fgq, w, inst, weights, prompt_chunks(torch, w)))
@@ -529,6 +563,7 @@ def main():
         "context": "pages' end-to-end FlexGen 4-bit OPT-175B on one T4 with offloading: 1.12 token/s "
                    "(all 96 layers, prefill included) - not comparable to this per-layer in-HBM rate",
     }
+    result["measured_ceilings"] = measured_ceilings(torch)
     if not args.no_cpu_baseline:
         t0 = time.time()
         result["cpu_baseline"] = cpu_baseline(w, args)

@@ -27,6 +27,8 @@
 //  * Scores of a 64-token chunk are formed first, the chunk max is taken over
 //    the wave, then the exponentials and the P.V pass run with that max: the
 //    running accumulators are rescaled once per chunk, not per token.
+#include <type_traits>
+
 #include "common.h"
 
 namespace fgq {
@@ -164,11 +166,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
             d.VM[it] = __builtin_nontemporal_load(vmb + jc * G);
         }
     };
-    auto process = [&](int c0, const Chunk &d) {
-        // ---- scores
+    // TAIL: the chunk may reach past the end of the split (the last one).
+    auto process = [&](int c0, const Chunk &d, auto tail) {
+        constexpr bool TAIL = decltype(tail)::value;
+        // ---- scores.  A token iteration wholly past the end of the split
+        // (the ragged last chunk) skips its arithmetic: its score is -inf
+        // (the test is the same in every lane).
         float s[CH];
 #pragma unroll
         for (int it = 0; it < CH; ++it) {
+            if (TAIL && c0 + it * TPI >= j1) {
+                s[it] = -INFINITY;
+                continue;
+            }
             const uint32_t w[4] = {d.K[it].x, d.K[it].y, d.K[it].z, d.K[it].w};
             float lo = 0.f, hi = 0.f;
 #pragma unroll
@@ -202,10 +212,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
         }
         const float m_new = m_run;
 
-        // ---- P.V, two tokens (it, it + CH/2) per dot2
+        // ---- P.V, two tokens (it, it + CH/2) per dot2; a pair wholly past
+        // the end adds nothing and is skipped (a pair with one token past the
+        // end runs with p = 0 for it: its loads re-read the last valid row,
+        // so every value is finite)
 #pragma unroll
         for (int pi = 0; pi < CH / 2; ++pi) {
             const int ia = pi, ib = pi + CH / 2;
+            if (TAIL && c0 + ia * TPI >= j1) continue;
             const float pa = fast_exp2(s[ia] - m_new), pb = fast_exp2(s[ib] - m_new);
             l_acc += pa + pb;
             const float sa = h2f((uint16_t)(d.VM[ia] >> 16)), sb = h2f((uint16_t)(d.VM[ib] >> 16));
@@ -242,13 +256,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
     Chunk bufA, bufB;
     int c0 = j0;
     if (c0 < j1) load(c0, bufA);
+    const std::true_type tail;
+    const std::false_type body;
     while (c0 < j1) {
-        if (c0 + STEP < j1) load(c0 + STEP, bufB);
-        process(c0, bufA);
+        if (c0 + STEP < j1) {
+            load(c0 + STEP, bufB);
+            process(c0, bufA, body);
+        } else {
+            process(c0, bufA, tail);
+        }
         c0 += STEP;
         if (c0 >= j1) break;
-        if (c0 + STEP < j1) load(c0 + STEP, bufA);
-        process(c0, bufB);
+        if (c0 + STEP < j1) {
+            load(c0 + STEP, bufA);
+            process(c0, bufB, body);
+        } else {
+            process(c0, bufB, tail);
+        }
         c0 += STEP;
     }
 
