@@ -294,6 +294,26 @@ def test_gemm_workload_full(name, idx):
     gu.assert_close(y, oracle.dequant_gemm(X, w.g, w.m, rc, rm), "gemm %s[%d]" % (name, idx))
 
 
+def _sampled_columns_check(Wt, X, g, m, slices, what):
+    """GEMM of the full weight on the GPU; the oracle quantises and multiplies
+    whole-group column slices on its own (groups run along N, so a slice of
+    whole groups has the same codes), after the GPU's codes of each slice are
+    checked equal to the oracle's."""
+    K, N = Wt.shape
+    codes, meta = gu.quantize(Wt)
+    refs = []
+    for n0 in slices:
+        rc, rm = oracle.quantize_g64(np.ascontiguousarray(Wt[:, n0:n0 + 256]))
+        assert np.array_equal(codes[:, n0 // 2:(n0 + 256) // 2], rc), (what, n0)
+        assert np.array_equal(meta[:, n0 // 64:(n0 + 256) // 64], rm), (what, n0)
+        refs.append((n0, rc, rm))
+    pc, pm = gu.pack(gu.to_dev(codes), gu.to_dev(meta), K, N)
+    del codes, meta
+    y = gu.gemm(X, g, m, pc, pm, K, N)
+    for n0, rc, rm in refs:
+        gu.assert_close(y[:, n0:n0 + 256], oracle.dequant_gemm(X, g, m, rc, rm), "%s cols %d.." % (what, n0))
+
+
 @pytest.mark.parametrize("idx", [0, 4, 5])
 def test_gemm_opt175b_sampled_columns(idx):
     """Bench launch configuration (M = 144 = 36 x 4) at full size; the oracle
@@ -301,18 +321,20 @@ def test_gemm_opt175b_sampled_columns(idx):
     w = W["opt-175b"]
     K, N = w.weights[idx]
     gu.note("gemm opt-175b[%d] M=%d K=%d N=%d" % (idx, w.batch, K, N))
-    Wt = synth.weight(w, idx)
-    X = synth.gemm_x(w, idx, 1)
-    codes, meta = gu.quantize(Wt)
-    del Wt
-    pc, pm = gu.pack(gu.to_dev(codes), gu.to_dev(meta), K, N)
-    y = gu.gemm(X, w.g, w.m, pc, pm, K, N)
-    for n0 in (0, N // 2 + 64, N - 256):
-        sl = slice(n0, n0 + 256)
-        c = np.ascontiguousarray(codes[:, n0 // 2:(n0 + 256) // 2])
-        m = np.ascontiguousarray(meta[:, n0 // 64:(n0 + 256) // 64])
-        exp = oracle.dequant_gemm(X, w.g, w.m, c, m)
-        gu.assert_close(y[:, sl], exp, "opt-175b[%d] cols %d.." % (idx, n0))
+    _sampled_columns_check(synth.weight(w, idx), synth.gemm_x(w, idx, 1), w.g, w.m,
+                           (0, N // 2 + 64, N - 256), "opt-175b[%d]" % idx)
+
+
+# Large ragged shapes at full size, checked on sampled columns: two k-phases
+# with three M blocks and an odd chunk count; a partial last column tile with
+# one M block; two M blocks and a partial last tile.  Slices cover the first
+# column tile, a tile boundary and the last (partial) tile.
+@pytest.mark.parametrize("M,K,N,tc", [(290, 8416, 14592, 256), (144, 8416, 33600, 256), (150, 9472, 33600, 512)])
+def test_gemm_large_ragged_sampled_columns(M, K, N, tc):
+    gu.note("gemm large ragged M=%d K=%d N=%d" % (M, K, N))
+    Wt = synth.to_f16(synth.normal(synth.stream_key(90, M, K, N), K * N, 0.02)).reshape(K, N)
+    X = synth.to_f16(synth.normal(synth.stream_key(91, M, K, N), M * K)).reshape(M, K)
+    _sampled_columns_check(Wt, X, M, 1, (0, 5 * tc - 128, N - 256), "gemm %dx%dx%d" % (M, K, N))
 
 
 @pytest.mark.parametrize("K,N", [(1024, 512), (4128, 1088)])
