@@ -11,9 +11,12 @@ Decode step t cycles through 1..32 (the pages' 32 generated tokens), so the
 attended length runs from prompt+1 to prompt+32.  Inputs are seeded synthetic
 draws (synth), already resident in HBM when the timed region starts.
 
-Prints one JSON line (see the `emit` call).  Per-kernel durations come from
-HIP events recorded on the launch stream around every call of the timed
-steps; the CPU baseline is the oracle on a bounded sample of one step.
+Prints one JSON line.  The steps are timed twice: an eager pass with HIP
+events recorded on the launch stream around every call (the per-kernel
+durations and the roofline come from it), then the same steps replayed as HIP
+graphs, one per (decode step, layer instance), which gives value and
+ms_per_step (--no-graph: the eager pass gives them).  The CPU baseline is the
+oracle on a bounded sample of one step.
 """
 from __future__ import annotations
 
@@ -50,6 +53,9 @@ def parse():
     ap.add_argument("--rotate", type=int, default=0,
                     help="layer instances cycled through (0: at least 3, and enough to exceed the 256 MB "
                          "last-level cache three times over)")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="time the eager launches only (default: the step is also replayed as HIP graphs, "
+                         "and that pass gives value and ms_per_step)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-seqs", type=int, default=4)
     ap.add_argument("--cpu-sample-cols", type=int, default=256)
@@ -440,7 +446,7 @@ def main():
     sh = stream.cuda_stream
     ops = ["append", "attention"] + ["gemm_" + p[0] for p in plan]
 
-    def run_step(i, ev=None):
+    def run_step(i, ev=None, sh=sh):
         t = i % w.steps + 1
         L = layers[i % R]
         d = steps_in[t - 1]
@@ -478,6 +484,37 @@ def main():
     wall = time.perf_counter() - wall0
     total_ms = start.elapsed_time(stop)
 
+    # ---------------- the same steps as HIP graphs: one graph per (decode step,
+    # layer instance), captured once, replayed with every input already in place
+    graph_ms = None
+    if not args.no_graph:
+        graphs = {}
+        cap = torch.cuda.Stream()      # capture needs a stream other than the default one
+        for i in range(args.warmup + args.steps):
+            key = (i % w.steps, i % R)
+            if key not in graphs:
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=cap):
+                    run_step(i, sh=cap.cuda_stream)
+                graphs[key] = g
+        torch.cuda.synchronize()
+        for i in range(args.warmup):
+            graphs[(i % w.steps, i % R)].replay()
+        torch.cuda.synchronize()
+        gstart = torch.cuda.Event(enable_timing=True)
+        gstop = torch.cuda.Event(enable_timing=True)
+        wall0 = time.perf_counter()
+        gstart.record(stream)
+        for i in range(args.steps):
+            j = args.warmup + i
+            graphs[(j % w.steps, j % R)].replay()
+        gstop.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - wall0
+        graph_ms = gstart.elapsed_time(gstop)
+        log("%d graphs captured; graph pass %.3f ms/step, eager pass %.3f ms/step" %
+            (len(graphs), graph_ms / args.steps, total_ms / args.steps))
+
     op_ms = {o: 0.0 for o in ops}
     for ev in events:
         op_ms["append"] += ev[0].elapsed_time(ev[1])
@@ -496,8 +533,9 @@ def main():
     gemm_ms = sum(op_ms["gemm_" + p[0]] for p in plan)
     attn_gbs = attn_bytes / (op_ms["attention"] * 1e-3) / 1e9
     gemm_tflops = gemm_flops / (gemm_ms * 1e-3) / 1e12 if gemm_ms > 0 else 0.0
-    ms_per_step = total_ms / K_steps
-    value = B * K_steps / (total_ms * 1e-3)
+    step_total_ms = total_ms if graph_ms is None else graph_ms
+    ms_per_step = step_total_ms / K_steps
+    value = B * K_steps / (step_total_ms * 1e-3)
 
     kernels = {
         "append": {"us_per_launch": 1e3 * op_ms["append"] / K_steps,
@@ -558,6 +596,9 @@ def main():
         "mfma_roofline_gemm": {"achieved": gemm_tflops, "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
                                "frac": gemm_tflops / MFMA_F16_PEAK_TFLOPS,
                                "GB_per_s": gemm_bytes / (gemm_ms * 1e-3) / 1e9 if gemm_ms else 0.0},
+        "step_launch": "eager" if graph_ms is None else "hip-graph replay (one graph per decode step and layer "
+                                                           "instance)",
+        "eager_ms_per_step": total_ms / K_steps,
         "kernels": kernels,
         "wall_s_timed_region": wall,
         "context": "pages' end-to-end FlexGen 4-bit OPT-175B on one T4 with offloading: 1.12 token/s "
