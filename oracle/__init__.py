@@ -55,8 +55,9 @@ def _load():
         lib.oracle_kv_append.argtypes = [vp, vp, i32, i32, i32, i32, i32, i32, vp, vp, vp, vp]
         lib.oracle_decode_attn.argtypes = [vp, i32, i32, i32, i32, vp, vp, vp, vp, i32, dbl, vp]
         lib.oracle_dequant_gemm.argtypes = [vp, i32, i32, i64, i64, vp, vp, vp]
+        lib.oracle_decode_attn_topk.argtypes = [vp, i32, i32, i32, i32, vp, vp, vp, vp, i32, i32, dbl, vp, vp]
         for f in (lib.oracle_quantize_g64, lib.oracle_dequant_g64, lib.oracle_kv_append,
-                  lib.oracle_decode_attn, lib.oracle_dequant_gemm):
+                  lib.oracle_decode_attn, lib.oracle_dequant_gemm, lib.oracle_decode_attn_topk):
             f.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -134,6 +135,22 @@ def decode_attn(kv: KVCache, q: np.ndarray, kv_len: int, scale: float = 0.0) -> 
                                       kv.v_codes.ctypes.data, kv.v_meta.ctypes.data,
                                       kv_len, float(scale), out.ctypes.data), "decode_attn")
     return out
+
+
+def decode_attn_topk(kv: KVCache, q: np.ndarray, kv_len: int, top_k: int, scale: float = 0.0):
+    """Top-K sparse decode attention: q fp16 [B][H*D] -> (fp32 [B][H*D], kept
+    positions int32 [B][H][min(top_k, kv_len)] ascending); scale <= 0 means 1/sqrt(D)."""
+    q = _c(q, np.float16)
+    if scale <= 0.0:
+        scale = 1.0 / np.sqrt(kv.head_dim)
+    out = np.zeros((kv.batch, kv.heads * kv.head_dim), np.float32)
+    sel = np.zeros((kv.batch, kv.heads, max(min(top_k, kv_len), 0)), np.int32)
+    _check(_load().oracle_decode_attn_topk(q.ctypes.data, kv.batch, kv.heads, kv.head_dim, kv.cap,
+                                           kv.k_codes.ctypes.data, kv.k_meta.ctypes.data,
+                                           kv.v_codes.ctypes.data, kv.v_meta.ctypes.data,
+                                           kv_len, top_k, float(scale), out.ctypes.data, sel.ctypes.data),
+           "decode_attn_topk")
+    return out, sel
 
 
 def dequant_gemm(x: np.ndarray, g: int, m: int, codes: np.ndarray, meta: np.ndarray) -> np.ndarray:

@@ -248,6 +248,87 @@ int oracle_decode_attn(const uint16_t *q, int32_t batch, int32_t heads, int32_t 
     return ORACLE_OK;
 }
 
+/* Top-K sparse decode attention: the paper's optional approximation that
+ * reads only the top 10% of the value cache (FlexGen review on
+ * blog.gzher.com, section 3.4; paper-graph-ui FlexGen summary, section 3.3
+ * "Roadmap for the Deep Dive": with 4-bit group-wise compression, one of the
+ * two section-5 approximations, both meant to cut I/O volume).  The pages
+ * give no formula.  Reading taken: every position is scored
+ * over the compressed K exactly as in dense decode attention; the top_k
+ * positions with the largest scores are kept, the scores compared as fp32
+ * values (the GPU's precision: fp64 score rounded once to fp32, -0 taken as
+ * +0), equal scores going to the lower position; softmax over the kept
+ * positions only, and V rows of kept positions only:
+ *   T   = top_k positions by (fp32(s_j) descending, j ascending)
+ *   o_d = sum_{j in T} exp(s_j - m) V^_{j,d} / sum_{j in T} exp(s_j - m),
+ *         m = max_j s_j                      (fp64, j ascending)
+ * top_k >= kv_len keeps every position, and then the result is the dense one
+ * bit for bit (the same loops in the same order).  sel (may be NULL) receives
+ * the kept positions of every (b, head) in ascending order, int32
+ * [batch][heads][min(top_k, kv_len)]. */
+typedef struct { float s32; int32_t j; } oracle_rank;
+
+static int rank_cmp(const void *pa, const void *pb) {
+    const oracle_rank *a = (const oracle_rank *)pa, *b = (const oracle_rank *)pb;
+    if (a->s32 > b->s32) return -1;
+    if (a->s32 < b->s32) return 1;
+    return (a->j > b->j) - (a->j < b->j);
+}
+
+int oracle_decode_attn_topk(const uint16_t *q, int32_t batch, int32_t heads, int32_t head_dim, int32_t cap,
+                            const uint8_t *k_codes, const uint32_t *k_meta,
+                            const uint8_t *v_codes, const uint32_t *v_meta,
+                            int32_t kv_len, int32_t top_k, double scale, float *out, int32_t *sel) {
+    if (head_dim % 64 != 0 || kv_len < 1 || kv_len > cap || top_k < 1) return ORACLE_ERR_SHAPE;
+    const int32_t kk = top_k < kv_len ? top_k : kv_len;
+    int64_t h = (int64_t)heads * head_dim;
+    int64_t gph = head_dim / 64;
+    #pragma omp parallel for collapse(2) schedule(static)
+    for (int32_t b = 0; b < batch; ++b)
+        for (int32_t hd = 0; hd < heads; ++hd) {
+            double *s = (double *)malloc(sizeof(double) * (size_t)kv_len);
+            unsigned char *keep = (unsigned char *)calloc((size_t)kv_len, 1);
+            oracle_rank *rk = (oracle_rank *)malloc(sizeof(oracle_rank) * (size_t)kv_len);
+            double *o = (double *)calloc((size_t)head_dim, sizeof(double));
+            const uint16_t *qv = q + (int64_t)b * h + (int64_t)hd * head_dim;
+            int64_t base = ((int64_t)b * heads + hd) * cap;
+            for (int32_t j = 0; j < kv_len; ++j) {
+                const uint8_t *kc = k_codes + (base + j) * (head_dim / 2);
+                const uint32_t *km = k_meta + (base + j) * gph;
+                double acc = 0.0;
+                for (int32_t d = 0; d < head_dim; ++d)
+                    acc += (double)oracle_f16_to_f32(qv[d]) * (double)dequant_one(km[d / 64], code_at(kc, d));
+                s[j] = acc * scale;
+                rk[j].s32 = (float)s[j] + 0.0f;
+                rk[j].j = j;
+            }
+            qsort(rk, (size_t)kv_len, sizeof(oracle_rank), rank_cmp);
+            for (int32_t i = 0; i < kk; ++i) keep[rk[i].j] = 1;
+            double mx = s[0];
+            for (int32_t j = 1; j < kv_len; ++j) if (s[j] > mx) mx = s[j];
+            double den = 0.0;
+            for (int32_t j = 0; j < kv_len; ++j)
+                if (keep[j]) { s[j] = exp(s[j] - mx); den += s[j]; }
+            int32_t n = 0;
+            for (int32_t j = 0; j < kv_len; ++j) {
+                if (!keep[j]) continue;
+                if (sel) sel[((int64_t)b * heads + hd) * kk + n] = j;
+                ++n;
+                const uint8_t *vc = v_codes + (base + j) * (head_dim / 2);
+                const uint32_t *vm = v_meta + (base + j) * gph;
+                for (int32_t d = 0; d < head_dim; ++d)
+                    o[d] += s[j] * (double)dequant_one(vm[d / 64], code_at(vc, d));
+            }
+            float *ov = out + (int64_t)b * h + (int64_t)hd * head_dim;
+            for (int32_t d = 0; d < head_dim; ++d) ov[d] = (float)(o[d] / den);
+            free(s);
+            free(keep);
+            free(rk);
+            free(o);
+        }
+    return ORACLE_OK;
+}
+
 /* Weight GEMM of one block of g*m rows (m GPU batches of g rows each, batch j
  * occupying rows j*g .. j*g+g-1) against the compressed weight W [K][N]
  * (codes [K][N/2], meta [K][N/64]: groups along the output channel n):
