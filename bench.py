@@ -76,6 +76,7 @@ def parse():
 KERNEL_SOURCES = {
     "dq_gemm_kernel": ("gemm.hip", "common.h"),
     "attn_split_kernel": ("attention.hip", "common.h"),
+    "attn_topk_wave_kernel": ("topk_attention.hip", "common.h"),
 }
 
 
@@ -197,10 +198,11 @@ class Layer:
     def __init__(self, torch, fgq, w, inst, host_weights, prompt_chunks):
         B, H, D, cap = w.batch, w.heads, w.head_dim, w.capacity
         dev = "cuda"
-        self.k_codes = torch.empty((B, H, cap, D // 2), dtype=torch.uint8, device=dev)
-        self.v_codes = torch.empty_like(self.k_codes)
-        self.k_meta = torch.empty((B, H, cap, D // 64), dtype=torch.int32, device=dev)
-        self.v_meta = torch.empty_like(self.k_meta)
+        # zero-filled: a position not yet appended reconstructs to 0 (min 0, step 0)
+        self.k_codes = torch.zeros((B, H, cap, D // 2), dtype=torch.uint8, device=dev)
+        self.v_codes = torch.zeros_like(self.k_codes)
+        self.k_meta = torch.zeros((B, H, cap, D // 64), dtype=torch.int32, device=dev)
+        self.v_meta = torch.zeros_like(self.k_meta)
         self.kv = fgq.kv_struct(self.k_codes, self.v_codes, self.k_meta, self.v_meta, B, H, D, cap)
         for b0, nb, kd, vd in prompt_chunks:
             sub = fgq.kv_struct(self.k_codes[b0:b0 + nb], self.v_codes[b0:b0 + nb], self.k_meta[b0:b0 + nb],
@@ -356,12 +358,19 @@ def summarize_trace(folder: str, w, steps: int) -> None:
     print("| step (sum) | %.1f |" % tot)
 
 
-def algorithmic_bytes_per_launch(kernel: str, w, n_steps: int = 0) -> float:
+def algorithmic_bytes_per_launch(kernel: str, w, n_steps: int = 0, warmup: int = 0) -> float:
     """Mean algorithmic HBM bytes of one launch of the kernel over the first
-    n_steps bench steps (0: one full cycle of decode steps)."""
+    n_steps bench steps (0: one full cycle of decode steps); the top-K kernel
+    runs min(warmup, 8) untimed launches and then one per timed step."""
     if kernel == "dq_gemm_kernel":
         plan = launch_plan(w)
         return float(np.mean([acc.gemm_bytes(w.batch, K, N) for _, K, N, _ in plan]))
+    if kernel == "attn_topk_wave_kernel":
+        n = n_steps or w.steps
+        ts = [i % w.steps + 1 for i in range(min(warmup, 8))] + \
+            [(warmup + i) % w.steps + 1 for i in range(n - warmup)]
+        return float(np.mean([acc.topk_attention_bytes(w.batch, w.hidden, w.kv_len(t), -(-w.kv_len(t) // 10))
+                              for t in ts]))
     ts = [i % w.steps + 1 for i in range(n_steps or w.steps)]
     return float(np.mean([acc.attention_bytes(w.batch, w.hidden, w.kv_len(t)) for t in ts]))
 
@@ -377,7 +386,7 @@ def main():
         n_f, fetch_kib = res["FETCH_SIZE"]
         n_w, write_kib = res["WRITE_SIZE"]
         per_launch = fetch_kib * 1024.0 * fac["FETCH_SIZE"] + write_kib * 1024.0 * fac["WRITE_SIZE"]
-        alg = algorithmic_bytes_per_launch(args.kernel, w, args.warmup + args.steps)
+        alg = algorithmic_bytes_per_launch(args.kernel, w, args.warmup + args.steps, args.warmup)
         d = {"kernel": args.kernel, "config": w.name, "source_sha256": source_hash(args.kernel),
              "dispatches": [n_f, n_w], "fetch_kib_per_dispatch": round(fetch_kib, 1),
              "write_kib_per_dispatch": round(write_kib, 1), "fetch_factor": round(fac["FETCH_SIZE"], 4),
@@ -553,6 +562,61 @@ def main():
             "frac_mfma_peak": f / (ms * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS,
             "GB_per_s": K_steps * acc.gemm_bytes(M, K, N) / (ms * 1e-3) / 1e9,
         }
+
+    # prompt bulk compression (the prefill side of the cache, reported beside the
+    # decode step): the first 8 sequences' prompt K and V rewritten into layer 0
+    nb = min(8, B)
+    kd = torch.from_numpy(synth.prompt_kv(w, "k", nb=nb)).to("cuda")
+    vd = torch.from_numpy(synth.prompt_kv(w, "v", nb=nb)).to("cuda")
+    L0 = layers[0]
+    sub = fgq.kv_struct(L0.k_codes[:nb], L0.v_codes[:nb], L0.k_meta[:nb], L0.v_meta[:nb], nb, H, D, w.capacity)
+    fgq.fgq_kv_append(sub, kd, vd, 0, w.prompt, sh)
+    torch.cuda.synchronize()
+    b0, b1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 10
+    b0.record(stream)
+    for _ in range(reps):
+        fgq.fgq_kv_append(sub, kd, vd, 0, w.prompt, sh)
+    b1.record(stream)
+    torch.cuda.synchronize()
+    bulk_us = 1e3 * b0.elapsed_time(b1) / reps
+    del kd, vd
+    kernels["prompt_bulk_append"] = {
+        "sequences": nb, "tokens_per_sequence": w.prompt, "us_per_launch": bulk_us,
+        "GB_per_s": acc.append_bytes(nb, h, w.prompt) / (bulk_us * 1e-6) / 1e9,
+        "frac_hbm_peak": acc.append_bytes(nb, h, w.prompt) / (bulk_us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+        "us_whole_block_estimate": bulk_us * B / nb}
+
+    # top-K sparse attention (the pages' optional approximation: keep the top
+    # tenth of the positions, read only their V rows), over the same decode steps
+    tk_out = torch.empty((B, h), dtype=torch.float32, device="cuda")
+
+    def topk_launch(i):
+        t = i % w.steps + 1
+        L_t = w.prompt + t
+        fgq.fgq_decode_attn_topk_q4kv(layers[i % R].kv, steps_in[t - 1]["q"], L_t, -(-L_t // 10), 0.0, tk_out,
+                                      fgq.FGQ_DTYPE_F32, None, sh)
+
+    for i in range(min(args.warmup, 8)):
+        topk_launch(i)
+    tk_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K_steps)]
+    torch.cuda.synchronize()
+    for i in range(K_steps):
+        tk_ev[i][0].record(stream)
+        topk_launch(args.warmup + i)
+        tk_ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    tk_ms = sum(a.elapsed_time(b) for a, b in tk_ev)
+    tk_bytes = sum(acc.topk_attention_bytes(B, h, w.kv_len(t), -(-w.kv_len(t) // 10)) for t in ts)
+    kernels["topk_attention"] = {
+        "kept": "ceil(kv_len/10)", "us_per_launch": 1e3 * tk_ms / K_steps,
+        "GB_per_s": tk_bytes / (tk_ms * 1e-3) / 1e9,
+        "frac_hbm_peak": tk_bytes / (tk_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "time_vs_dense_attention": tk_ms / op_ms["attention"]}
+    tk_tr = committed_traffic("attn_topk_wave_kernel", w.name)
+    if tk_tr is not None and w.kv_len(w.steps) <= 2048:
+        kernels["topk_attention"]["traffic_bytes_per_launch"] = tk_tr["bytes_per_launch"]
+        kernels["topk_attention"]["traffic_vs_algorithmic"] = tk_tr["ratio"]
 
     if w.weights and gemm_ms >= op_ms["attention"]:
         kname = "dq_gemm_kernel"

@@ -146,6 +146,34 @@ fgq_status fgq_decode_attn_q4kv(const fgq_kv_cache *kv, const void *q_f16, int32
                                 void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * fgq_decode_attn_topk_q4kv - top-K sparse variant of fgq_decode_attn_q4kv:
+ * the paper's optional approximation that reads only the top 10% of the value
+ * cache (FlexGen review on blog.gzher.com, section 3.4; paper-graph-ui FlexGen
+ * summary, section 3.3: a section-5 approximation meant to cut I/O).  For
+ * each (sequence, head):
+ *   s_j = softmax_scale * sum_d q_d * K^_{j,d},  j in [0, kv_len)
+ *   T   = the kk = min(top_k, kv_len) positions with the largest s_j, scores
+ *         compared as fp32 values (-0 as +0), equal scores going to the
+ *         lower position
+ *   o_d = sum_{j in T} exp(s_j - m) V^_{j,d} / sum_{j in T} exp(s_j - m),
+ *         m = max_j s_j
+ * Every K row is read; only the kk kept V rows are.  top_k >= kv_len is
+ * dense attention.
+ *   q fp16 [batch][heads*head_dim]; out [batch][heads*head_dim] in out_dtype.
+ *   sel: NULL, or int32 [batch][heads][kk] receiving the kept positions of
+ *   every (sequence, head) in ascending order.
+ *   softmax_scale <= 0 selects 1/sqrt(head_dim).  Requires top_k >= 1
+ *   (FGQ_ERR_INVALID_ARG), 1 <= kv_len <= capacity, and
+ *   kv_len + kk <= FGQ_TOPK_MAX_POSITIONS (FGQ_ERR_UNSUPPORTED: the scores
+ *   and the kept list of one (sequence, head) live in on-chip memory).
+ *   No workspace.
+ */
+#define FGQ_TOPK_MAX_POSITIONS 15360
+fgq_status fgq_decode_attn_topk_q4kv(const fgq_kv_cache *kv, const void *q_f16, int32_t kv_len,
+                                     int32_t top_k, float softmax_scale, void *out, int32_t out_dtype,
+                                     int32_t *sel, void *stream);
+
+/*
  * fgq_pack_weight_g64 - one-time re-layout of a compressed weight (codes and
  * meta as fgq_quantize_g64 writes them for W [K][N]) into the tile order the
  * GEMM consumes.  Pure permutation: no value changes.

@@ -53,6 +53,12 @@ def attention_bytes(batch: int, hidden: int, kv_len: int, out_bytes: int = 4) ->
     return 2 * packed_bytes(batch * hidden * kv_len) + batch * hidden * (2 + out_bytes)
 
 
+def topk_attention_bytes(batch: int, hidden: int, kv_len: int, kept: int, out_bytes: int = 4) -> float:
+    """Top-K sparse attention: the compressed K of every position, the
+    compressed V of the kept positions only, plus the query and the output."""
+    return packed_bytes(batch * hidden * (kv_len + min(kept, kv_len))) + batch * hidden * (2 + out_bytes)
+
+
 def attention_flops(batch: int, hidden: int, kv_len: int) -> float:
     """q.k and p*v: two multiply-adds per cached element per sequence."""
     return 4.0 * batch * hidden * kv_len

@@ -1,5 +1,6 @@
 // extern "C" entry points of libfgq: argument validation on the host (nothing
 // is enqueued when a check fails), then the launches.
+#include <climits>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -17,6 +18,9 @@ fgq_status launch_pack_weight(const uint8_t *codes, const uint32_t *meta, int64_
 size_t attn_ws_bytes(int32_t batch, int32_t heads, int32_t head_dim, int32_t kv_len);
 fgq_status launch_decode_attn(const fgq_kv_cache *kv, const void *q, int32_t kv_len, float scale, void *out,
                               int32_t out_dtype, void *ws, hipStream_t stream);
+size_t attn_topk_lds_bytes(int32_t kv_len, int32_t kept);
+fgq_status launch_decode_attn_topk(const fgq_kv_cache *kv, const void *q, int32_t kv_len, int32_t kept,
+                                   float scale, void *out, int32_t out_dtype, int32_t *sel, hipStream_t stream);
 size_t gemm_ws_bytes(int64_t M, int64_t K, int64_t N);
 fgq_status launch_dequant_gemm(const void *x, int64_t M, int64_t K, int64_t N, const uint32_t *pc,
                                const uint32_t *pm, void *y, int32_t y_dtype, void *ws, hipStream_t stream);
@@ -130,6 +134,31 @@ fgq_status fgq_decode_attn_q4kv(const fgq_kv_cache *kv, const void *q_f16, int32
     }
     const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt((float)kv->head_dim);
     return launch_decode_attn(kv, q_f16, kv_len, scale, out, out_dtype, ws, static_cast<hipStream_t>(stream));
+}
+
+fgq_status fgq_decode_attn_topk_q4kv(const fgq_kv_cache *kv, const void *q_f16, int32_t kv_len, int32_t top_k,
+                                     float softmax_scale, void *out, int32_t out_dtype, int32_t *sel, void *stream) {
+    g_err[0] = 0;
+    fgq_status s = check_kv(kv);
+    if (s != FGQ_OK) return s;
+    if (out_dtype != FGQ_DTYPE_F32 && out_dtype != FGQ_DTYPE_F16)
+        return fail(FGQ_ERR_DTYPE, "out_dtype %d", out_dtype);
+    if (kv_len < 1) return fail(FGQ_ERR_SHAPE, "kv_len %d < 1", kv_len);
+    if (kv_len > kv->capacity) return fail(FGQ_ERR_CAPACITY, "kv_len %d > capacity %d", kv_len, kv->capacity);
+    if (top_k < 1) return fail(FGQ_ERR_INVALID_ARG, "top_k %d < 1", top_k);
+    if (!std::isfinite(softmax_scale)) return fail(FGQ_ERR_INVALID_ARG, "softmax_scale is not finite");
+    const int32_t kept = top_k < kv_len ? top_k : kv_len;
+    if (attn_topk_lds_bytes(kv_len, kept) > FGQ_TOPK_MAX_POSITIONS * sizeof(float))
+        return fail(FGQ_ERR_UNSUPPORTED, "kv_len + min(top_k, kv_len) = %d > %d", kv_len + kept,
+                    FGQ_TOPK_MAX_POSITIONS);
+    if ((int64_t)kv->batch * kv->heads > INT32_MAX) return fail(FGQ_ERR_SHAPE, "batch * heads > 2^31 - 1");
+    if (kv->batch == 0 || kv->heads == 0) return FGQ_OK;
+    if (!q_f16 || !out) return fail(FGQ_ERR_INVALID_ARG, "NULL q or out");
+    if (!aligned16(q_f16) || !aligned16(out) || (sel && !aligned16(sel)))
+        return fail(FGQ_ERR_ALIGN, "q/out/sel must be 16-byte aligned");
+    const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt((float)kv->head_dim);
+    return launch_decode_attn_topk(kv, q_f16, kv_len, kept, scale, out, out_dtype, sel,
+                                   static_cast<hipStream_t>(stream));
 }
 
 fgq_status fgq_pack_weight_g64(const uint8_t *codes, const uint32_t *meta, int64_t K, int64_t N,

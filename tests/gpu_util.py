@@ -98,6 +98,20 @@ class DevKV:
         torch.cuda.synchronize()
         return to_host(out).astype(np.float32)
 
+    def attend_topk(self, q16: np.ndarray, kv_len: int, top_k: int, scale: float = 0.0, out_f16: bool = False,
+                    want_sel: bool = True):
+        """Top-K sparse attention -> (fp32 [B][H*D], kept positions int32 [B][H][kk] or None)."""
+        torch = torch_cuda()
+        qd = to_dev(q16)
+        out = torch.empty((self.batch, self.heads * self.head_dim),
+                          dtype=torch.float16 if out_f16 else torch.float32, device="cuda")
+        kk = min(top_k, kv_len)
+        sel = torch.full((self.batch, self.heads, kk), -1, dtype=torch.int32, device="cuda") if want_sel else None
+        fgq.fgq_decode_attn_topk_q4kv(self.struct, qd, kv_len, top_k, scale, out,
+                                      fgq.FGQ_DTYPE_F16 if out_f16 else fgq.FGQ_DTYPE_F32, sel)
+        torch.cuda.synchronize()
+        return to_host(out).astype(np.float32), (to_host(sel) if want_sel else None)
+
     def host(self):
         return {a: to_host(getattr(self, a), np.uint32 if "meta" in a else None)
                 for a in ("k_codes", "k_meta", "v_codes", "v_meta")}

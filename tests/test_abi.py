@@ -107,6 +107,26 @@ def test_attention_validation_and_workspace(lib):
     assert fgq.fgq_decode_attn_ws_bytes(0, 96, 128, 544) == 0
 
 
+def test_topk_attention_validation(lib):
+    t = fgq.fgq_decode_attn_topk_q4kv
+    assert _status(lambda: t(_kv(), GOOD, 0, 1, 0.0, GOOD, 0, None, 0)) == fgq.FGQ_ERR_SHAPE
+    assert _status(lambda: t(_kv(), GOOD, 17, 1, 0.0, GOOD, 0, None, 0)) == fgq.FGQ_ERR_CAPACITY
+    assert _status(lambda: t(_kv(), GOOD, 4, 0, 0.0, GOOD, 0, None, 0)) == fgq.FGQ_ERR_INVALID_ARG
+    assert _status(lambda: t(_kv(), GOOD, 4, -3, 0.0, GOOD, 0, None, 0)) == fgq.FGQ_ERR_INVALID_ARG
+    assert _status(lambda: t(_kv(), GOOD, 4, 2, 0.0, GOOD, 7, None, 0)) == fgq.FGQ_ERR_DTYPE
+    assert _status(lambda: t(_kv(), GOOD, 4, 2, float("inf"), GOOD, 0, None, 0)) == fgq.FGQ_ERR_INVALID_ARG
+    assert _status(lambda: t(_kv(), BAD, 4, 2, 0.0, GOOD, 0, None, 0)) == fgq.FGQ_ERR_ALIGN
+    assert _status(lambda: t(_kv(), GOOD, 4, 2, 0.0, GOOD, 0, BAD, 0)) == fgq.FGQ_ERR_ALIGN
+    assert _status(lambda: t(_kv(), 0, 4, 2, 0.0, GOOD, 0, None, 0)) == fgq.FGQ_ERR_INVALID_ARG
+    assert _status(lambda: t(_kv(head_dim=96), GOOD, 4, 2, 0.0, GOOD, 0, None, 0)) == fgq.FGQ_ERR_SHAPE
+    # the scores and kept list of one (sequence, head) must fit on chip
+    cap = 20000
+    assert _status(lambda: t(_kv(cap=cap), GOOD, 14000, 1400, 0.0, GOOD, 0, None, 0)) == fgq.FGQ_ERR_UNSUPPORTED
+    assert _status(lambda: t(_kv(cap=cap), GOOD, 8000, 8000, 0.0, GOOD, 0, None, 0)) == fgq.FGQ_ERR_UNSUPPORTED
+    # empty batch: nothing to do, no pointer is touched
+    assert _status(lambda: t(_kv(batch=0), 0, 4, 2, 0.0, 0, 0, None, 0)) == fgq.FGQ_OK
+
+
 def test_gemm_validation_and_workspace(lib):
     gm = fgq.fgq_dequant_gemm
     assert _status(lambda: gm(GOOD, 4, 1, 48, 64, GOOD, GOOD, GOOD, 0, 0, 0, 0)) == fgq.FGQ_ERR_SHAPE

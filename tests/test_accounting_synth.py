@@ -53,6 +53,15 @@ def test_packed_cost_per_element():
 
 # ------------------------------------------------------------------ generator
 
+def test_topk_attention_bytes():
+    """Keeping every position costs what dense attention costs; keeping a tenth
+    reads K in full and V for a tenth: 0.5625*h*(L + L/10) plus q and out."""
+    B, h, L = 144, 12288, 540
+    assert acc.topk_attention_bytes(B, h, L, L) == acc.attention_bytes(B, h, L)
+    assert acc.topk_attention_bytes(B, h, L, 10 * L) == acc.attention_bytes(B, h, L)
+    assert acc.topk_attention_bytes(B, h, L, 54) == 0.5625 * B * h * (L + 54) + B * h * 6
+
+
 def test_philox_known_answers():
     """Known-answer vectors published with the Random123 library for
     Philox4x32-10 (zero, all-ones and pi-digit counters/keys)."""
