@@ -235,7 +235,7 @@ def build_weights(torch, fgq, w):
         meta = torch.empty((K, N // 64), dtype=torch.int32, device="cuda")
         fgq.fgq_quantize_g64(wd, K, N, N, codes, meta)
         pc = torch.empty(K * N // 8, dtype=torch.int32, device="cuda")
-        pm = torch.empty(K * N // 64, dtype=torch.int32, device="cuda")
+        pm = torch.empty(fgq.fgq_pack_weight_meta_words(K, N), dtype=torch.int32, device="cuda")
         fgq.fgq_pack_weight_g64(codes, meta, K, N, pc, pm)
         torch.cuda.synchronize()
         del wd, codes, meta

@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define FGQ_ABI_VERSION 1
+#define FGQ_ABI_VERSION 2
 
 typedef int32_t fgq_status;
 #define FGQ_OK 0
@@ -176,15 +176,23 @@ fgq_status fgq_decode_attn_topk_q4kv(const fgq_kv_cache *kv, const void *q_f16, 
 /*
  * fgq_pack_weight_g64 - one-time re-layout of a compressed weight (codes and
  * meta as fgq_quantize_g64 writes them for W [K][N]) into the tile order the
- * GEMM consumes.  Pure permutation: no value changes.
+ * GEMM consumes.
  *   packed_codes uint32 [K/32][N/64][64][4]: word (kc, g, lane, j) holds the
  *     codes of W[k][n], n = 64g + 16j + lane%16, k = 32kc + 8(lane/16) + i for
- *     i = 0..7, code i in nibble [0,4,1,5,2,6,3,7][i] of the word.
- *   packed_meta  uint32 [K/32][N/64][4][8]: entry (kc, g, kq, t) is the half2
- *     {step[k], step[k+1]} for t < 4, {min[k], min[k+1]} for t >= 4, with
- *     k = 32kc + 8kq + 2(t%4), of group g.
- * Same byte sizes as codes and meta.  Requires K % 32 == 0, N % 64 == 0.
+ *     i = 0..7, code i in nibble [0,4,1,5,2,6,3,7][i] of the word (same byte
+ *     size as codes).
+ *   packed_meta uint32, fgq_pack_weight_meta_words(K, N) = K*N/64 + N/64
+ *     words: first [K/32][N/64][4][8], entry (kc, g, kq, t) the half2
+ *     {step[k] * 2^s, step[k+1] * 2^s} for t < 4 (s = 24 - e_g for even t,
+ *     20 - e_g for odd t) and {min[k] * 2^-e_g, min[k+1] * 2^-e_g} for
+ *     t >= 4, with k = 32kc + 8kq + 2(t%4), each rounded to fp16 (exact
+ *     unless it falls below the fp16 normal range); then int32 e_g for every
+ *     column group g: the smallest e >= 0 with max_k step[k][g] * 2^(24-e)
+ *     <= 65504.  (The GEMM multiplies codes placed as q * 2^-24 or q * 2^-20
+ *     by these steps, and its result by 2^e_g.)
+ * Requires K % 32 == 0, N % 64 == 0.
  */
+size_t fgq_pack_weight_meta_words(int64_t K, int64_t N);
 fgq_status fgq_pack_weight_g64(const uint8_t *codes, const uint32_t *meta, int64_t K, int64_t N,
                                uint32_t *packed_codes, uint32_t *packed_meta, void *stream);
 

@@ -161,6 +161,11 @@ fgq_status fgq_decode_attn_topk_q4kv(const fgq_kv_cache *kv, const void *q_f16, 
                                    static_cast<hipStream_t>(stream));
 }
 
+size_t fgq_pack_weight_meta_words(int64_t K, int64_t N) {
+    if (K <= 0 || N <= 0 || K % 32 != 0 || N % 64 != 0) return 0;
+    return (size_t)(K * (N / 64) + N / 64);
+}
+
 fgq_status fgq_pack_weight_g64(const uint8_t *codes, const uint32_t *meta, int64_t K, int64_t N,
                                uint32_t *packed_codes, uint32_t *packed_meta, void *stream) {
     g_err[0] = 0;

@@ -20,10 +20,13 @@
 //    wave's packed code words and its group metadata) as deep as the LDS
 //    allows, all but one slot in flight, one barrier per slot;
 //  * the packed weight layout puts the 8 k-values of one output channel in
-//    one 32-bit word, in the nibble order that AND/OR with the fp16 magic
-//    numbers 0x6400 (1024 + q) and 0x5400 (64 + q) turn into two values per
-//    op; a packed subtract and a packed FMA give two fp16 W^ values, and the
-//    next chunk is dequantised between the current chunk's MFMAs;
+//    one 32-bit word, in a nibble order where one AND leaves two codes in
+//    the mantissas of two fp16 subnormals (q * 2^-24 or q * 2^-20); the
+//    packed metadata holds the steps pre-scaled to match and everything
+//    scaled by a per-column-group power of two 2^-e that keeps the scaled
+//    steps finite, so one packed FMA gives two values 2^-e * W^ (W^ itself
+//    rounded once) and the epilogue multiplies by 2^e; the next chunk is
+//    dequantised between the current chunk's MFMAs;
 //  * A fragments stream three m-tiles ahead across chunk and slot boundaries;
 //    X rows sit in LDS with a 16-byte-slot XOR swizzle, so the rows of an A
 //    fragment read hit distinct banks;
@@ -227,26 +230,22 @@ void dq_gemm_kernel(const uint16_t *__restrict__ x, int M, int64_t K, int64_t N,
         if (lane < nmeta) dma16(pm + ((int64_t)kc * ng + gl) * 32, moff, sb + C::XBYTES + C::BBYTES + wv * LC * 128);
     };
 
-    // The fp16 magic numbers live in VGPRs so that the AND/OR pairs below
-    // become single v_and_or_b32 (a VOP3 operand may not be a literal here).
-    uint32_t mag1024, mag64;
-    asm volatile("v_mov_b32 %0, 0x64006400" : "=v"(mag1024));
-    asm volatile("v_mov_b32 %0, 0x54005400" : "=v"(mag64));
-
     // Half h (0..7) of the dequantisation of one chunk's B fragments: n-tile
     // j = h/2, k-values 0..3 (h even) or 4..7 (h odd) of the packed word.
-    // The code pairs become 1024 + q and 64 + q in fp16 through AND/OR with
-    // the magic numbers; a packed subtract and a packed FMA give the fp16 W^.
+    // One AND leaves a code pair in the mantissas of two fp16 subnormals:
+    // q * 2^-24 (codes 0, 1 of the pair of pairs) or q * 2^-20 (codes 2, 3).
+    // The packed steps are pre-scaled by 2^(24 - e) and 2^(20 - e) and the
+    // minima by 2^-e, so one packed FMA gives 2^-e * fp16(min + q * step)
+    // with a single rounding (the product is exact); the epilogue multiplies
+    // by 2^e.
     auto dequant_half = [&](const uint4 cw, const uint4 ms, const uint4 mm, int h, u32x4(&b)[4]) {
         const int j = h >> 1;
         const uint32_t W[4] = {cw.x, cw.y, cw.z, cw.w};
         const uint32_t w = (h & 1) ? W[j] >> 8 : W[j];
         const uint32_t s0 = (h & 1) ? ms.z : ms.x, s1 = (h & 1) ? ms.w : ms.y;
         const uint32_t n0 = (h & 1) ? mm.z : mm.x, n1 = (h & 1) ? mm.w : mm.y;
-        const uint32_t p0 = (w & 0x000F000Fu) | mag1024;
-        const uint32_t p1 = (w & 0x00F000F0u) | mag64;
-        const f16x2 c0 = as_f16x2(p0) - f16x2{(_Float16)1024.0f, (_Float16)1024.0f};
-        const f16x2 c1 = as_f16x2(p1) - f16x2{(_Float16)64.0f, (_Float16)64.0f};
+        const f16x2 c0 = as_f16x2(w & 0x000F000Fu);
+        const f16x2 c1 = as_f16x2(w & 0x00F000F0u);
         const f16x2 w0 = __builtin_elementwise_fma(c0, as_f16x2(s0), as_f16x2(n0));
         const f16x2 w1 = __builtin_elementwise_fma(c1, as_f16x2(s1), as_f16x2(n1));
         const uint32_t u0 = __builtin_bit_cast(uint32_t, w0), u1 = __builtin_bit_cast(uint32_t, w1);
@@ -406,6 +405,12 @@ void dq_gemm_kernel(const uint16_t *__restrict__ x, int M, int64_t K, int64_t N,
     }
 
     if (!gvalid || phase != 0) return;
+    // ---- undo the column group's exponent (a power of two: exact)
+    const float gscale = __builtin_amdgcn_ldexpf(1.0f, (int)pm[(int64_t)nchunks * ng * 32 + g]);
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] *= gscale;
     // ---- store: lane holds rows 4*(lane/16)+r, column lane%16 of each 16x16 tile
     const int crow = (lane >> 4) * 4, ccol = lane & 15;
     const int64_t col0 = g * 64 + ccol;

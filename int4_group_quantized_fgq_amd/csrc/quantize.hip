@@ -149,9 +149,47 @@ __global__ __launch_bounds__(256) void pack_codes_kernel(const uint8_t *__restri
     packed[w] = out;
 }
 
-// One thread per packed meta word (kc, g, kq, t).
+// Column-group exponent e_g: the smallest e >= 0 with max_k step[k][g] *
+// 2^(24 - e) <= 65504, so that every step scaled for the GEMM's subnormal
+// code placement stays a finite fp16.  One workgroup per column group g.
+__global__ __launch_bounds__(256) void pack_exponent_kernel(const uint32_t *__restrict__ meta, int64_t K,
+                                                            int64_t N, int32_t *__restrict__ exps) {
+    __shared__ uint32_t red[256];
+    const int64_t ng = N >> 6;
+    const int64_t g = blockIdx.x;
+    uint32_t mx = 0u;   // steps are >= +0, so their fp16 bits order like their values
+    for (int64_t k = threadIdx.x; k < K; k += 256) {
+        const uint32_t st = meta[k * ng + g] >> 16;
+        mx = st > mx ? st : mx;
+    }
+    red[threadIdx.x] = mx;
+    __syncthreads();
+    for (int off = 128; off > 0; off >>= 1) {
+        if ((int)threadIdx.x < off) red[threadIdx.x] = max(red[threadIdx.x], red[threadIdx.x + off]);
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) {
+        const float ms = h2f((uint16_t)red[0]);
+        int e = 0;
+        while (e < 24 && ms * __builtin_amdgcn_ldexpf(1.0f, 24 - e) > 65504.0f) ++e;
+        exps[g] = e;
+    }
+}
+
+// fp16 value (bits) times 2^s, rounded to fp16 (exact unless the result is
+// an fp16 subnormal).
+__device__ __forceinline__ uint32_t scale_h(uint32_t hbits, int s) {
+    return f2h_rne(h2f((uint16_t)hbits) * __builtin_amdgcn_ldexpf(1.0f, s));
+}
+
+// One thread per packed meta word (kc, g, kq, t).  The GEMM places codes
+// 0, 1 (and 4, 5) of a word in fp16 subnormal mantissas as q * 2^-24, and
+// codes 2, 3 (and 6, 7) as q * 2^-20, so their steps are stored times
+// 2^(24 - e_g) (t = 0, 2) and 2^(20 - e_g) (t = 1, 3), and the minima
+// times 2^-e_g; the GEMM multiplies its result by 2^e_g.
 __global__ __launch_bounds__(256) void pack_meta_kernel(const uint32_t *__restrict__ meta, int64_t K,
-                                                        int64_t N, uint32_t *__restrict__ packed) {
+                                                        int64_t N, const int32_t *__restrict__ exps,
+                                                        uint32_t *__restrict__ packed) {
     const int64_t words = K * N / 64;
     const int64_t w = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (w >= words) return;
@@ -162,7 +200,11 @@ __global__ __launch_bounds__(256) void pack_meta_kernel(const uint32_t *__restri
     const int64_t g = tile % ng, kc = tile / ng;
     const int64_t k = 32 * kc + 8 * kq + 2 * (t & 3);
     const uint32_t m0 = meta[k * ng + g], m1 = meta[(k + 1) * ng + g];
-    packed[w] = (t < 4) ? ((m0 >> 16) | (m1 & 0xffff0000u)) : ((m0 & 0xffffu) | (m1 << 16));
+    const int e = exps[g];
+    const int s = t >= 4 ? -e : ((t & 1) ? 20 - e : 24 - e);
+    const uint32_t h0 = t < 4 ? (m0 >> 16) : (m0 & 0xffffu);
+    const uint32_t h1 = t < 4 ? (m1 >> 16) : (m1 & 0xffffu);
+    packed[w] = scale_h(h0, s) | (scale_h(h1, s) << 16);
 }
 
 }  // namespace
@@ -194,7 +236,11 @@ fgq_status launch_pack_weight(const uint8_t *codes, const uint32_t *meta, int64_
     pack_codes_kernel<<<dim3((unsigned)((cw + 255) / 256)), dim3(256), 0, stream>>>(codes, K, N, packed_codes);
     fgq_status s = check_launch("pack_codes_kernel");
     if (s != FGQ_OK) return s;
-    pack_meta_kernel<<<dim3((unsigned)((mw + 255) / 256)), dim3(256), 0, stream>>>(meta, K, N, packed_meta);
+    int32_t *exps = reinterpret_cast<int32_t *>(packed_meta + mw);   // [N/64], after the meta words
+    pack_exponent_kernel<<<dim3((unsigned)(N / 64)), dim3(256), 0, stream>>>(meta, K, N, exps);
+    s = check_launch("pack_exponent_kernel");
+    if (s != FGQ_OK) return s;
+    pack_meta_kernel<<<dim3((unsigned)((mw + 255) / 256)), dim3(256), 0, stream>>>(meta, K, N, exps, packed_meta);
     return check_launch("pack_meta_kernel");
 }
 

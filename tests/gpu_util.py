@@ -120,7 +120,7 @@ class DevKV:
 def pack(codes_d, meta_d, K, N):
     torch = torch_cuda()
     pc = torch.empty(K * N // 8, dtype=torch.int32, device="cuda")
-    pm = torch.empty(K * N // 64, dtype=torch.int32, device="cuda")
+    pm = torch.empty(fgq.fgq_pack_weight_meta_words(K, N), dtype=torch.int32, device="cuda")
     fgq.fgq_pack_weight_g64(codes_d, meta_d, K, N, pc, pm)
     return pc, pm
 
@@ -137,9 +137,18 @@ def gemm(x16: np.ndarray, g: int, m: int, pc, pm, K: int, N: int, y_f16: bool = 
     return to_host(y).astype(np.float32)
 
 
+def _scale_f16_bits(h: np.ndarray, s: np.ndarray) -> np.ndarray:
+    """fp16 bit patterns times 2^s (per element), rounded to fp16 (numpy's
+    float32 -> float16 conversion rounds to nearest even)."""
+    f = h.astype(np.uint16).view(np.float16).astype(np.float32) * np.exp2(s.astype(np.float32))
+    return f.astype(np.float16).view(np.uint16).astype(np.uint32)
+
+
 def pack_reference(codes: np.ndarray, meta: np.ndarray):
-    """The packed layout of include/fgq.h, built with numpy index arithmetic
-    (a re-layout of stored values; no arithmetic of the method)."""
+    """The packed layout of include/fgq.h, built with numpy: a re-layout of
+    the stored codes, and the stored steps and minima times the powers of two
+    the header defines (per column group g the smallest e >= 0 with
+    max_k step * 2^(24-e) <= 65504), followed by the exponents."""
     K, half = codes.shape
     N = half * 2
     q = np.zeros((K, N), np.uint32)
@@ -157,10 +166,17 @@ def pack_reference(codes: np.ndarray, meta: np.ndarray):
             out[:, :, :, j] |= vals << np.uint32(4 * slot_of[i])
     mins = (meta & 0xFFFF).astype(np.uint32)
     steps = (meta >> 16).astype(np.uint32)
+    max_step = steps.astype(np.uint16).view(np.float16).astype(np.float64).max(axis=0)   # [g]
+    e = np.zeros(g_n, np.int64)
+    for g in range(g_n):
+        while e[g] < 24 and max_step[g] * 2.0 ** (24 - e[g]) > 65504.0:
+            e[g] += 1
     pm = np.zeros((kc_n, g_n, 4, 8), np.uint32)
     for kq in range(4):
         for t in range(4):
             k = np.arange(kc_n) * 32 + 8 * kq + 2 * t
-            pm[:, :, kq, t] = steps[k, :] | (steps[k + 1, :] << np.uint32(16))
-            pm[:, :, kq, t + 4] = mins[k, :] | (mins[k + 1, :] << np.uint32(16))
-    return out.reshape(-1), pm.reshape(-1)
+            sh = np.broadcast_to((24 if t % 2 == 0 else 20) - e, (kc_n, g_n))
+            pm[:, :, kq, t] = _scale_f16_bits(steps[k, :], sh) | (_scale_f16_bits(steps[k + 1, :], sh) << np.uint32(16))
+            sm = np.broadcast_to(-e, (kc_n, g_n))
+            pm[:, :, kq, t + 4] = _scale_f16_bits(mins[k, :], sm) | (_scale_f16_bits(mins[k + 1, :], sm) << np.uint32(16))
+    return out.reshape(-1), np.concatenate([pm.reshape(-1), e.astype(np.uint32)])

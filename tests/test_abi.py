@@ -32,14 +32,14 @@ def test_every_declared_symbol_is_exported(lib):
 
 def test_header_compiles_as_plain_c(tmp_path):
     src = tmp_path / "t.c"
-    src.write_text('#include "fgq.h"\nint main(void){ fgq_kv_cache kv; (void)kv; return fgq_abi_version() != 1; }\n')
+    src.write_text('#include "fgq.h"\nint main(void){ fgq_kv_cache kv; (void)kv; return fgq_abi_version() != 2; }\n')
     inc = os.path.join(os.path.dirname(fgq.HEADER_PATH))
     subprocess.check_call(["gcc", "-std=c99", "-Wall", "-Werror", "-c", str(src), "-I", inc, "-o",
                            str(tmp_path / "t.o")])
 
 
 def test_version_and_status_strings(lib):
-    assert fgq.fgq_abi_version() == 1
+    assert fgq.fgq_abi_version() == 2
     assert fgq.status_string(fgq.FGQ_OK) == "ok"
     codes = [fgq.FGQ_ERR_INVALID_ARG, fgq.FGQ_ERR_SHAPE, fgq.FGQ_ERR_ALIGN, fgq.FGQ_ERR_CAPACITY,
              fgq.FGQ_ERR_WORKSPACE, fgq.FGQ_ERR_DTYPE, fgq.FGQ_ERR_DEVICE, fgq.FGQ_ERR_UNSUPPORTED]

@@ -248,14 +248,44 @@ def _gemm_case(x16, g, m, Wt):
 
 
 def test_pack_matches_layout_definition():
+    """Column groups of very different ranges (exponents 0 up to 24, fp16
+    subnormal minima after scaling) packed bit for bit as the header says."""
     rng = np.random.default_rng(3)
     Wt = (rng.standard_normal((96, 320)) * 0.02).astype(np.float16)
+    Wt[:, 64:128] *= np.float16(400.0)                      # steps ~ 2.5: e = 16
+    Wt[:, 128:192] = (rng.standard_normal((96, 64)) * 20000).clip(-65000, 65000).astype(np.float16)
+    Wt[:, 192:256] *= np.float16(1e-3)                      # tiny steps: e = 0
     gu.note("pack layout 96x320")
     codes, meta = oracle.quantize_g64(Wt)
     pc, pm = gu.pack(gu.to_dev(codes), gu.to_dev(meta), 96, 320)
     ec, em = gu.pack_reference(codes, meta)
+    assert em.size == gu.fgq.fgq_pack_weight_meta_words(96, 320)
     assert np.array_equal(gu.to_host(pc, np.uint32), ec)
     assert np.array_equal(gu.to_host(pm, np.uint32), em)
+    assert em[-5:].min() == 0 and em[-5:].max() >= 20      # the tiny and the huge column groups
+
+
+def test_gemm_on_wide_ranging_column_groups():
+    """The GEMM undoes each column group's power of two: groups whose steps
+    need exponents from 0 to 24 against the oracle."""
+    rng = np.random.default_rng(31)
+    K, N, g, m = 256, 384, 8, 2
+    Wt = (rng.standard_normal((K, N)) * 0.02).astype(np.float16)
+    Wt[:, 64:128] *= np.float16(400.0)
+    Wt[:, 128:192] = (rng.standard_normal((K, 64)) * 20000).clip(-65000, 65000).astype(np.float16)
+    Wt[:, 192:256] *= np.float16(1e-3)
+    Wt[:, 256:320] = np.float16(0.75)                       # constant groups: step 0
+    X = (rng.standard_normal((g * m, K)) * 0.01).astype(np.float16)
+    rc, rm, pc, pm = _gemm_case(X, g, m, Wt)
+    ex = gu.to_host(pm, np.uint32)[-(N // 64):]
+    gu.note("gemm wide-ranging groups, exponents %s" % ex.tolist())
+    assert ex.min() == 0 and ex.max() >= 20
+    y = gu.gemm(X, g, m, pc, pm, K, N)
+    exp = oracle.dequant_gemm(X, g, m, rc, rm)
+    for c in range(N // 64):   # each column group against the bar on its own scale
+        sl = slice(64 * c, 64 * c + 64)
+        s = max(1.0, float(np.abs(exp[:, sl]).max()))
+        gu.assert_close(y[:, sl] / s, exp[:, sl] / s, "group %d (scaled by %.3g)" % (c, s))
 
 
 # The last three take two k-phases per workgroup: an odd chunk count with no
