@@ -56,8 +56,10 @@ def _load():
         lib.oracle_decode_attn.argtypes = [vp, i32, i32, i32, i32, vp, vp, vp, vp, i32, dbl, vp]
         lib.oracle_dequant_gemm.argtypes = [vp, i32, i32, i64, i64, vp, vp, vp]
         lib.oracle_decode_attn_topk.argtypes = [vp, i32, i32, i32, i32, vp, vp, vp, vp, i32, i32, dbl, vp, vp]
+        lib.oracle_prefill_attn.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32, dbl, vp]
         for f in (lib.oracle_quantize_g64, lib.oracle_dequant_g64, lib.oracle_kv_append,
-                  lib.oracle_decode_attn, lib.oracle_dequant_gemm, lib.oracle_decode_attn_topk):
+                  lib.oracle_decode_attn, lib.oracle_dequant_gemm, lib.oracle_decode_attn_topk,
+                  lib.oracle_prefill_attn):
             f.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -151,6 +153,24 @@ def decode_attn_topk(kv: KVCache, q: np.ndarray, kv_len: int, top_k: int, scale:
                                            kv_len, top_k, float(scale), out.ctypes.data, sel.ctypes.data),
            "decode_attn_topk")
     return out, sel
+
+
+def prefill_attn(q: np.ndarray, k: np.ndarray, v: np.ndarray, heads: int, scale: float = 0.0,
+                 rows=None) -> np.ndarray:
+    """Causal prefill attention over fp16 q, k, v [B][s][H*D] -> fp32 [B][s][H*D];
+    only query rows [rows[0], rows[1]) are computed (others are NaN).
+    scale <= 0 means 1/sqrt(D)."""
+    q, k, v = _c(q, np.float16), _c(k, np.float16), _c(v, np.float16)
+    B, s, h = q.shape
+    assert k.shape == q.shape and v.shape == q.shape and h % heads == 0
+    D = h // heads
+    if scale <= 0.0:
+        scale = 1.0 / np.sqrt(D)
+    r0, r1 = (0, s) if rows is None else rows
+    out = np.full((B, s, h), np.nan, np.float32)
+    _check(_load().oracle_prefill_attn(q.ctypes.data, k.ctypes.data, v.ctypes.data, B, s, heads, D, r0, r1,
+                                       float(scale), out.ctypes.data), "prefill_attn")
+    return out
 
 
 def dequant_gemm(x: np.ndarray, g: int, m: int, codes: np.ndarray, meta: np.ndarray) -> np.ndarray:

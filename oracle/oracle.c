@@ -329,6 +329,58 @@ int oracle_decode_attn_topk(const uint16_t *q, int32_t batch, int32_t heads, int
     return ORACLE_OK;
 }
 
+/* Prefill attention over the prompt's fp16 K and V, before they are
+ * compressed: the prefill step runs every prompt token at once and leaves
+ * each layer's KV cache behind (paper-graph-ui FlexGen summary, section 3.4,
+ * the problem formulation around Figure 2, where token 0 of the grid is the
+ * prefill step; FlexGen review on blog.gzher.com, section 1, the prefill /
+ * decode split).  OPT models are decoder-only, so each prompt token attends
+ * to itself and the tokens before it (the plainest reading; the pages do not
+ * spell out the mask).  q, k, v fp16 [batch][seq][heads*head_dim]
+ * (token-major, as the QKV projection emits them); rows [row0, row1) of
+ * every sequence and head are computed:
+ *   s_ij = scale * sum_d q_{i,d} k_{j,d}               j <= i   (fp64)
+ *   o_i  = sum_{j<=i} exp(s_ij - m_i) v_j / sum_{j<=i} exp(s_ij - m_i)
+ * out fp32 [batch][seq][heads*head_dim]; rows outside [row0, row1) are
+ * left untouched. */
+int oracle_prefill_attn(const uint16_t *q, const uint16_t *k, const uint16_t *v, int32_t batch, int32_t seq,
+                        int32_t heads, int32_t head_dim, int32_t row0, int32_t row1, double scale, float *out) {
+    if (batch < 0 || seq < 0 || heads < 0 || head_dim <= 0 || row0 < 0 || row1 > seq || row0 > row1)
+        return ORACLE_ERR_SHAPE;
+    const int64_t h = (int64_t)heads * head_dim;
+    #pragma omp parallel for collapse(3) schedule(dynamic, 1)
+    for (int32_t b = 0; b < batch; ++b)
+        for (int32_t hd = 0; hd < heads; ++hd)
+            for (int32_t i = row0; i < row1; ++i) {
+                double *s = (double *)malloc(sizeof(double) * (size_t)(i + 1));
+                double *o = (double *)calloc((size_t)head_dim, sizeof(double));
+                const uint16_t *qi = q + ((int64_t)b * seq + i) * h + (int64_t)hd * head_dim;
+                double mx = -INFINITY;
+                for (int32_t j = 0; j <= i; ++j) {
+                    const uint16_t *kj = k + ((int64_t)b * seq + j) * h + (int64_t)hd * head_dim;
+                    double acc = 0.0;
+                    for (int32_t d = 0; d < head_dim; ++d)
+                        acc += (double)oracle_f16_to_f32(qi[d]) * (double)oracle_f16_to_f32(kj[d]);
+                    s[j] = acc * scale;
+                    if (s[j] > mx) mx = s[j];
+                }
+                double den = 0.0;
+                for (int32_t j = 0; j <= i; ++j) {
+                    s[j] = exp(s[j] - mx);
+                    den += s[j];
+                }
+                for (int32_t j = 0; j <= i; ++j) {
+                    const uint16_t *vj = v + ((int64_t)b * seq + j) * h + (int64_t)hd * head_dim;
+                    for (int32_t d = 0; d < head_dim; ++d) o[d] += s[j] * (double)oracle_f16_to_f32(vj[d]);
+                }
+                float *oi = out + ((int64_t)b * seq + i) * h + (int64_t)hd * head_dim;
+                for (int32_t d = 0; d < head_dim; ++d) oi[d] = (float)(o[d] / den);
+                free(s);
+                free(o);
+            }
+    return ORACLE_OK;
+}
+
 /* Weight GEMM of one block of g*m rows (m GPU batches of g rows each, batch j
  * occupying rows j*g .. j*g+g-1) against the compressed weight W [K][N]
  * (codes [K][N/2], meta [K][N/64]: groups along the output channel n):
