@@ -580,7 +580,25 @@ def main():
     b1.record(stream)
     torch.cuda.synchronize()
     bulk_us = 1e3 * b0.elapsed_time(b1) / reps
-    del kd, vd
+    # prefill attention over the same sequences' fp16 prompt (causal), which
+    # precedes that compression in a prefill step
+    qd = torch.from_numpy(synth.prompt_q(w, nb=nb)).to("cuda")
+    pf_out = torch.empty((nb, w.prompt, h), dtype=torch.float32, device="cuda")
+    fgq.fgq_prefill_attn_f16(qd, kd, vd, nb, w.prompt, H, D, 0.0, pf_out, fgq.FGQ_DTYPE_F32, sh)
+    torch.cuda.synchronize()
+    b0.record(stream)
+    for _ in range(reps):
+        fgq.fgq_prefill_attn_f16(qd, kd, vd, nb, w.prompt, H, D, 0.0, pf_out, fgq.FGQ_DTYPE_F32, sh)
+    b1.record(stream)
+    torch.cuda.synchronize()
+    pf_us = 1e3 * b0.elapsed_time(b1) / reps
+    pf_flops = acc.prefill_attention_flops(nb, h, w.prompt)
+    kernels["prefill_attention"] = {
+        "sequences": nb, "tokens_per_sequence": w.prompt, "us_per_launch": pf_us,
+        "TFLOP_per_s": pf_flops / (pf_us * 1e-6) / 1e12,
+        "frac_mfma_peak": pf_flops / (pf_us * 1e-6) / 1e12 / MFMA_F16_PEAK_TFLOPS,
+        "us_whole_block_estimate": pf_us * B / nb}
+    del kd, vd, qd, pf_out
     kernels["prompt_bulk_append"] = {
         "sequences": nb, "tokens_per_sequence": w.prompt, "us_per_launch": bulk_us,
         "GB_per_s": acc.append_bytes(nb, h, w.prompt) / (bulk_us * 1e-6) / 1e9,

@@ -174,6 +174,24 @@ fgq_status fgq_decode_attn_topk_q4kv(const fgq_kv_cache *kv, const void *q_f16, 
                                      int32_t *sel, void *stream);
 
 /*
+ * fgq_prefill_attn_f16 - attention of the prefill step over the prompt's own
+ * fp16 q, k, v, before its K and V are compressed (then one bulk
+ * fgq_kv_append with n_new = seq): the prefill step runs every prompt token
+ * at once and leaves each layer's KV cache behind (paper-graph-ui FlexGen
+ * summary, section 3.4, token 0 of the Figure-2 grid; FlexGen review on
+ * blog.gzher.com, section 1).  Causal: per (sequence, head, token i)
+ *   o_i = sum_{j<=i} softmax_j(softmax_scale * q_i . k_j) v_j
+ *   q, k, v fp16 [batch][seq][heads*head_dim] (token-major, as the QKV
+ *   projection emits them); out [batch][seq][heads*head_dim] in out_dtype.
+ *   softmax_scale <= 0 selects 1/sqrt(head_dim).  head_dim 64 or 128;
+ *   batch, heads <= 65535 (FGQ_ERR_SHAPE).  Fp16 matrix cores with fp32
+ *   accumulation; the probabilities enter P.V rounded to fp16.  No workspace.
+ */
+fgq_status fgq_prefill_attn_f16(const void *q_f16, const void *k_f16, const void *v_f16, int32_t batch,
+                                int32_t seq, int32_t heads, int32_t head_dim, float softmax_scale, void *out,
+                                int32_t out_dtype, void *stream);
+
+/*
  * fgq_pack_weight_g64 - one-time re-layout of a compressed weight (codes and
  * meta as fgq_quantize_g64 writes them for W [K][N]) into the tile order the
  * GEMM consumes.

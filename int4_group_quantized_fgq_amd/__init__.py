@@ -66,6 +66,7 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
         "fgq_decode_attn_ws_bytes": ([i32, i32, i32, i32], sz),
         "fgq_decode_attn_q4kv": ([kvp, vp, i32, f32, vp, i32, vp, sz, vp], i32),
         "fgq_decode_attn_topk_q4kv": ([kvp, vp, i32, i32, f32, vp, i32, vp, vp], i32),
+        "fgq_prefill_attn_f16": ([vp, vp, vp, i32, i32, i32, i32, f32, vp, i32, vp], i32),
         "fgq_pack_weight_meta_words": ([i64, i64], sz),
         "fgq_pack_weight_g64": ([vp, vp, i64, i64, vp, vp, vp], i32),
         "fgq_dequant_gemm_ws_bytes": ([i64, i64, i64], sz),
@@ -151,6 +152,11 @@ def fgq_decode_attn_topk_q4kv(kv: fgq_kv_cache, q, kv_len, top_k, softmax_scale,
                               stream=None) -> None:
     _check(load().fgq_decode_attn_topk_q4kv(ctypes.byref(kv), _ptr(q), kv_len, top_k, softmax_scale, _ptr(out),
                                             out_dtype, _ptr(sel), _stream(stream)), "fgq_decode_attn_topk_q4kv")
+
+
+def fgq_prefill_attn_f16(q, k, v, batch, seq, heads, head_dim, softmax_scale, out, out_dtype, stream=None) -> None:
+    _check(load().fgq_prefill_attn_f16(_ptr(q), _ptr(k), _ptr(v), batch, seq, heads, head_dim, softmax_scale,
+                                       _ptr(out), out_dtype, _stream(stream)), "fgq_prefill_attn_f16")
 
 
 def fgq_pack_weight_meta_words(K, N) -> int:

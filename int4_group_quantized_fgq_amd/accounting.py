@@ -64,6 +64,12 @@ def attention_flops(batch: int, hidden: int, kv_len: int) -> float:
     return 4.0 * batch * hidden * kv_len
 
 
+def prefill_attention_flops(batch: int, hidden: int, seq: int) -> float:
+    """Causal prefill attention: q.k and p*v, two multiply-adds per element
+    for each of the seq*(seq+1)/2 (query, key) pairs of a sequence."""
+    return 4.0 * batch * hidden * seq * (seq + 1) / 2
+
+
 def append_bytes(batch: int, hidden: int, n_new: int = 1) -> float:
     """fp16 K and V rows in, compressed K and V rows out."""
     return batch * n_new * (2 * 2 * hidden + 2 * packed_bytes(hidden))

@@ -21,6 +21,9 @@ fgq_status launch_decode_attn(const fgq_kv_cache *kv, const void *q, int32_t kv_
 size_t attn_topk_lds_bytes(int32_t kv_len, int32_t kept);
 fgq_status launch_decode_attn_topk(const fgq_kv_cache *kv, const void *q, int32_t kv_len, int32_t kept,
                                    float scale, void *out, int32_t out_dtype, int32_t *sel, hipStream_t stream);
+fgq_status launch_prefill_attn(const void *q, const void *k, const void *v, int32_t batch, int32_t seq,
+                               int32_t heads, int32_t head_dim, float scale, void *out, int32_t out_dtype,
+                               hipStream_t stream);
 size_t gemm_ws_bytes(int64_t M, int64_t K, int64_t N);
 fgq_status launch_dequant_gemm(const void *x, int64_t M, int64_t K, int64_t N, const uint32_t *pc,
                                const uint32_t *pm, void *y, int32_t y_dtype, void *ws, hipStream_t stream);
@@ -159,6 +162,30 @@ fgq_status fgq_decode_attn_topk_q4kv(const fgq_kv_cache *kv, const void *q_f16, 
     const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt((float)kv->head_dim);
     return launch_decode_attn_topk(kv, q_f16, kv_len, kept, scale, out, out_dtype, sel,
                                    static_cast<hipStream_t>(stream));
+}
+
+fgq_status fgq_prefill_attn_f16(const void *q_f16, const void *k_f16, const void *v_f16, int32_t batch,
+                                int32_t seq, int32_t heads, int32_t head_dim, float softmax_scale, void *out,
+                                int32_t out_dtype, void *stream) {
+    g_err[0] = 0;
+    if (batch < 0 || seq < 0 || heads < 0 || head_dim <= 0) return fail(FGQ_ERR_INVALID_ARG, "negative size");
+    if (head_dim != 64 && head_dim != 128) {
+        if (head_dim % 64 != 0) return fail(FGQ_ERR_SHAPE, "head_dim %d is not a multiple of 64", head_dim);
+        return fail(FGQ_ERR_UNSUPPORTED, "head_dim %d (64 or 128 supported)", head_dim);
+    }
+    if (out_dtype != FGQ_DTYPE_F32 && out_dtype != FGQ_DTYPE_F16)
+        return fail(FGQ_ERR_DTYPE, "out_dtype %d", out_dtype);
+    if (!std::isfinite(softmax_scale)) return fail(FGQ_ERR_INVALID_ARG, "softmax_scale is not finite");
+    if (batch > 65535 || heads > 65535) return fail(FGQ_ERR_SHAPE, "batch and heads must be <= 65535");
+    if ((int64_t)batch * seq * heads * head_dim > ((int64_t)1 << 40))
+        return fail(FGQ_ERR_SHAPE, "q/k/v larger than 2^40 elements");
+    if (batch == 0 || seq == 0 || heads == 0) return FGQ_OK;
+    if (!q_f16 || !k_f16 || !v_f16 || !out) return fail(FGQ_ERR_INVALID_ARG, "NULL array");
+    if (!aligned16(q_f16) || !aligned16(k_f16) || !aligned16(v_f16) || !aligned16(out))
+        return fail(FGQ_ERR_ALIGN, "q/k/v/out must be 16-byte aligned");
+    const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt((float)head_dim);
+    return launch_prefill_attn(q_f16, k_f16, v_f16, batch, seq, heads, head_dim, scale, out, out_dtype,
+                               static_cast<hipStream_t>(stream));
 }
 
 size_t fgq_pack_weight_meta_words(int64_t K, int64_t N) {

@@ -1,0 +1,273 @@
+// Prefill attention over the prompt's fp16 q, k, v (before the prompt's K
+// and V are compressed into the cache by one bulk append).
+//
+// What is computed: the prefill step runs every prompt token at once and
+// leaves each layer's KV cache behind (paper-graph-ui FlexGen summary,
+// section 3.4, token 0 of the Figure-2 grid; FlexGen review on
+// blog.gzher.com, section 1).  For a decoder-only model each token attends to
+// itself and the tokens before it: per (sequence b, head h, token i)
+//   o_i = sum_{j<=i} softmax_j(scale * q_i . k_j) v_j
+// with q, k, v, o token-major [batch][seq][heads*head_dim].
+//
+// Design (MFMA-bound: 4*D flops per (i, j) pair, ~2 bytes per pair of HBM):
+//  * a workgroup of 8 waves takes 256 query rows of one (b, h), a wave 32
+//    (two 16-row MFMA tiles, so every K and V fragment read from LDS feeds
+//    two MFMAs);
+//    key blocks of 64 are staged in LDS for the 8 waves: K row-major, V
+//    transposed (d-major), the next block's global loads in flight while the
+//    current one is multiplied;
+//  * scores are formed transposed, S^T = K Q^T, on v_mfma_f32_16x16x32_f16
+//    (A = K rows from LDS, B = the wave's Q fragments held in registers), so
+//    a lane's accumulators all belong to one query: the running max, the
+//    rescale of the output and the exponentials stay in the lane, with two
+//    cross-lane steps for the row max and one pair at the end for the sum;
+//  * P.V is formed transposed too, O^T = V^T P^T, with P^T taken straight
+//    from the score accumulators: the 32 k-slots of an MFMA are mapped to
+//    keys in the order the accumulators hold them, and the V^T rows are read
+//    from LDS in the same order (two 8-byte reads per fragment);
+//  * online softmax in the log2 domain (exp2 on the transcendental unit);
+//    the output is rescaled only when some lane's running max moved; blocks
+//    wholly above a wave's diagonal are skipped, blocks that reach it mask
+//    j > i.
+#include "common.h"
+
+namespace fgq {
+namespace {
+
+constexpr float kPfLog2e = 1.4426950408889634f;
+constexpr int kPfWaveRows = 32;              // query rows per wave (two 16-row MFMA tiles)
+constexpr int kPfWaves = 8;                  // waves per workgroup
+constexpr int kPfThreads = 64 * kPfWaves;
+constexpr int kPfRows = kPfWaves * kPfWaveRows;  // query rows per workgroup
+constexpr int kPfKeys = 64;   // keys per block
+
+// Global loads of key block kb (K rows by 16-byte column chunks, coalesced
+// along each row; V one key per lane so that its transposed LDS writes hit
+// consecutive halves) into registers, rows past the prompt clamped to its
+// last token.
+constexpr int pf_loads(int D) { return kPfKeys * D / 8 / kPfThreads; }   // 16-byte loads per thread per tile
+
+template <int D>
+__device__ __forceinline__ void pf_load_tile(const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
+                                             size_t base, size_t rs, int S, int kb, int tid,
+                                             u32x4 (&kr)[pf_loads(D)], u32x4 (&vr)[pf_loads(D)]) {
+    constexpr int KCH = D / 8;                     // 16-byte chunks per row
+#pragma unroll
+    for (int p = 0; p < pf_loads(D); ++p) {
+        const int idx = p * kPfThreads + tid;
+        const int row = idx / KCH, ch = idx % KCH;
+        int j = kb * kPfKeys + row;
+        j = j < S ? j : S - 1;
+        kr[p] = *reinterpret_cast<const u32x4 *>(k + base + (size_t)j * rs + 8 * ch);
+        const int key = tid & 63, vch = (tid >> 6) + kPfWaves * p;
+        int jv = kb * kPfKeys + key;
+        jv = jv < S ? jv : S - 1;
+        vr[p] = *reinterpret_cast<const u32x4 *>(v + base + (size_t)jv * rs + 8 * vch);
+    }
+}
+
+// The registers of pf_load_tile into LDS: K row-major (row stride KS
+// halves), V transposed (d-major, row stride VS halves).
+template <int D, int KS, int VS>
+__device__ __forceinline__ void pf_store_tile(uint16_t *ks, uint16_t *vt, int tid, const u32x4 (&kr)[pf_loads(D)],
+                                              const u32x4 (&vr)[pf_loads(D)]) {
+    constexpr int KCH = D / 8;
+#pragma unroll
+    for (int p = 0; p < pf_loads(D); ++p) {
+        const int idx = p * kPfThreads + tid;
+        const int row = idx / KCH, ch = idx % KCH;
+        *reinterpret_cast<u32x4 *>(ks + row * KS + 8 * ch) = kr[p];
+        const int key = tid & 63, vch = (tid >> 6) + kPfWaves * p;
+        uint16_t *col = vt + 8 * vch * VS + key;
+        col[0 * VS] = (uint16_t)(vr[p][0] & 0xffffu);
+        col[1 * VS] = (uint16_t)(vr[p][0] >> 16);
+        col[2 * VS] = (uint16_t)(vr[p][1] & 0xffffu);
+        col[3 * VS] = (uint16_t)(vr[p][1] >> 16);
+        col[4 * VS] = (uint16_t)(vr[p][2] & 0xffffu);
+        col[5 * VS] = (uint16_t)(vr[p][2] >> 16);
+        col[6 * VS] = (uint16_t)(vr[p][3] & 0xffffu);
+        col[7 * VS] = (uint16_t)(vr[p][3] >> 16);
+    }
+}
+
+template <int D>
+__global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2))) void prefill_attn_kernel(const uint16_t *__restrict__ q,
+                                                           const uint16_t *__restrict__ k,
+                                                           const uint16_t *__restrict__ v, int S, int H,
+                                                           float sl2, void *__restrict__ out, int out_f16) {
+    constexpr int KS = D + 8;            // K row stride in halves (16-byte pad)
+    constexpr int VS = kPfKeys + 4;      // V^T row stride in halves (8-byte pad)
+    constexpr int NP = pf_loads(D);      // 16-byte global loads per thread per tile (K and V each)
+    constexpr int KSTEP = D / 32;        // MFMA k-steps over d
+    constexpr int NDT = D / 16;          // output d-tiles
+    constexpr int QT = kPfWaveRows / 16; // query tiles per wave
+    __shared__ __attribute__((aligned(16))) uint16_t ks[kPfKeys * KS];
+    __shared__ __attribute__((aligned(16))) uint16_t vt[D * VS];
+
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int g = lane >> 4, c = lane & 15;
+    const int nqb = gridDim.x;
+    const int qb = nqb - 1 - (int)blockIdx.x;      // the longest rows first
+    const int h = blockIdx.y, b = blockIdx.z;
+    const size_t rs = (size_t)H * D;               // token stride in halves
+    const size_t base = (size_t)b * S * rs + (size_t)h * D;
+
+    // ---- the wave's Q fragments (B operands): query tile n holds query
+    // q0 + 16n + c, d = 32*s + 8*g + 0..7
+    const int q0 = qb * kPfRows + wv * kPfWaveRows;
+    int qi[QT];
+    f16x8 qf[QT][KSTEP];
+#pragma unroll
+    for (int n = 0; n < QT; ++n) {
+        qi[n] = q0 + 16 * n + c;
+        const int qic = qi[n] < S ? qi[n] : S - 1;
+#pragma unroll
+        for (int s = 0; s < KSTEP; ++s)
+            qf[n][s] = *reinterpret_cast<const f16x8 *>(q + base + (size_t)qic * rs + 32 * s + 8 * g);
+    }
+
+    u32x4 kr[NP], vr[NP];
+    f32x4 o[NDT][QT];
+#pragma unroll
+    for (int t = 0; t < NDT; ++t)
+#pragma unroll
+        for (int n = 0; n < QT; ++n) o[t][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m_run[QT], l_run[QT];
+#pragma unroll
+    for (int n = 0; n < QT; ++n) {
+        m_run[n] = -INFINITY;
+        l_run[n] = 0.f;
+    }
+
+    // key blocks holding a key <= the workgroup's last query (and < S)
+    const int q_last = min(qb * kPfRows + kPfRows, S) - 1;
+    const int kb_last = q_last / kPfKeys;
+    const int wave_q_last = q0 + kPfWaveRows - 1;
+    pf_load_tile<D>(k, v, base, rs, S, 0, tid, kr, vr);
+    for (int kb = 0; kb <= kb_last; ++kb) {
+        __syncthreads();                           // every wave is done with the previous tile
+        pf_store_tile<D, KS, VS>(ks, vt, tid, kr, vr);
+        __syncthreads();
+        if (kb < kb_last) pf_load_tile<D>(k, v, base, rs, S, kb + 1, tid, kr, vr);   // in flight during the MFMAs
+        if (kb * kPfKeys > wave_q_last) continue;  // every key of the block is past this wave's queries
+
+        // ---- S^T = K Q^T: st[t][n] holds keys 16t + 4g + r (r = 0..3) of query tile n
+        f32x4 st[4][QT];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+#pragma unroll
+            for (int n = 0; n < QT; ++n) st[t][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < KSTEP; ++s) {
+                const f16x8 a = *reinterpret_cast<const f16x8 *>(ks + (16 * t + c) * KS + 32 * s + 8 * g);
+#pragma unroll
+                for (int n = 0; n < QT; ++n)
+                    st[t][n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, qf[n][s], st[t][n], 0, 0, 0);
+            }
+        }
+        // ---- causal mask (only blocks that reach past the wave's first query
+        // need it), running max on the raw scores (the scale is positive);
+        // the output is rescaled only when some lane's max moved
+        if ((kb + 1) * kPfKeys - 1 > q0) {
+#pragma unroll
+            for (int n = 0; n < QT; ++n)
+#pragma unroll
+                for (int t = 0; t < 4; ++t)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        if (kb * kPfKeys + 16 * t + 4 * g + r > qi[n]) st[t][n][r] = -INFINITY;
+        }
+        float corr[QT], msc[QT];
+        bool moved = false;
+#pragma unroll
+        for (int n = 0; n < QT; ++n) {
+            float mb = -INFINITY;
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+                mb = fmaxf(mb, fmaxf(fmaxf(st[t][n][0], st[t][n][1]), fmaxf(st[t][n][2], st[t][n][3])));
+            mb = fmaxf(mb, __shfl_xor(mb, 16, 64));
+            mb = fmaxf(mb, __shfl_xor(mb, 32, 64));
+            const float m_new = fmaxf(m_run[n], mb);
+            corr[n] = __builtin_amdgcn_exp2f((m_run[n] - m_new) * sl2);
+            moved |= m_new != m_run[n];
+            m_run[n] = m_new;
+            msc[n] = m_new * sl2;
+            l_run[n] *= corr[n];
+        }
+        if (__ballot(moved)) {
+#pragma unroll
+            for (int t = 0; t < NDT; ++t)
+#pragma unroll
+                for (int n = 0; n < QT; ++n) o[t][n] *= corr[n];
+        }
+        // ---- P^T fragments, p = 2^(s*scale*log2e - m*scale*log2e): k-slot
+        // (g, e) of k-step kk is key 32kk + 4g + e (e < 4) or 32kk + 16 + 4g +
+        // e - 4 (e >= 4), as the accumulators hold them
+        f16x8 pb[QT][2];
+#pragma unroll
+        for (int n = 0; n < QT; ++n)
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(st[2 * kk + (e >> 2)][n][e & 3], sl2, -msc[n]));
+                    l_run[n] += pv;
+                    pb[n][kk][e] = (_Float16)pv;
+                }
+        // ---- O^T += V^T P^T: row d = 16dt + c of V^T, keys in the same k-slot order
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+            for (int t = 0; t < NDT; ++t) {
+                const uint16_t *vrow = vt + (16 * t + c) * VS + 32 * kk + 4 * g;
+                const uint2 lo = *reinterpret_cast<const uint2 *>(vrow);
+                const uint2 hi = *reinterpret_cast<const uint2 *>(vrow + 16);
+                const u32x4 a4 = {lo.x, lo.y, hi.x, hi.y};
+                const f16x8 a = __builtin_bit_cast(f16x8, a4);
+#pragma unroll
+                for (int n = 0; n < QT; ++n)
+                    o[t][n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, pb[n][kk], o[t][n], 0, 0, 0);
+            }
+    }
+
+    // ---- normalise and store: lane holds d = 16dt + 4g + r of query qi[n]
+#pragma unroll
+    for (int n = 0; n < QT; ++n) {
+        float l = l_run[n];
+        l += __shfl_xor(l, 16, 64);
+        l += __shfl_xor(l, 32, 64);
+        if (qi[n] >= S) continue;
+        const float inv = 1.0f / l;
+        const size_t ob = base + (size_t)qi[n] * rs + 4 * g;
+#pragma unroll
+        for (int t = 0; t < NDT; ++t) {
+            const f32x4 val = o[t][n] * inv;
+            if (out_f16) {
+                _Float16 *op = static_cast<_Float16 *>(out) + ob + 16 * t;
+                op[0] = (_Float16)val[0]; op[1] = (_Float16)val[1]; op[2] = (_Float16)val[2]; op[3] = (_Float16)val[3];
+            } else {
+                *reinterpret_cast<f32x4 *>(static_cast<float *>(out) + ob + 16 * t) = val;
+            }
+        }
+    }
+}
+
+}  // namespace
+
+fgq_status launch_prefill_attn(const void *q, const void *k, const void *v, int32_t batch, int32_t seq,
+                               int32_t heads, int32_t head_dim, float scale, void *out, int32_t out_dtype,
+                               hipStream_t stream) {
+    if (batch == 0 || seq == 0 || heads == 0) return FGQ_OK;
+    const dim3 grid((unsigned)((seq + kPfRows - 1) / kPfRows), (unsigned)heads, (unsigned)batch);
+    const float sl2 = scale * kPfLog2e;
+    const int f16 = out_dtype == FGQ_DTYPE_F16;
+    const uint16_t *qh = static_cast<const uint16_t *>(q), *kh = static_cast<const uint16_t *>(k),
+                   *vh = static_cast<const uint16_t *>(v);
+    if (head_dim == 128)
+        prefill_attn_kernel<128><<<grid, dim3(kPfThreads), 0, stream>>>(qh, kh, vh, seq, heads, sl2, out, f16);
+    else
+        prefill_attn_kernel<64><<<grid, dim3(kPfThreads), 0, stream>>>(qh, kh, vh, seq, heads, sl2, out, f16);
+    return check_launch("prefill_attn_kernel");
+}
+
+}  // namespace fgq

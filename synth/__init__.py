@@ -37,6 +37,7 @@ T_GEMM_X = 6      # + weight index
 T_WEIGHT = 20     # + weight index
 T_OUTLIER = 40
 T_CONST_MASK = 41
+T_PROMPT_Q = 42
 
 
 def build(force: bool = True) -> str:
@@ -238,6 +239,17 @@ def step_q(w: Workload, t: int, layer: int = 0) -> np.ndarray:
     """Query of decode step t: fp16 [batch][hidden], N(0, 1)."""
     key = stream_key(w.cid, T_STEP_Q, layer, t)
     return to_f16(normal(key, w.batch * w.hidden)).reshape(w.batch, w.hidden)
+
+
+def prompt_q(w: Workload, layer: int = 0, b0: int = 0, nb: Optional[int] = None) -> np.ndarray:
+    """Queries of the prompt tokens (prefill): fp16 [nb][prompt][hidden], N(0, 1)."""
+    nb = w.batch - b0 if nb is None else nb
+    key = stream_key(w.cid, T_PROMPT_Q, layer)
+    n = w.prompt * w.hidden
+    x = np.empty((nb, w.prompt, w.hidden), np.float32)
+    for i in range(nb):
+        x[i] = normal(key, n, 1.0, (b0 + i) * n).reshape(w.prompt, w.hidden)
+    return to_f16(x)
 
 
 def weight(w: Workload, idx: int, layer: int = 0, rows: Optional[Tuple[int, int]] = None) -> np.ndarray:

@@ -127,6 +127,19 @@ def test_topk_attention_validation(lib):
     assert _status(lambda: t(_kv(batch=0), 0, 4, 2, 0.0, 0, 0, None, 0)) == fgq.FGQ_OK
 
 
+def test_prefill_attention_validation(lib):
+    p = fgq.fgq_prefill_attn_f16
+    assert _status(lambda: p(GOOD, GOOD, GOOD, 2, 16, 2, 96, 0.0, GOOD, 0, 0)) == fgq.FGQ_ERR_SHAPE
+    assert _status(lambda: p(GOOD, GOOD, GOOD, 2, 16, 2, 256, 0.0, GOOD, 0, 0)) == fgq.FGQ_ERR_UNSUPPORTED
+    assert _status(lambda: p(GOOD, GOOD, GOOD, -1, 16, 2, 128, 0.0, GOOD, 0, 0)) == fgq.FGQ_ERR_INVALID_ARG
+    assert _status(lambda: p(GOOD, GOOD, GOOD, 2, 16, 2, 128, 0.0, GOOD, 5, 0)) == fgq.FGQ_ERR_DTYPE
+    assert _status(lambda: p(GOOD, GOOD, GOOD, 2, 16, 2, 128, float("nan"), GOOD, 0, 0)) == fgq.FGQ_ERR_INVALID_ARG
+    assert _status(lambda: p(GOOD, GOOD, GOOD, 70000, 16, 2, 128, 0.0, GOOD, 0, 0)) == fgq.FGQ_ERR_SHAPE
+    assert _status(lambda: p(GOOD, BAD, GOOD, 2, 16, 2, 128, 0.0, GOOD, 0, 0)) == fgq.FGQ_ERR_ALIGN
+    assert _status(lambda: p(GOOD, GOOD, 0, 2, 16, 2, 128, 0.0, GOOD, 0, 0)) == fgq.FGQ_ERR_INVALID_ARG
+    assert _status(lambda: p(0, 0, 0, 2, 0, 2, 128, 0.0, 0, 0, 0)) == fgq.FGQ_OK     # empty prompt
+
+
 def test_gemm_validation_and_workspace(lib):
     gm = fgq.fgq_dequant_gemm
     assert _status(lambda: gm(GOOD, 4, 1, 48, 64, GOOD, GOOD, GOOD, 0, 0, 0, 0)) == fgq.FGQ_ERR_SHAPE

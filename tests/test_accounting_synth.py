@@ -62,6 +62,13 @@ def test_topk_attention_bytes():
     assert acc.topk_attention_bytes(B, h, L, 54) == 0.5625 * B * h * (L + 54) + B * h * 6
 
 
+def test_prefill_attention_flops():
+    """4*h flops per (query, key) pair, s(s+1)/2 causal pairs per sequence:
+    one token is one pair; OPT-175B's prompt of 512 is 131328 pairs."""
+    assert acc.prefill_attention_flops(1, 128, 1) == 4 * 128
+    assert acc.prefill_attention_flops(2, 12288, 512) == 2 * 4 * 12288 * 131328
+
+
 def test_philox_known_answers():
     """Known-answer vectors published with the Random123 library for
     Philox4x32-10 (zero, all-ones and pi-digit counters/keys)."""
@@ -89,6 +96,16 @@ def test_prompt_windows_match_full_tensor():
     a = synth.prompt_kv(w5, "k", b0=3, nb=1, t0=100, nt=8)
     b = synth.prompt_kv(w5, "k", b0=3, nb=1, t0=96, nt=16)
     assert np.array_equal(a, b[:, 4:12])
+
+
+def test_prompt_query_windows_and_distribution():
+    w = synth.WORKLOADS["tiny"]
+    full = synth.prompt_q(w)
+    assert full.shape == (w.batch, w.prompt, w.hidden) and full.dtype == np.float16
+    assert np.array_equal(synth.prompt_q(w, b0=1, nb=2), full[1:3])
+    x = full.astype(np.float64)
+    assert abs(x.mean()) < 0.02 and abs(x.std() - 1.0) < 0.02
+    assert not np.array_equal(full, synth.prompt_kv(w, "k"))
 
 
 def test_streams_are_distinct_and_deterministic():
