@@ -11,8 +11,8 @@
 // for bit.
 //
 // Mapping: one group per 8 consecutive lanes, each lane owning 8 elements
-// (one 16-byte load).  The group's min and max are exchanged with DPP-free
-// xor shuffles inside the 8-lane segment; each lane then writes one 32-bit
+// (one 16-byte load).  The group's min and max are combined with DPP lane
+// moves inside the 8-lane segment; each lane then writes one 32-bit
 // word of codes (8 nibbles) and the segment's first lane writes the meta
 // word.  The division is the correctly rounded one (HIP default).
 #include "common.h"
@@ -25,8 +25,13 @@ struct GroupOut {
     uint32_t meta;    // valid in every lane of the segment
 };
 
+template <int CTRL>
+__device__ __forceinline__ float q_dpp(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+
 // x8: the lane's 8 fp16 values (as raw halves). All 8 lanes of the segment
-// must call this together (shuffles).
+// must call this together (lane exchanges).
 __device__ __forceinline__ GroupOut quantize8(const uint4 raw) {
 #pragma clang fp contract(off)
     float x[8];
@@ -42,11 +47,15 @@ __device__ __forceinline__ GroupOut quantize8(const uint4 raw) {
         a = fminf(a, x[i]);
         b = fmaxf(b, x[i]);
     }
-#pragma unroll
-    for (int s = 1; s < 8; s <<= 1) {
-        a = fminf(a, __shfl_xor(a, s, 64));
-        b = fmaxf(b, __shfl_xor(b, s, 64));
-    }
+    // min and max over the 8 lanes of the segment with DPP lane moves (no LDS
+    // round trip): swap neighbours, swap pairs, then mirror the half-row
+    // (lane i <-> 7 - i) to combine the two quads.  Exact in any order.
+    a = fminf(a, q_dpp<0xB1>(a));
+    b = fmaxf(b, q_dpp<0xB1>(b));
+    a = fminf(a, q_dpp<0x4E>(a));
+    b = fmaxf(b, q_dpp<0x4E>(b));
+    a = fminf(a, q_dpp<0x141>(a));
+    b = fmaxf(b, q_dpp<0x141>(b));
     a = a + 0.0f;   // -0 -> +0
     b = b + 0.0f;
     GroupOut out;
@@ -57,14 +66,26 @@ __device__ __forceinline__ GroupOut quantize8(const uint4 raw) {
         return out;
     }
     const float d = __fsub_rn(b, a);
+    // The code is rint(RN(RN(t / d) * 15)), t = x - a.  A cheaper estimate
+    // t * RN(15 * rcp(d)) is within 2^-16 of that value (both are within a
+    // few ulp of the exact 15t/d <= 15), so wherever the estimate is at least
+    // 2^-15 away from a rounding boundary k + 1/2 it rounds to the same
+    // integer; only elements closer than that (exact ties among them) take
+    // the correctly rounded division.
+    const float r15 = __fmul_rn(15.0f, __builtin_amdgcn_rcpf(d));
     uint32_t packed = 0u;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         const float t = __fsub_rn(x[i], a);
-        const float u = __fdiv_rn(t, d);
-        const float v = __fmul_rn(u, 15.0f);
-        float r = rintf(v);                 // v_rndne_f32: ties to even
-        r = fminf(fmaxf(r, 0.0f), 15.0f);
+        const float va = __fmul_rn(t, r15);
+        float r = rintf(va);
+        // va - r is exact (|va - r| <= 1/2); near a boundary it is close to +-1/2
+        if (__builtin_expect(fabsf(__fsub_rn(va, r)) > 0.5f - 3.0517578125e-05f, 0)) {
+            const float u = __fdiv_rn(t, d);
+            const float v = __fmul_rn(u, 15.0f);
+            r = rintf(v);                   // v_rndne_f32: ties to even
+        }
+        // 0 <= t <= d, so 0 <= r <= 15 on both paths: no clamp is needed
         packed |= ((uint32_t)r) << (4 * i);
     }
     const float step = __fdiv_rn(d, 15.0f);
@@ -93,7 +114,10 @@ __global__ __launch_bounds__(256) void quantize_g64_kernel(const uint16_t *__res
 }
 
 // One group = 64 hidden elements of one token's K or V row of one head.
-// gid enumerates (which in {K,V}, b, i, head, group-in-head).
+// gid enumerates (which in {K,V}, b, head, i, group-in-head), the group
+// fastest and then the token: the groups of consecutive tokens of one head
+// are consecutive in the head-major cache, so a wave's code and meta writes
+// are contiguous runs (its reads are 128-byte slices of token rows).
 __global__ __launch_bounds__(256) void kv_append_kernel(const uint16_t *__restrict__ k_new,
                                                         const uint16_t *__restrict__ v_new,
                                                         fgq_kv_cache kv, int32_t pos, int32_t n_new) {
@@ -106,10 +130,10 @@ __global__ __launch_bounds__(256) void kv_append_kernel(const uint16_t *__restri
     int64_t rem = valid ? gid - which * per_tensor : 0;
     const int gi = (int)(rem % gph);
     rem /= gph;
-    const int hd = (int)(rem % kv.heads);
-    rem /= kv.heads;
     const int i = (int)(rem % n_new);
-    const int64_t b = rem / n_new;
+    rem /= n_new;
+    const int hd = (int)(rem % kv.heads);
+    const int64_t b = rem / kv.heads;
     const int64_t hidden = (int64_t)kv.heads * kv.head_dim;
     const uint16_t *src = which ? v_new : k_new;
     uint4 raw = make_uint4(0u, 0u, 0u, 0u);
