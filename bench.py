@@ -53,6 +53,8 @@ def parse():
     ap.add_argument("--rotate", type=int, default=0,
                     help="layer instances cycled through (0: at least 3, and enough to exceed the 256 MB "
                          "last-level cache three times over)")
+    ap.add_argument("--no-stream", action="store_true",
+                    help="skip the weight-streaming measurement (packed weights from pinned host memory)")
     ap.add_argument("--no-graph", action="store_true",
                     help="time the eager launches only (default: the step is also replayed as HIP graphs, "
                          "and that pass gives value and ms_per_step)")
@@ -375,6 +377,74 @@ def algorithmic_bytes_per_launch(kernel: str, w, n_steps: int = 0, warmup: int =
     return float(np.mean([acc.attention_bytes(w.batch, w.hidden, w.kv_len(t)) for t in ts]))
 
 
+def weight_streaming(torch, fgq, w, layers, plan, steps_in, attn_out, ys, attn_ws, attn_ws_b, gemm_ws, gemm_ws_b,
+                     stream, args):
+    """The layer step with the layer's packed weights arriving from pinned host
+    memory each step (the offloading setting compression was made for): two
+    device buffers, the next step's weights copied on a second stream while
+    this step computes; the KV cache stays in HBM.  Also times the plain
+    host-to-device copy of the same bytes and of the fp16 weights they replace."""
+    B = w.batch
+    host = [(pc.cpu().pin_memory(), pm.cpu().pin_memory()) for pc, pm in layers[0].packed]
+    nbytes = sum(a.numel() * 4 + b.numel() * 4 for a, b in host)
+    bufs = [[(torch.empty_like(pc), torch.empty_like(pm)) for pc, pm in layers[0].packed] for _ in range(2)]
+    cstream = torch.cuda.Stream()
+    ch = stream.cuda_stream
+    copied = [torch.cuda.Event() for _ in range(2)]
+    freed = [torch.cuda.Event() for _ in range(2)]
+    L = layers[0]
+    n = 8
+
+    def copy(i):
+        k = i % 2
+        with torch.cuda.stream(cstream):
+            cstream.wait_event(freed[k])
+            for (hc, hm), (dc, dm) in zip(host, bufs[k]):
+                dc.copy_(hc, non_blocking=True)
+                dm.copy_(hm, non_blocking=True)
+            copied[k].record(cstream)
+
+    def step(i):
+        k = i % 2
+        t = i % w.steps + 1
+        d = steps_in[t - 1]
+        stream.wait_event(copied[k])
+        fgq.fgq_kv_append(L.kv, d["k"], d["v"], w.prompt + t - 1, 1, ch)
+        fgq.fgq_decode_attn_q4kv(L.kv, d["q"], w.prompt + t, 0.0, attn_out, fgq.FGQ_DTYPE_F32, attn_ws, attn_ws_b, ch)
+        for wi, (_, K, N, _) in enumerate(plan):
+            dc, dm = bufs[k][wi]
+            fgq.fgq_dequant_gemm(d["x"][wi], w.g, w.m, K, N, dc, dm, ys[wi], fgq.FGQ_DTYPE_F32, gemm_ws, gemm_ws_b, ch)
+        freed[k].record(stream)
+
+    for k in range(2):
+        freed[k].record(stream)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    copy(0)
+    e0.record(stream)
+    for i in range(n):
+        if i + 1 < n:
+            copy(i + 1)
+        step(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / n
+    # the plain copy of the packed bytes, and of fp16 weights of the same matrices
+    f16 = torch.empty(sum(K * N for _, K, N, _ in plan), dtype=torch.float16).pin_memory()
+    dev16 = torch.empty_like(f16, device="cuda")
+    g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    g0.record(stream)
+    dev16.copy_(f16, non_blocking=True)
+    g1.record(stream)
+    torch.cuda.synchronize()
+    f16_ms = g0.elapsed_time(g1)
+    del dev16, f16, bufs, host
+    return {"steps": n, "packed_bytes_per_step": nbytes, "ms_per_step": ms,
+            "tokens_per_s_per_layer": B / (ms * 1e-3), "h2d_GB_per_s": nbytes / (ms * 1e-3) / 1e9,
+            "fp16_weights_copy_ms": f16_ms, "fp16_over_packed_bytes": 2.0 * sum(K * N for _, K, N, _ in plan) / nbytes}
+
+
 def main():
     args = parse()
     if args.summarize_trace:
@@ -635,6 +705,10 @@ def main():
     if tk_tr is not None and w.kv_len(w.steps) <= 2048:
         kernels["topk_attention"]["traffic_bytes_per_launch"] = tk_tr["bytes_per_launch"]
         kernels["topk_attention"]["traffic_vs_algorithmic"] = tk_tr["ratio"]
+
+    if w.weights and not args.no_stream:
+        kernels["weight_streaming"] = weight_streaming(torch, fgq, w, layers, plan, steps_in, attn_out, ys, attn_ws,
+                                                       attn_ws_b, gemm_ws, gemm_ws_b, stream, args)
 
     if w.weights and gemm_ms >= op_ms["attention"]:
         kname = "dq_gemm_kernel"
