@@ -57,9 +57,10 @@ def _load():
         lib.oracle_dequant_gemm.argtypes = [vp, i32, i32, i64, i64, vp, vp, vp]
         lib.oracle_decode_attn_topk.argtypes = [vp, i32, i32, i32, i32, vp, vp, vp, vp, i32, i32, dbl, vp, vp]
         lib.oracle_prefill_attn.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32, dbl, vp]
+        lib.oracle_decode_attn_gqa.argtypes = [vp, i32, i32, i32, i32, i32, vp, vp, vp, vp, i32, dbl, vp]
         for f in (lib.oracle_quantize_g64, lib.oracle_dequant_g64, lib.oracle_kv_append,
                   lib.oracle_decode_attn, lib.oracle_dequant_gemm, lib.oracle_decode_attn_topk,
-                  lib.oracle_prefill_attn):
+                  lib.oracle_prefill_attn, lib.oracle_decode_attn_gqa):
             f.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -136,6 +137,22 @@ def decode_attn(kv: KVCache, q: np.ndarray, kv_len: int, scale: float = 0.0) -> 
                                       kv.k_codes.ctypes.data, kv.k_meta.ctypes.data,
                                       kv.v_codes.ctypes.data, kv.v_meta.ctypes.data,
                                       kv_len, float(scale), out.ctypes.data), "decode_attn")
+    return out
+
+
+def decode_attn_gqa(kv: KVCache, q: np.ndarray, q_heads: int, kv_len: int, scale: float = 0.0) -> np.ndarray:
+    """Grouped-query decode attention: the cache holds kv.heads K/V heads, q
+    fp16 [B][q_heads*D] -> fp32 [B][q_heads*D]; query head hq reads cache head
+    hq // (q_heads // kv.heads).  scale <= 0 means 1/sqrt(D)."""
+    q = _c(q, np.float16)
+    if scale <= 0.0:
+        scale = 1.0 / np.sqrt(kv.head_dim)
+    assert q.shape == (kv.batch, q_heads * kv.head_dim)
+    out = np.zeros((kv.batch, q_heads * kv.head_dim), np.float32)
+    _check(_load().oracle_decode_attn_gqa(q.ctypes.data, kv.batch, q_heads, kv.heads, kv.head_dim, kv.cap,
+                                          kv.k_codes.ctypes.data, kv.k_meta.ctypes.data,
+                                          kv.v_codes.ctypes.data, kv.v_meta.ctypes.data,
+                                          kv_len, float(scale), out.ctypes.data), "decode_attn_gqa")
     return out
 
 

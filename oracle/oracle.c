@@ -419,3 +419,64 @@ int oracle_dequant_gemm(const uint16_t *x, int32_t g, int32_t m, int64_t K, int6
     }
     return ORACLE_OK;
 }
+
+/* Decode attention with grouped K/V heads (GQA) or one shared K/V head (MQA)
+ * over the compressed cache (vTensor page on papercache.org, background
+ * section "GQA and MQA optimisation": with MQA every query head shares one
+ * key head and one value head; with GQA the query heads are divided into
+ * groups and each group shares one key head and one value head; section
+ * "Roofline comparison" and Figure 3: fewer shared heads raise the
+ * arithmetic intensity of decode attention).  The pages do not say which
+ * query heads form a group; the reading taken is consecutive heads:
+ * with R = q_heads / kv_heads, query head hq reads cache head kh = hq / R.
+ * q fp16 [batch][q_heads*head_dim]; the cache holds kv_heads heads; out fp32
+ * [batch][q_heads*head_dim].  Per (b, hq):
+ *   s_j = scale * sum_d q_{hq,d} * K^_{kh,j,d}        (fp64, d ascending)
+ *   o_d = sum_j exp(s_j - max s) * V^_{kh,j,d} / sum_j exp(s_j - max s)
+ * kv_heads == q_heads is plain multi-head attention (R = 1). */
+int oracle_decode_attn_gqa(const uint16_t *q, int32_t batch, int32_t q_heads, int32_t kv_heads,
+                           int32_t head_dim, int32_t cap, const uint8_t *k_codes, const uint32_t *k_meta,
+                           const uint8_t *v_codes, const uint32_t *v_meta, int32_t kv_len, double scale,
+                           float *out) {
+    if (head_dim % 64 != 0 || kv_len < 1 || kv_len > cap || kv_heads < 1 || q_heads < kv_heads ||
+        q_heads % kv_heads != 0)
+        return ORACLE_ERR_SHAPE;
+    const int32_t R = q_heads / kv_heads;
+    const int64_t hq_stride = (int64_t)q_heads * head_dim;
+    const int64_t gph = head_dim / 64;
+    #pragma omp parallel for collapse(2) schedule(static)
+    for (int32_t b = 0; b < batch; ++b)
+        for (int32_t hq = 0; hq < q_heads; ++hq) {
+            const int32_t kh = hq / R;
+            double *s = (double *)malloc(sizeof(double) * (size_t)kv_len);
+            double *o = (double *)calloc((size_t)head_dim, sizeof(double));
+            const uint16_t *qv = q + (int64_t)b * hq_stride + (int64_t)hq * head_dim;
+            const int64_t base = ((int64_t)b * kv_heads + kh) * cap;
+            double mx = -INFINITY;
+            for (int32_t j = 0; j < kv_len; ++j) {
+                const uint8_t *kc = k_codes + (base + j) * (head_dim / 2);
+                const uint32_t *km = k_meta + (base + j) * gph;
+                double acc = 0.0;
+                for (int32_t d = 0; d < head_dim; ++d)
+                    acc += (double)oracle_f16_to_f32(qv[d]) * (double)dequant_one(km[d / 64], code_at(kc, d));
+                s[j] = acc * scale;
+                if (s[j] > mx) mx = s[j];
+            }
+            double den = 0.0;
+            for (int32_t j = 0; j < kv_len; ++j) {
+                s[j] = exp(s[j] - mx);
+                den += s[j];
+            }
+            for (int32_t j = 0; j < kv_len; ++j) {
+                const uint8_t *vc = v_codes + (base + j) * (head_dim / 2);
+                const uint32_t *vm = v_meta + (base + j) * gph;
+                for (int32_t d = 0; d < head_dim; ++d)
+                    o[d] += s[j] * (double)dequant_one(vm[d / 64], code_at(vc, d));
+            }
+            float *ov = out + (int64_t)b * hq_stride + (int64_t)hq * head_dim;
+            for (int32_t d = 0; d < head_dim; ++d) ov[d] = (float)(o[d] / den);
+            free(s);
+            free(o);
+        }
+    return ORACLE_OK;
+}

@@ -137,6 +137,7 @@ class Workload:
     outlier_scale: float = 1.0
     const_group_frac: float = 0.0
     weight_sigma: float = 0.02
+    kv_heads: int = 0                       # K/V heads; 0 means one per query head
 
     @property
     def batch(self) -> int:
@@ -144,7 +145,17 @@ class Workload:
 
     @property
     def hidden(self) -> int:
+        """Query width: heads * head_dim."""
         return self.heads * self.head_dim
+
+    @property
+    def n_kv_heads(self) -> int:
+        return self.kv_heads or self.heads
+
+    @property
+    def kv_hidden(self) -> int:
+        """Width of one token's K (or V) row: kv_heads * head_dim."""
+        return self.n_kv_heads * self.head_dim
 
     @property
     def capacity(self) -> int:
@@ -172,6 +183,12 @@ WORKLOADS = {
     "long-t3": Workload(5, "long-t3", g=32, m=1, heads=96, head_dim=128, prompt=4096, steps=32,
                         weights=(), kv_dist="t3", outlier_channels=8, outlier_scale=20.0,
                         const_group_frac=0.01),
+    # Grouped-query decode attention at the shape of the vTensor page's
+    # decode-kernel evaluation (section "Decoding kernel evaluation", Figure 7:
+    # 16K cached positions, batch up to 32, 32 query heads with 32 down to 1
+    # K/V heads): batch 16, 32 query heads x 128 sharing 8 K/V heads.
+    "gqa": Workload(6, "gqa", g=16, m=1, heads=32, kv_heads=8, head_dim=128, prompt=16384, steps=32,
+                    weights=()),
 }
 
 
@@ -184,7 +201,7 @@ def outlier_channels(w: Workload, layer: int = 0) -> np.ndarray:
     first = 0
     while len(chosen) < w.outlier_channels:
         for u in uniform(key, 64, first):
-            c = int(u * w.hidden)
+            c = int(u * w.kv_hidden)
             if c not in chosen:
                 chosen.append(c)
                 if len(chosen) == w.outlier_channels:
@@ -195,9 +212,9 @@ def outlier_channels(w: Workload, layer: int = 0) -> np.ndarray:
 
 def _kv_rows(w: Workload, tensor: int, layer: int, step: int, ntok_full: int,
              b0: int, nb: int, t0: int, nt: int) -> np.ndarray:
-    """fp16 [nb][nt][hidden]: batch rows b0.., tokens t0.. of a K or V stream
-    whose full layout is [batch][ntok_full][hidden]."""
-    h = w.hidden
+    """fp16 [nb][nt][kv_hidden]: batch rows b0.., tokens t0.. of a K or V stream
+    whose full layout is [batch][ntok_full][kv_hidden]."""
+    h = w.kv_hidden
     key = stream_key(w.cid, tensor, layer, step)
     draw = student_t3 if w.kv_dist == "t3" else normal
     x = np.empty((nb, nt, h), np.float32)
@@ -221,7 +238,7 @@ def _kv_rows(w: Workload, tensor: int, layer: int, step: int, ntok_full: int,
 
 def prompt_kv(w: Workload, which: str, layer: int = 0, b0: int = 0, nb: Optional[int] = None,
               t0: int = 0, nt: Optional[int] = None) -> np.ndarray:
-    """Prompt K (which='k') or V ('v'): fp16 [nb][nt][hidden], token-major;
+    """Prompt K (which='k') or V ('v'): fp16 [nb][nt][kv_hidden], token-major;
     defaults cover every sequence and every prompt token."""
     nb = w.batch - b0 if nb is None else nb
     nt = w.prompt - t0 if nt is None else nt
@@ -230,7 +247,7 @@ def prompt_kv(w: Workload, which: str, layer: int = 0, b0: int = 0, nb: Optional
 
 
 def step_kv(w: Workload, which: str, t: int, layer: int = 0) -> np.ndarray:
-    """K or V of decode step t (1-based): fp16 [batch][1][hidden]."""
+    """K or V of decode step t (1-based): fp16 [batch][1][kv_hidden]."""
     tid = T_STEP_K if which == "k" else T_STEP_V
     return _kv_rows(w, tid, layer, t, 1, 0, w.batch, 0, 1)
 
