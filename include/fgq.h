@@ -146,6 +146,34 @@ fgq_status fgq_decode_attn_q4kv(const fgq_kv_cache *kv, const void *q_f16, int32
                                 void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * fgq_decode_attn_gqa_q4kv - decode attention with grouped K/V heads (GQA) or
+ * one shared K/V head (MQA) over the compressed cache (vTensor page on
+ * papercache.org, background section "GQA and MQA optimisation": the query
+ * heads are divided into groups, each group sharing one key head and one
+ * value head; MQA shares a single one).  The cache holds kv->heads K/V heads;
+ * with R = q_heads / kv->heads, query head hq reads cache head hq / R
+ * (consecutive query heads form a group).  For each (sequence, query head):
+ *   s_j = softmax_scale * sum_d q_{hq,d} * K^_{hq/R,j,d},  j in [0, kv_len)
+ *   o_d = sum_j softmax(s)_j * V^_{hq/R,j,d}
+ *   q    fp16 [batch][q_heads*head_dim];  out [batch][q_heads*head_dim] in out_dtype.
+ *   Requires q_heads a multiple of kv->heads (FGQ_ERR_SHAPE) and
+ *   R <= FGQ_GQA_MAX_GROUP (FGQ_ERR_UNSUPPORTED); R == 1 is
+ *   fgq_decode_attn_q4kv.  softmax_scale <= 0 selects 1/sqrt(head_dim); every
+ *   sequence attends the same kv_len positions; 1 <= kv_len <= capacity.
+ *   ws / ws_bytes: at least fgq_decode_attn_gqa_ws_bytes(...) bytes (may be
+ *   NULL when that is 0): per-split partial softmax states.
+ * Fp16 matrix cores with fp32 accumulation: the codes enter exactly, the
+ * probabilities enter the p.v product as fp16(p * step).  The result depends
+ * on the split plan only through fp32 rounding.
+ */
+#define FGQ_GQA_MAX_GROUP 32
+size_t fgq_decode_attn_gqa_ws_bytes(int32_t batch, int32_t q_heads, int32_t kv_heads, int32_t head_dim,
+                                    int32_t kv_len);
+fgq_status fgq_decode_attn_gqa_q4kv(const fgq_kv_cache *kv, const void *q_f16, int32_t q_heads,
+                                    int32_t kv_len, float softmax_scale, void *out, int32_t out_dtype,
+                                    void *ws, size_t ws_bytes, void *stream);
+
+/*
  * fgq_decode_attn_topk_q4kv - top-K sparse variant of fgq_decode_attn_q4kv:
  * the paper's optional approximation that reads only the top 10% of the value
  * cache (FlexGen review on blog.gzher.com, section 3.4; paper-graph-ui FlexGen

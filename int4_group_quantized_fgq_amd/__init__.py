@@ -66,6 +66,8 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
         "fgq_decode_attn_ws_bytes": ([i32, i32, i32, i32], sz),
         "fgq_decode_attn_q4kv": ([kvp, vp, i32, f32, vp, i32, vp, sz, vp], i32),
         "fgq_decode_attn_topk_q4kv": ([kvp, vp, i32, i32, f32, vp, i32, vp, vp], i32),
+        "fgq_decode_attn_gqa_ws_bytes": ([i32, i32, i32, i32, i32], sz),
+        "fgq_decode_attn_gqa_q4kv": ([kvp, vp, i32, i32, f32, vp, i32, vp, sz, vp], i32),
         "fgq_prefill_attn_f16": ([vp, vp, vp, i32, i32, i32, i32, f32, vp, i32, vp], i32),
         "fgq_pack_weight_meta_words": ([i64, i64], sz),
         "fgq_pack_weight_g64": ([vp, vp, i64, i64, vp, vp, vp], i32),
@@ -146,6 +148,17 @@ def fgq_decode_attn_q4kv(kv: fgq_kv_cache, q, kv_len, softmax_scale, out, out_dt
                          stream=None) -> None:
     _check(load().fgq_decode_attn_q4kv(ctypes.byref(kv), _ptr(q), kv_len, softmax_scale, _ptr(out), out_dtype,
                                        _ptr(ws), ws_bytes, _stream(stream)), "fgq_decode_attn_q4kv")
+
+
+def fgq_decode_attn_gqa_ws_bytes(batch, q_heads, kv_heads, head_dim, kv_len) -> int:
+    return load().fgq_decode_attn_gqa_ws_bytes(batch, q_heads, kv_heads, head_dim, kv_len)
+
+
+def fgq_decode_attn_gqa_q4kv(kv: fgq_kv_cache, q, q_heads, kv_len, softmax_scale, out, out_dtype, ws, ws_bytes,
+                             stream=None) -> None:
+    _check(load().fgq_decode_attn_gqa_q4kv(ctypes.byref(kv), _ptr(q), q_heads, kv_len, softmax_scale, _ptr(out),
+                                           out_dtype, _ptr(ws), ws_bytes, _stream(stream)),
+           "fgq_decode_attn_gqa_q4kv")
 
 
 def fgq_decode_attn_topk_q4kv(kv: fgq_kv_cache, q, kv_len, top_k, softmax_scale, out, out_dtype, sel=None,

@@ -18,6 +18,9 @@ fgq_status launch_pack_weight(const uint8_t *codes, const uint32_t *meta, int64_
 size_t attn_ws_bytes(int32_t batch, int32_t heads, int32_t head_dim, int32_t kv_len);
 fgq_status launch_decode_attn(const fgq_kv_cache *kv, const void *q, int32_t kv_len, float scale, void *out,
                               int32_t out_dtype, void *ws, hipStream_t stream);
+size_t gqa_ws_bytes(int32_t batch, int32_t q_heads, int32_t kv_heads, int32_t head_dim, int32_t kv_len);
+fgq_status launch_decode_attn_gqa(const fgq_kv_cache *kv, const void *q, int32_t q_heads, int32_t kv_len,
+                                  float scale, void *out, int32_t out_dtype, void *ws, hipStream_t stream);
 size_t attn_topk_lds_bytes(int32_t kv_len, int32_t kept);
 fgq_status launch_decode_attn_topk(const fgq_kv_cache *kv, const void *q, int32_t kv_len, int32_t kept,
                                    float scale, void *out, int32_t out_dtype, int32_t *sel, hipStream_t stream);
@@ -137,6 +140,50 @@ fgq_status fgq_decode_attn_q4kv(const fgq_kv_cache *kv, const void *q_f16, int32
     }
     const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt((float)kv->head_dim);
     return launch_decode_attn(kv, q_f16, kv_len, scale, out, out_dtype, ws, static_cast<hipStream_t>(stream));
+}
+
+size_t fgq_decode_attn_gqa_ws_bytes(int32_t batch, int32_t q_heads, int32_t kv_heads, int32_t head_dim,
+                                    int32_t kv_len) {
+    if (batch <= 0 || kv_heads <= 0 || q_heads < kv_heads || q_heads % kv_heads != 0 ||
+        q_heads / kv_heads > FGQ_GQA_MAX_GROUP || (head_dim != 64 && head_dim != 128) || kv_len <= 0)
+        return 0;
+    if (q_heads == kv_heads) return attn_ws_bytes(batch, q_heads, head_dim, kv_len);
+    return gqa_ws_bytes(batch, q_heads, kv_heads, head_dim, kv_len);
+}
+
+fgq_status fgq_decode_attn_gqa_q4kv(const fgq_kv_cache *kv, const void *q_f16, int32_t q_heads, int32_t kv_len,
+                                    float softmax_scale, void *out, int32_t out_dtype, void *ws, size_t ws_bytes,
+                                    void *stream) {
+    g_err[0] = 0;
+    fgq_status s = check_kv(kv);
+    if (s != FGQ_OK) return s;
+    if (q_heads < 0) return fail(FGQ_ERR_INVALID_ARG, "negative q_heads");
+    if (kv->heads == 0 || q_heads < kv->heads || q_heads % kv->heads != 0)
+        return fail(FGQ_ERR_SHAPE, "q_heads %d is not a positive multiple of kv heads %d", q_heads, kv->heads);
+    if (q_heads / kv->heads > FGQ_GQA_MAX_GROUP)
+        return fail(FGQ_ERR_UNSUPPORTED, "%d query heads per K/V head (at most %d)", q_heads / kv->heads,
+                    FGQ_GQA_MAX_GROUP);
+    if (out_dtype != FGQ_DTYPE_F32 && out_dtype != FGQ_DTYPE_F16)
+        return fail(FGQ_ERR_DTYPE, "out_dtype %d", out_dtype);
+    if (kv_len < 1) return fail(FGQ_ERR_SHAPE, "kv_len %d < 1", kv_len);
+    if (kv_len > kv->capacity) return fail(FGQ_ERR_CAPACITY, "kv_len %d > capacity %d", kv_len, kv->capacity);
+    if (!std::isfinite(softmax_scale)) return fail(FGQ_ERR_INVALID_ARG, "softmax_scale is not finite");
+    if ((int64_t)kv->batch * q_heads > INT32_MAX) return fail(FGQ_ERR_SHAPE, "batch * q_heads > 2^31 - 1");
+    if (kv->batch == 0) return FGQ_OK;
+    if (!q_f16 || !out) return fail(FGQ_ERR_INVALID_ARG, "NULL q or out");
+    if (!aligned16(q_f16) || !aligned16(out)) return fail(FGQ_ERR_ALIGN, "q/out must be 16-byte aligned");
+    const bool mha = q_heads == kv->heads;
+    const size_t need = mha ? attn_ws_bytes(kv->batch, kv->heads, kv->head_dim, kv_len)
+                            : gqa_ws_bytes(kv->batch, q_heads, kv->heads, kv->head_dim, kv_len);
+    if (need > 0) {
+        if (!ws || ws_bytes < need)
+            return fail(FGQ_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws ? ws_bytes : (size_t)0, need);
+        if (!aligned16(ws)) return fail(FGQ_ERR_ALIGN, "workspace must be 16-byte aligned");
+    }
+    const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt((float)kv->head_dim);
+    if (mha) return launch_decode_attn(kv, q_f16, kv_len, scale, out, out_dtype, ws, static_cast<hipStream_t>(stream));
+    return launch_decode_attn_gqa(kv, q_f16, q_heads, kv_len, scale, out, out_dtype, ws,
+                                  static_cast<hipStream_t>(stream));
 }
 
 fgq_status fgq_decode_attn_topk_q4kv(const fgq_kv_cache *kv, const void *q_f16, int32_t kv_len, int32_t top_k,

@@ -98,6 +98,19 @@ class DevKV:
         torch.cuda.synchronize()
         return to_host(out).astype(np.float32)
 
+    def attend_gqa(self, q16: np.ndarray, q_heads: int, kv_len: int, scale: float = 0.0, out_f16: bool = False):
+        """Grouped-query attention: q fp16 [B][q_heads*D] over this cache's K/V heads -> fp32 [B][q_heads*D]."""
+        torch = torch_cuda()
+        qd = to_dev(q16)
+        out = torch.empty((self.batch, q_heads * self.head_dim),
+                          dtype=torch.float16 if out_f16 else torch.float32, device="cuda")
+        wsb = fgq.fgq_decode_attn_gqa_ws_bytes(self.batch, q_heads, self.heads, self.head_dim, kv_len)
+        ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device="cuda")
+        fgq.fgq_decode_attn_gqa_q4kv(self.struct, qd, q_heads, kv_len, scale, out,
+                                     fgq.FGQ_DTYPE_F16 if out_f16 else fgq.FGQ_DTYPE_F32, ws, wsb)
+        torch.cuda.synchronize()
+        return to_host(out).astype(np.float32)
+
     def attend_topk(self, q16: np.ndarray, kv_len: int, top_k: int, scale: float = 0.0, out_f16: bool = False,
                     want_sel: bool = True):
         """Top-K sparse attention -> (fp32 [B][H*D], kept positions int32 [B][H][kk] or None)."""

@@ -107,6 +107,36 @@ def test_attention_validation_and_workspace(lib):
     assert fgq.fgq_decode_attn_ws_bytes(0, 96, 128, 544) == 0
 
 
+def test_gqa_attention_validation_and_workspace(lib):
+    a = fgq.fgq_decode_attn_gqa_q4kv
+    kv = _kv(batch=2, heads=2, head_dim=128, cap=16)
+    assert _status(lambda: a(kv, GOOD, 3, 4, 0.0, GOOD, 0, 0, 0, 0)) == fgq.FGQ_ERR_SHAPE      # 3 % 2 != 0
+    assert _status(lambda: a(kv, GOOD, 1, 4, 0.0, GOOD, 0, 0, 0, 0)) == fgq.FGQ_ERR_SHAPE      # fewer than kv heads
+    assert _status(lambda: a(kv, GOOD, -2, 4, 0.0, GOOD, 0, 0, 0, 0)) == fgq.FGQ_ERR_INVALID_ARG
+    assert _status(lambda: a(kv, GOOD, 66, 4, 0.0, GOOD, 0, 0, 0, 0)) == fgq.FGQ_ERR_UNSUPPORTED  # R = 33
+    assert _status(lambda: a(_kv(heads=0), GOOD, 4, 4, 0.0, GOOD, 0, 0, 0, 0)) == fgq.FGQ_ERR_SHAPE
+    assert _status(lambda: a(kv, GOOD, 8, 0, 0.0, GOOD, 0, 0, 0, 0)) == fgq.FGQ_ERR_SHAPE
+    assert _status(lambda: a(kv, GOOD, 8, 17, 0.0, GOOD, 0, 0, 0, 0)) == fgq.FGQ_ERR_CAPACITY
+    assert _status(lambda: a(kv, GOOD, 8, 4, 0.0, GOOD, 3, 0, 0, 0)) == fgq.FGQ_ERR_DTYPE
+    assert _status(lambda: a(kv, GOOD, 8, 4, float("nan"), GOOD, 0, 0, 0, 0)) == fgq.FGQ_ERR_INVALID_ARG
+    assert _status(lambda: a(kv, BAD, 8, 4, 0.0, GOOD, 0, 0, 0, 0)) == fgq.FGQ_ERR_ALIGN
+    assert _status(lambda: a(kv, GOOD, 8, 4, 0.0, 0, 0, 0, 0, 0)) == fgq.FGQ_ERR_INVALID_ARG
+    assert _status(lambda: a(_kv(head_dim=96), GOOD, 8, 4, 0.0, GOOD, 0, 0, 0, 0)) == fgq.FGQ_ERR_SHAPE
+    assert _status(lambda: a(_kv(batch=0), 0, 8, 4, 0.0, 0, 0, 0, 0, 0)) == fgq.FGQ_OK
+    # few sequences and K/V heads over a long context need split states
+    B, Hq, Hkv, D, L = 2, 32, 8, 128, 16384
+    need = fgq.fgq_decode_attn_gqa_ws_bytes(B, Hq, Hkv, D, L)
+    assert need > 0 and need % 16 == 0
+    big = _kv(B, Hkv, D, L)
+    assert _status(lambda: a(big, GOOD, Hq, L, 0.0, GOOD, 0, 0, 0, 0)) == fgq.FGQ_ERR_WORKSPACE
+    assert _status(lambda: a(big, GOOD, Hq, L, 0.0, GOOD, 0, GOOD, need - 16, 0)) == fgq.FGQ_ERR_WORKSPACE
+    assert _status(lambda: a(big, GOOD, Hq, L, 0.0, GOOD, 0, BAD, need, 0)) == fgq.FGQ_ERR_ALIGN
+    # one query head per K/V head is the multi-head call, with its workspace
+    assert fgq.fgq_decode_attn_gqa_ws_bytes(1, 2, 2, 128, 4096) == fgq.fgq_decode_attn_ws_bytes(1, 2, 128, 4096)
+    assert fgq.fgq_decode_attn_gqa_ws_bytes(2, 30, 8, 128, 64) == 0        # not a multiple
+    assert fgq.fgq_decode_attn_gqa_ws_bytes(2, 8 * 33, 8, 128, 64) == 0    # group of 33
+
+
 def test_topk_attention_validation(lib):
     t = fgq.fgq_decode_attn_topk_q4kv
     assert _status(lambda: t(_kv(), GOOD, 0, 1, 0.0, GOOD, 0, None, 0)) == fgq.FGQ_ERR_SHAPE
