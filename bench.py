@@ -59,6 +59,7 @@ def parse():
                     help="time the eager launches only (default: the step is also replayed as HIP graphs, "
                          "and that pass gives value and ms_per_step)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-gqa", action="store_true", help="skip the grouped-query attention line")
     ap.add_argument("--cpu-sample-seqs", type=int, default=4)
     ap.add_argument("--cpu-sample-cols", type=int, default=256)
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -445,6 +446,101 @@ def weight_streaming(torch, fgq, w, layers, plan, steps_in, attn_out, ys, attn_w
             "fp16_weights_copy_ms": f16_ms, "fp16_over_packed_bytes": 2.0 * sum(K * N for _, K, N, _ in plan) / nbytes}
 
 
+def gqa_attention_line(torch, fgq, stream, steps: int, warmup: int) -> dict:
+    """Grouped-query decode attention over the compressed cache at the grouped
+    workload's shape (16 sequences, 16K cached positions, 32 query heads over
+    8 K/V heads): the prompt bulk-compressed into the cache, then decode steps
+    of one appended K/V token and attention over prompt + t positions, the
+    attention timed with HIP events on the launch stream.  The K/V-head sweep
+    reuses that cache: its first heads for fewer K/V heads, its heads
+    repeated for more (same seeded values; the timing does not depend on them)."""
+    w = synth.WORKLOADS["gqa"]
+    B, Hq, Hkv, D, cap = w.batch, w.heads, w.n_kv_heads, w.head_dim, w.capacity
+    sh = stream.cuda_stream
+
+    def alloc(hk):
+        kc = torch.zeros((B, hk, cap, D // 2), dtype=torch.uint8, device="cuda")
+        km = torch.zeros((B, hk, cap, D // 64), dtype=torch.int32, device="cuda")
+        return kc, torch.zeros_like(kc), km, torch.zeros_like(km)
+
+    kc, vc, km, vm = alloc(Hkv)
+    for b0 in range(0, B, 4):
+        nb = min(4, B - b0)
+        sub = fgq.kv_struct(kc[b0:b0 + nb], vc[b0:b0 + nb], km[b0:b0 + nb], vm[b0:b0 + nb], nb, Hkv, D, cap)
+        kd = torch.from_numpy(synth.prompt_kv(w, "k", b0=b0, nb=nb)).to("cuda")
+        vd = torch.from_numpy(synth.prompt_kv(w, "v", b0=b0, nb=nb)).to("cuda")
+        fgq.fgq_kv_append(sub, kd, vd, 0, w.prompt, sh)
+        torch.cuda.synchronize()
+        del kd, vd
+    kv = fgq.kv_struct(kc, vc, km, vm, B, Hkv, D, cap)
+    st = [{"k": torch.from_numpy(synth.step_kv(w, "k", t)).to("cuda"),
+           "v": torch.from_numpy(synth.step_kv(w, "v", t)).to("cuda"),
+           "q": torch.from_numpy(synth.step_q(w, t)).to("cuda")} for t in range(1, w.steps + 1)]
+    out = torch.empty((B, Hq * D), dtype=torch.float32, device="cuda")
+    wsb = max(fgq.fgq_decode_attn_gqa_ws_bytes(B, Hq, Hkv, D, L) for L in range(w.prompt + 1, cap + 1))
+    wsb_all = max(fgq.fgq_decode_attn_gqa_ws_bytes(B, Hq, hk, D, cap) for hk in (1, 2, 4, 8, 16, 32))
+    ws = torch.empty(max(wsb, wsb_all, 16), dtype=torch.uint8, device="cuda")
+
+    def step(i, ev=None):
+        t = i % w.steps + 1
+        d = st[t - 1]
+        fgq.fgq_kv_append(kv, d["k"], d["v"], w.prompt + t - 1, 1, sh)
+        if ev is not None:
+            ev[0].record(stream)
+        fgq.fgq_decode_attn_gqa_q4kv(kv, d["q"], Hq, w.prompt + t, 0.0, out, fgq.FGQ_DTYPE_F32, ws, ws.numel(), sh)
+        if ev is not None:
+            ev[1].record(stream)
+
+    for i in range(warmup):
+        step(i)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    for i in range(steps):
+        step(warmup + i, evs[i])
+    torch.cuda.synchronize()
+    ms = sum(a.elapsed_time(b) for a, b in evs)
+    ts = [(warmup + i) % w.steps + 1 for i in range(steps)]
+    byts = sum(acc.gqa_attention_bytes(B, Hq, Hkv, D, w.kv_len(t)) for t in ts)
+    fl = sum(acc.gqa_attention_flops(B, Hq, D, w.kv_len(t)) for t in ts)
+    line = {"workload": "gqa: %d sequences, %d query heads over %d K/V heads x %d, prompt %d + %d decode steps"
+                        % (B, Hq, Hkv, D, w.prompt, w.steps),
+            "us_per_launch": 1e3 * ms / steps, "GB_per_s": byts / (ms * 1e-3) / 1e9,
+            "frac_hbm_peak": byts / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "TFLOP_per_s": fl / (ms * 1e-3) / 1e12}
+
+    # K/V-head sweep at kv_len = capacity (the cache now holds every decode step)
+    sweep = {}
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    q = st[-1]["q"]
+    for hk in (32, 16, 8, 4, 2, 1):
+        if hk == Hkv:
+            arrs = (kc, vc, km, vm)
+        elif hk < Hkv:
+            arrs = tuple(a[:, :hk].contiguous() for a in (kc, vc, km, vm))
+        else:
+            arrs = tuple(a.repeat_interleave(hk // Hkv, dim=1) for a in (kc, vc, km, vm))
+        kvs = fgq.kv_struct(*arrs, B, hk, D, cap)
+        for _ in range(3):
+            fgq.fgq_decode_attn_gqa_q4kv(kvs, q, Hq, cap, 0.0, out, fgq.FGQ_DTYPE_F32, ws, ws.numel(), sh)
+        torch.cuda.synchronize()
+        reps = 10
+        e0.record(stream)
+        for _ in range(reps):
+            fgq.fgq_decode_attn_gqa_q4kv(kvs, q, Hq, cap, 0.0, out, fgq.FGQ_DTYPE_F32, ws, ws.numel(), sh)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = 1e3 * e0.elapsed_time(e1) / reps
+        b = acc.gqa_attention_bytes(B, Hq, hk, D, cap)
+        sweep["kv_heads_%d" % hk] = {"group": Hq // hk, "us_per_launch": us, "GB_per_s": b / us / 1e3,
+                                     "frac_hbm_peak": b / us / 1e3 / HBM_PEAK_GBS,
+                                     "TFLOP_per_s": acc.gqa_attention_flops(B, Hq, D, cap) / us / 1e6}
+        del arrs, kvs
+    line["kv_head_sweep_at_kv_len_%d" % cap] = sweep
+    del kc, vc, km, vm, st
+    torch.cuda.empty_cache()
+    return line
+
+
 def main():
     args = parse()
     if args.summarize_trace:
@@ -705,6 +801,11 @@ def main():
     if tk_tr is not None and w.kv_len(w.steps) <= 2048:
         kernels["topk_attention"]["traffic_bytes_per_launch"] = tk_tr["bytes_per_launch"]
         kernels["topk_attention"]["traffic_vs_algorithmic"] = tk_tr["ratio"]
+
+    if not args.no_gqa:
+        t0 = time.time()
+        kernels["gqa_attention"] = gqa_attention_line(torch, fgq, stream, 32, 8)
+        log("gqa attention line %.1fs" % (time.time() - t0))
 
     if w.weights and not args.no_stream:
         kernels["weight_streaming"] = weight_streaming(torch, fgq, w, layers, plan, steps_in, attn_out, ys, attn_ws,

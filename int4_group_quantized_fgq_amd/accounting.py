@@ -53,6 +53,19 @@ def attention_bytes(batch: int, hidden: int, kv_len: int, out_bytes: int = 4) ->
     return 2 * packed_bytes(batch * hidden * kv_len) + batch * hidden * (2 + out_bytes)
 
 
+def gqa_attention_bytes(batch: int, q_heads: int, kv_heads: int, head_dim: int, kv_len: int,
+                        out_bytes: int = 4) -> float:
+    """Grouped-query attention: the compressed K and V of the kv_heads cache
+    heads over kv_len positions (read once for the whole group of query heads),
+    plus the fp16 queries and the outputs of all q_heads."""
+    return 2 * packed_bytes(batch * kv_heads * head_dim * kv_len) + batch * q_heads * head_dim * (2 + out_bytes)
+
+
+def gqa_attention_flops(batch: int, q_heads: int, head_dim: int, kv_len: int) -> float:
+    """q.k and p*v for every query head: two multiply-adds per cached element per head."""
+    return 4.0 * batch * q_heads * head_dim * kv_len
+
+
 def topk_attention_bytes(batch: int, hidden: int, kv_len: int, kept: int, out_bytes: int = 4) -> float:
     """Top-K sparse attention: the compressed K of every position, the
     compressed V of the kept positions only, plus the query and the output."""

@@ -49,7 +49,15 @@ namespace {
 constexpr float kGqLog2e = 1.4426950408889634f;
 constexpr int kGqWaves = 4;    // waves per workgroup (one work item)
 constexpr int kGqBlock = 32;   // tokens per wave iteration: two 16-token MFMA tiles
-constexpr uint32_t kLow4 = 0x000F000Fu;
+#ifndef FGQ_GQA_RING
+#define FGQ_GQA_RING 3         // blocks per wave in the load ring (RING - 1 in flight)
+#endif
+#ifndef FGQ_GQA_WAVES_PER_EU
+#define FGQ_GQA_WAVES_PER_EU 2 // occupancy the register budget is fitted to
+#endif
+constexpr int kGqRing = FGQ_GQA_RING;
+constexpr uint32_t kLow4 = 0x000F000Fu;    // nibbles 0 and 4 of a word: codes * 2^-24 as fp16
+constexpr uint32_t kHigh4 = 0x00F000F0u;   // nibbles 1 and 5: codes * 2^-20
 
 typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -59,10 +67,14 @@ __device__ __forceinline__ f16x8 pack4(uint32_t a, uint32_t b, uint32_t c, uint3
     return __builtin_bit_cast(f16x8, v);
 }
 
-// The 8 codes of a packed word as fp16 subnormals c * 2^-24, in the k-slot
-// order [n0, n4, n1, n5, n2, n6, n3, n7] (nibble i = element i of the word).
+// The 8 codes of a packed word as fp16 subnormals, in the k-slot order
+// [n0, n4, n1, n5, n2, n6, n3, n7] (nibble i = element i of the word):
+// nibbles 0, 4 (and 2, 6 after one shift) land in the low mantissa bits as
+// c * 2^-24, nibbles 1, 5 (3, 7) four bits up as c * 2^-20.  The matching
+// query slots carry q / 16, so every product is c * q * 2^-24.
 __device__ __forceinline__ f16x8 codes_as_f16(uint32_t w) {
-    return pack4(w & kLow4, (w >> 4) & kLow4, (w >> 8) & kLow4, (w >> 12) & kLow4);
+    const uint32_t w8 = w >> 8;
+    return pack4(w & kLow4, w & kHigh4, w8 & kLow4, w8 & kHigh4);
 }
 
 __device__ __forceinline__ float lo_f(uint32_t m) { return (float)as_f16x2(m).x; }
@@ -85,7 +97,8 @@ struct GqBlock {
 };
 
 template <int D, int NT>
-__global__ __launch_bounds__(64 * kGqWaves) void attn_gqa_kernel(
+__global__ __launch_bounds__(64 * kGqWaves)
+__attribute__((amdgpu_waves_per_eu(NT == 1 ? FGQ_GQA_WAVES_PER_EU : 1))) void attn_gqa_kernel(
     const uint8_t *__restrict__ kc, const uint32_t *__restrict__ km, const uint8_t *__restrict__ vc,
     const uint32_t *__restrict__ vm, const uint16_t *__restrict__ q, int Hkv, int R, int cap, int L, int n_split,
     int tok_per_split, float sl2, float *__restrict__ ws, void *__restrict__ out, int out_f16) {
@@ -128,10 +141,13 @@ __global__ __launch_bounds__(64 * kGqWaves) void attn_gqa_kernel(
             for (int hh = 0; hh < 2; ++hh) {
                 uint4 w = *reinterpret_cast<const uint4 *>(qrow + 64 * grp + 16 * g + 8 * hh);
                 if (!valid) w = make_uint4(0u, 0u, 0u, 0u);
+                // slots (d1, d5) and (d3, d7) meet codes scaled by 2^-20: q / 16
+                // there (exact unless |q| < 2^-10, then within 2^-25)
+                const f16x2 sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
                 qf[2 * grp + hh][nt] = pack4(__builtin_amdgcn_perm(w.z, w.x, 0x05040100u),
-                                             __builtin_amdgcn_perm(w.z, w.x, 0x07060302u),
+                                             as_u32(as_f16x2(__builtin_amdgcn_perm(w.z, w.x, 0x07060302u)) * sixteenth),
                                              __builtin_amdgcn_perm(w.w, w.y, 0x05040100u),
-                                             __builtin_amdgcn_perm(w.w, w.y, 0x07060302u));
+                                             as_u32(as_f16x2(__builtin_amdgcn_perm(w.w, w.y, 0x07060302u)) * sixteenth));
                 const uint32_t ws4[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
                 for (int i = 0; i < 4; ++i) part += lo_f(ws4[i]) + hi_f(ws4[i]);
@@ -307,43 +323,44 @@ __global__ __launch_bounds__(64 * kGqWaves) void attn_gqa_kernel(
                         wb[grp][nt][4 * t + r] = (_Float16)__builtin_fmaf(p, hi_f(mw), 0.0f);
                     }
                 }
-        // ---- O^T += V^T W^T: tile n = 4 grp + qn holds d = 64 grp + 4 row + qn
+        // ---- O^T += V^T W^T: tile n = 4 grp + qn holds d = 64 grp + 4 row + qn;
+        // its codes are c * 2^-24 (qn even) or c * 2^-20 (qn odd)
 #pragma unroll
         for (int n = 0; n < NDT; ++n) {
-            const int grp = n / 4, sh = 4 * (n % 4);
-            const f16x8 a = pack4((vv[0][0][grp] >> sh) & kLow4, (vv[0][1][grp] >> sh) & kLow4,
-                                  (vv[1][0][grp] >> sh) & kLow4, (vv[1][1][grp] >> sh) & kLow4);
+            const int grp = n / 4, sh = (n % 4) >= 2 ? 8 : 0;
+            const uint32_t msk = (n % 2) ? kHigh4 : kLow4;
+            const f16x8 a = pack4((vv[0][0][grp] >> sh) & msk, (vv[0][1][grp] >> sh) & msk,
+                                  (vv[1][0][grp] >> sh) & msk, (vv[1][1][grp] >> sh) & msk);
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt)
                 o[n][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, wb[grp][nt], o[n][nt], 0, 0, 0);
         }
     };
 
-    // ---- the wave's blocks: j0 + 32 (wv + 4 i), a ring of three blocks: the
-    // loads of the next two are in flight while one is multiplied.  Loads
-    // past the end of the split re-read its last row (in bounds, unused), so
-    // every iteration issues the same loads and the waits are static.
+    // ---- the wave's blocks: j0 + 32 (wv + 4 i), a ring of kGqRing blocks:
+    // the loads of the next kGqRing - 1 are in flight while one is
+    // multiplied.  Loads past the end of the split re-read its last row (in
+    // bounds, unused), so every iteration issues the same loads and the waits
+    // are static.
     constexpr int STRIDE = kGqBlock * kGqWaves;
     int jb = j0 + kGqBlock * wv;
     if (jb < j1) {
-        GqBlock<G> buf0, buf1, buf2;
+        GqBlock<G> buf[kGqRing];
         const std::true_type tail;
         const std::false_type body;
-        load(jb, buf0);
-        load(jb + STRIDE, buf1);
-        for (;;) {
-            load(jb + 2 * STRIDE, buf2);
-            if (jb + kGqBlock <= j1) process(jb, buf0, body); else process(jb, buf0, tail);
-            jb += STRIDE;
-            if (jb >= j1) break;
-            load(jb + 2 * STRIDE, buf0);
-            if (jb + kGqBlock <= j1) process(jb, buf1, body); else process(jb, buf1, tail);
-            jb += STRIDE;
-            if (jb >= j1) break;
-            load(jb + 2 * STRIDE, buf1);
-            if (jb + kGqBlock <= j1) process(jb, buf2, body); else process(jb, buf2, tail);
-            jb += STRIDE;
-            if (jb >= j1) break;
+#pragma unroll
+        for (int i = 0; i + 1 < kGqRing; ++i) load(jb + i * STRIDE, buf[i]);
+        bool more = true;
+        while (more) {
+#pragma unroll
+            for (int i = 0; i < kGqRing; ++i) {
+                if (more) {
+                    load(jb + (kGqRing - 1) * STRIDE, buf[(i + kGqRing - 1) % kGqRing]);
+                    if (jb + kGqBlock <= j1) process(jb, buf[i], body); else process(jb, buf[i], tail);
+                    jb += STRIDE;
+                    more = jb < j1;
+                }
+            }
         }
     }
 
@@ -399,7 +416,9 @@ __global__ __launch_bounds__(64 * kGqWaves) void attn_gqa_kernel(
 #pragma unroll
                 for (int qn = 0; qn < 4; ++qn)
                     val[qn] = __builtin_fmaf(
-                        f[w], __builtin_fmaf(s_o[((w * NDT + 4 * grp + qn) * NT + nt) * 4 + r][lane], 16777216.0f, base),
+                        f[w],
+                        __builtin_fmaf(s_o[((w * NDT + 4 * grp + qn) * NT + nt) * 4 + r][lane],
+                                       (qn & 1) ? 1048576.0f : 16777216.0f, base),
                         val[qn]);
             }
             if (col >= R) continue;
@@ -433,9 +452,12 @@ __global__ __launch_bounds__(128) void attn_gqa_merge_kernel(const float *__rest
     const size_t row = blockIdx.x;
     const int d = threadIdx.x;
     const float *base = ws + row * n_split * (D + 4);
+    // unrolled so that the loads of several splits are in flight at once
     float mx = -INFINITY;
+#pragma unroll 8
     for (int i = 0; i < n_split; ++i) mx = fmaxf(mx, base[i * (D + 4) + D]);
     float num = 0.f, den = 0.f;
+#pragma unroll 8
     for (int i = 0; i < n_split; ++i) {
         const float w = exp2f(base[i * (D + 4) + D] - mx);
         num += w * base[i * (D + 4) + d];
@@ -455,13 +477,14 @@ struct GqaPlan {
     int tok_per_split;
 };
 
-// Splits of the sequence: enough workgroups to cover the CUs a few times
-// over, each split long enough that its partial state (R rows of D + 4
-// floats) stays small against the cache bytes it reads.
+// Splits of the sequence: about one resident round of workgroups (two per
+// CU with one 16-head column tile, one with two), each split long enough
+// that its partial state (R rows of D + 4 floats) stays small against the
+// cache bytes it reads.
 GqaPlan gqa_plan(int32_t batch, int32_t kv_heads, int32_t group, int32_t kv_len) {
     constexpr int per_round = kGqBlock * kGqWaves;
     const int64_t items = (int64_t)batch * kv_heads;
-    const int64_t target = 4LL * kNumCU;
+    const int64_t target = (group <= 16 ? 2LL : 1LL) * kNumCU;
     int n_split = 1;
     if (items > 0 && items < target) {
         n_split = (int)((target + items - 1) / items);
