@@ -60,6 +60,11 @@ def parse():
                          "and that pass gives value and ms_per_step)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-gqa", action="store_true", help="skip the grouped-query attention line")
+    ap.add_argument("--gqa-only", action="store_true",
+                    help="only run the grouped-query attention line (for profiling that kernel)")
+    ap.add_argument("--no-gqa-sweep", action="store_true", help="skip the K/V-head sweep of the grouped line")
+    ap.add_argument("--summarize-gqa-trace", metavar="DIR",
+                    help="only summarise a rocprofv3 --kernel-trace --stats folder of a --gqa-only run")
     ap.add_argument("--cpu-sample-seqs", type=int, default=4)
     ap.add_argument("--cpu-sample-cols", type=int, default=256)
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -78,6 +83,7 @@ def parse():
 # summary applies only while their hash is unchanged.
 KERNEL_SOURCES = {
     "dq_gemm_kernel": ("gemm.hip", "common.h"),
+    "attn_gqa_kernel": ("gqa_attention.hip", "common.h"),
     "attn_split_kernel": ("attention.hip", "common.h"),
     "attn_topk_wave_kernel": ("topk_attention.hip", "common.h"),
 }
@@ -361,6 +367,50 @@ def summarize_trace(folder: str, w, steps: int) -> None:
     print("| step (sum) | %.1f |" % tot)
 
 
+def summarize_gqa_trace(folder: str) -> None:
+    """Markdown for a rocprofv3 run of `bench.py --gqa-only`: the kernel
+    statistics, then the mean duration of the grouped attention launches of
+    the decode steps (the grid of the workload's split plan) and of their
+    split merges."""
+    import csv
+    import glob
+
+    def one(pattern):
+        f = glob.glob(os.path.join(folder, "**", pattern), recursive=True)
+        if not f:
+            raise SystemExit("no %s under %s" % (pattern, folder))
+        with open(f[0]) as fh:
+            return list(csv.DictReader(fh))
+
+    stats = one("*kernel_stats.csv")
+    print("| kernel | calls | average us | total ms | % of GPU time |")
+    print("|---|---|---|---|---|")
+    for r in stats[:10]:
+        print("| %s | %s | %.1f | %.2f | %.1f |" % (short_name(r["Name"]), r["Calls"], float(r["AverageNs"]) / 1e3,
+                                                  float(r["TotalDurationNs"]) / 1e6, float(r["Percentage"])))
+    trace = sorted(one("*kernel_trace.csv"), key=lambda r: int(r["Start_Timestamp"]))
+    by_grid = {}
+    merge = []
+    prev = None
+    for r in trace:
+        n = short_name(r["Kernel_Name"])
+        d = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+        if n.startswith("attn_gqa_kernel"):
+            by_grid.setdefault((n, int(r["Grid_Size_X"])), []).append(d)
+            prev = (n, int(r["Grid_Size_X"]))
+        elif n.startswith("attn_gqa_merge_kernel") and prev is not None:
+            merge.append((prev, d))
+    print()
+    print("Grouped attention launches by grid (the decode steps are the most frequent grid):")
+    print()
+    print("| kernel | grid (threads) | launches | mean us | split merge mean us |")
+    print("|---|---|---|---|---|")
+    for key, ds in sorted(by_grid.items(), key=lambda kv: -len(kv[1])):
+        ms = [d for k, d in merge if k == key]
+        print("| %s | %d | %d | %.1f | %s |" % (key[0], key[1], len(ds), float(np.mean(ds)),
+                                              "%.1f" % float(np.mean(ms)) if ms else "-"))
+
+
 def algorithmic_bytes_per_launch(kernel: str, w, n_steps: int = 0, warmup: int = 0) -> float:
     """Mean algorithmic HBM bytes of one launch of the kernel over the first
     n_steps bench steps (0: one full cycle of decode steps); the top-K kernel
@@ -368,6 +418,12 @@ def algorithmic_bytes_per_launch(kernel: str, w, n_steps: int = 0, warmup: int =
     if kernel == "dq_gemm_kernel":
         plan = launch_plan(w)
         return float(np.mean([acc.gemm_bytes(w.batch, K, N) for _, K, N, _ in plan]))
+    if kernel == "attn_gqa_kernel":
+        g = synth.WORKLOADS["gqa"]
+        n = n_steps or g.steps
+        ts = [i % g.steps + 1 for i in range(n)]
+        return float(np.mean([acc.gqa_attention_bytes(g.batch, g.heads, g.n_kv_heads, g.head_dim, g.kv_len(t))
+                              for t in ts]))
     if kernel == "attn_topk_wave_kernel":
         n = n_steps or w.steps
         ts = [i % w.steps + 1 for i in range(min(warmup, 8))] + \
@@ -446,7 +502,7 @@ def weight_streaming(torch, fgq, w, layers, plan, steps_in, attn_out, ys, attn_w
             "fp16_weights_copy_ms": f16_ms, "fp16_over_packed_bytes": 2.0 * sum(K * N for _, K, N, _ in plan) / nbytes}
 
 
-def gqa_attention_line(torch, fgq, stream, steps: int, warmup: int) -> dict:
+def gqa_attention_line(torch, fgq, stream, steps: int, warmup: int, sweep_heads=(32, 16, 8, 4, 2, 1)) -> dict:
     """Grouped-query decode attention over the compressed cache at the grouped
     workload's shape (16 sequences, 16K cached positions, 32 query heads over
     8 K/V heads): the prompt bulk-compressed into the cache, then decode steps
@@ -512,7 +568,7 @@ def gqa_attention_line(torch, fgq, stream, steps: int, warmup: int) -> dict:
     sweep = {}
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     q = st[-1]["q"]
-    for hk in (32, 16, 8, 4, 2, 1):
+    for hk in sweep_heads:
         if hk == Hkv:
             arrs = (kc, vc, km, vm)
         elif hk < Hkv:
@@ -535,7 +591,12 @@ def gqa_attention_line(torch, fgq, stream, steps: int, warmup: int) -> dict:
                                      "frac_hbm_peak": b / us / 1e3 / HBM_PEAK_GBS,
                                      "TFLOP_per_s": acc.gqa_attention_flops(B, Hq, D, cap) / us / 1e6}
         del arrs, kvs
-    line["kv_head_sweep_at_kv_len_%d" % cap] = sweep
+    tr = committed_traffic("attn_gqa_kernel", "gqa")
+    if tr is not None:
+        line["traffic_bytes_per_launch"] = tr["bytes_per_launch"]
+        line["traffic_vs_algorithmic"] = tr["ratio"]
+    if sweep:
+        line["kv_head_sweep_at_kv_len_%d" % cap] = sweep
     del kc, vc, km, vm, st
     torch.cuda.empty_cache()
     return line
@@ -545,6 +606,9 @@ def main():
     args = parse()
     if args.summarize_trace:
         summarize_trace(args.summarize_trace, synth.WORKLOADS[args.config], args.steps)
+        return
+    if args.summarize_gqa_trace:
+        summarize_gqa_trace(args.summarize_gqa_trace)
         return
     if args.summarize_pmc:
         w = synth.WORKLOADS[args.config]
@@ -582,6 +646,11 @@ def main():
     torch.cuda.set_device(0)
     if args.calibrate_copy:
         calibrate_copy(torch, args.calibrate_copy)
+        return
+    if args.gqa_only:
+        line = gqa_attention_line(torch, fgq, torch.cuda.current_stream(), args.steps, args.warmup,
+                                  () if args.no_gqa_sweep else (32, 16, 8, 4, 2, 1))
+        print(json.dumps({"gqa_attention": line}), flush=True)
         return
     w = synth.WORKLOADS[args.config]
     B, H, D, h = w.batch, w.heads, w.head_dim, w.hidden
@@ -804,7 +873,8 @@ def main():
 
     if not args.no_gqa:
         t0 = time.time()
-        kernels["gqa_attention"] = gqa_attention_line(torch, fgq, stream, 32, 8)
+        kernels["gqa_attention"] = gqa_attention_line(torch, fgq, stream, 32, 8,
+                                                      () if args.no_gqa_sweep else (32, 16, 8, 4, 2, 1))
         log("gqa attention line %.1fs" % (time.time() - t0))
 
     if w.weights and not args.no_stream:
