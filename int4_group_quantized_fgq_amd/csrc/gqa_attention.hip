@@ -47,10 +47,13 @@ namespace fgq {
 namespace {
 
 constexpr float kGqLog2e = 1.4426950408889634f;
-constexpr int kGqWaves = 4;    // waves per workgroup (one work item)
+constexpr int kGqWaves = 4;    // waves per workgroup
 constexpr int kGqBlock = 32;   // tokens per wave iteration: two 16-token MFMA tiles
 #ifndef FGQ_GQA_RING
 #define FGQ_GQA_RING 3         // blocks per wave in the load ring (RING - 1 in flight)
+#endif
+#ifndef FGQ_GQA_WAVE_ITEMS
+#define FGQ_GQA_WAVE_ITEMS 2048 // (sequence, K/V head) pairs from which each pair gets one wave
 #endif
 #ifndef FGQ_GQA_WAVES_PER_EU
 #define FGQ_GQA_WAVES_PER_EU 2 // occupancy the register budget is fitted to
@@ -96,12 +99,16 @@ struct GqBlock {
     uint32_t mt[G];
 };
 
-template <int D, int NT>
+// WPI = waves per work item (sequence, K/V head, split): 4 (the workgroup's
+// waves share the item and merge in LDS) when there are few items, 1 (four
+// independent items per workgroup) when there are enough to fill the chip.
+template <int D, int NT, int WPI>
 __global__ __launch_bounds__(64 * kGqWaves)
 __attribute__((amdgpu_waves_per_eu(NT == 1 ? FGQ_GQA_WAVES_PER_EU : 1))) void attn_gqa_kernel(
     const uint8_t *__restrict__ kc, const uint32_t *__restrict__ km, const uint8_t *__restrict__ vc,
     const uint32_t *__restrict__ vm, const uint16_t *__restrict__ q, int Hkv, int R, int cap, int L, int n_split,
-    int tok_per_split, float sl2, float *__restrict__ ws, void *__restrict__ out, int out_f16) {
+    int tok_per_split, int total_items, float sl2, float *__restrict__ ws, void *__restrict__ out, int out_f16) {
+    static_assert(WPI == 1 || WPI == kGqWaves, "a work item takes one wave or the whole workgroup");
     constexpr int G = D / 64;       // groups per token row
     constexpr int KS = 2 * G;       // q.k MFMA k-steps (32 d each)
     constexpr int NDT = 4 * G;      // p.v output tiles of 16 d
@@ -116,7 +123,9 @@ __attribute__((amdgpu_waves_per_eu(NT == 1 ? FGQ_GQA_WAVES_PER_EU : 1))) void at
     const int lane = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
     const int c = lane & 15, g = lane >> 4;
-    const int item = blockIdx.x;
+    const int item = WPI == 1 ? (int)blockIdx.x * kGqWaves + wv : (int)blockIdx.x;
+    if (WPI == 1 && item >= total_items) return;   // wave-uniform; no workgroup barrier on this path
+    const int wi = WPI == 1 ? 0 : wv;               // the wave's place within its item
     const int split = item % n_split;
     const int bk = item / n_split;           // b * Hkv + kv head
     const int b = bk / Hkv, kh = bk - b * Hkv;
@@ -342,8 +351,8 @@ __attribute__((amdgpu_waves_per_eu(NT == 1 ? FGQ_GQA_WAVES_PER_EU : 1))) void at
     // multiplied.  Loads past the end of the split re-read its last row (in
     // bounds, unused), so every iteration issues the same loads and the waits
     // are static.
-    constexpr int STRIDE = kGqBlock * kGqWaves;
-    int jb = j0 + kGqBlock * wv;
+    constexpr int STRIDE = kGqBlock * WPI;
+    int jb = j0 + kGqBlock * wi;
     if (jb < j1) {
         GqBlock<G> buf[kGqRing];
         const std::true_type tail;
@@ -375,6 +384,50 @@ __attribute__((amdgpu_waves_per_eu(NT == 1 ? FGQ_GQA_WAVES_PER_EU : 1))) void at
             mc[grp][nt] += __shfl_xor(mc[grp][nt], 16, 64);
             mc[grp][nt] += __shfl_xor(mc[grp][nt], 32, 64);
         }
+    }
+
+    if constexpr (WPI == 1) {
+        // ---- one wave holds the whole item: lane (c, g) finishes
+        // d = 64 grp + 16 g + 4 r + qn, qn = 0..3 (16-byte stores)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+            const int col = 16 * nt + c;
+            if (col >= R) continue;
+            const size_t orow = (size_t)b * Hq + (size_t)kh * R + col;
+            const float inv = 1.0f / l_run[nt];
+#pragma unroll
+            for (int grp = 0; grp < G; ++grp)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    f32x4 val;
+#pragma unroll
+                    for (int qn = 0; qn < 4; ++qn)
+                        val[qn] = __builtin_fmaf(o[4 * grp + qn][nt][r], (qn & 1) ? 1048576.0f : 16777216.0f,
+                                                 mc[grp][nt]);
+                    const int d0 = 64 * grp + 16 * g + 4 * r;
+                    if (n_split == 1) {
+                        val *= inv;
+                        if (out_f16) {
+                            _Float16 *op = static_cast<_Float16 *>(out) + orow * D + d0;
+                            op[0] = (_Float16)val[0]; op[1] = (_Float16)val[1];
+                            op[2] = (_Float16)val[2]; op[3] = (_Float16)val[3];
+                        } else {
+                            *reinterpret_cast<f32x4 *>(static_cast<float *>(out) + orow * D + d0) = val;
+                        }
+                    } else {
+                        float *wrow = ws + (orow * n_split + split) * (D + 4);
+                        *reinterpret_cast<f32x4 *>(wrow + d0) = val;
+                        if (grp == 0 && r == 0 && g == 0) {
+                            wrow[D] = m_run[nt];
+                            wrow[D + 1] = l_run[nt];
+                        }
+                    }
+                }
+        }
+        return;
+    } else {
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
         if (g == 0) {
             s_m[wv][nt][c] = m_run[nt];
             s_l[wv][nt][c] = l_run[nt];
@@ -387,7 +440,6 @@ __attribute__((amdgpu_waves_per_eu(NT == 1 ? FGQ_GQA_WAVES_PER_EU : 1))) void at
             for (int r = 0; r < 4; ++r) s_o[((wv * NDT + n) * NT + nt) * 4 + r][lane] = o[n][nt][r];
     }
     __syncthreads();
-
     // ---- merge the 4 waves: wave wv finishes (group, row) pairs wv*G .. wv*G + G-1,
     // i.e. d = 64 grp + 16 g + 4 r + qn for qn = 0..3 (one 16-byte store)
 #pragma unroll
@@ -442,6 +494,7 @@ __attribute__((amdgpu_waves_per_eu(NT == 1 ? FGQ_GQA_WAVES_PER_EU : 1))) void at
             }
         }
     }
+    }
 }
 
 // Merge the n_split partial states (o unnormalised, m in the log2 domain, l)
@@ -475,6 +528,7 @@ __global__ __launch_bounds__(128) void attn_gqa_merge_kernel(const float *__rest
 struct GqaPlan {
     int n_split;
     int tok_per_split;
+    int wpi;    // waves per work item
 };
 
 // Splits of the sequence: about one resident round of workgroups (two per
@@ -482,8 +536,10 @@ struct GqaPlan {
 // that its partial state (R rows of D + 4 floats) stays small against the
 // cache bytes it reads.
 GqaPlan gqa_plan(int32_t batch, int32_t kv_heads, int32_t group, int32_t kv_len) {
-    constexpr int per_round = kGqBlock * kGqWaves;
     const int64_t items = (int64_t)batch * kv_heads;
+    // enough (sequence, K/V head) pairs for two waves per SIMD: one wave each, no splits
+    if (group <= 16 && items >= FGQ_GQA_WAVE_ITEMS) return {1, kv_len, 1};
+    constexpr int per_round = kGqBlock * kGqWaves;
     const int64_t target = (group <= 16 ? 2LL : 1LL) * kNumCU;
     int n_split = 1;
     if (items > 0 && items < target) {
@@ -495,7 +551,7 @@ GqaPlan gqa_plan(int32_t batch, int32_t kv_heads, int32_t group, int32_t kv_len)
     int per = (kv_len + n_split - 1) / n_split;
     per = ((per + per_round - 1) / per_round) * per_round;
     n_split = (kv_len + per - 1) / per;
-    return {n_split, per};
+    return {n_split, per, kGqWaves};
 }
 
 size_t gqa_ws_bytes(int32_t batch, int32_t q_heads, int32_t kv_heads, int32_t head_dim, int32_t kv_len) {
@@ -512,17 +568,21 @@ fgq_status launch_decode_attn_gqa(const fgq_kv_cache *kv, const void *q, int32_t
     if (items == 0) return FGQ_OK;
     const float sl2 = scale * kGqLog2e;
     const int f16 = out_dtype == FGQ_DTYPE_F16;
-    const dim3 grid((unsigned)items), block(64 * kGqWaves);
+    const dim3 grid((unsigned)(p.wpi == 1 ? (items + kGqWaves - 1) / kGqWaves : items)), block(64 * kGqWaves);
     const uint16_t *qh = static_cast<const uint16_t *>(q);
     float *w = static_cast<float *>(ws);
-#define FGQ_GQA_LAUNCH(D, NT)                                                                                   \
-    attn_gqa_kernel<D, NT><<<grid, block, 0, stream>>>(kv->k_codes, kv->k_meta, kv->v_codes, kv->v_meta, qh,  \
-                                                       kv->heads, R, kv->capacity, kv_len, p.n_split,          \
-                                                       p.tok_per_split, sl2, w, out, f16)
+#define FGQ_GQA_LAUNCH(D, NT, WPI)                                                                              \
+    attn_gqa_kernel<D, NT, WPI><<<grid, block, 0, stream>>>(kv->k_codes, kv->k_meta, kv->v_codes, kv->v_meta, \
+                                                            qh, kv->heads, R, kv->capacity, kv_len, p.n_split, \
+                                                            p.tok_per_split, (int)items, sl2, w, out, f16)
     if (kv->head_dim == 128) {
-        if (R <= 16) FGQ_GQA_LAUNCH(128, 1); else FGQ_GQA_LAUNCH(128, 2);
+        if (R > 16) FGQ_GQA_LAUNCH(128, 2, kGqWaves);
+        else if (p.wpi == 1) FGQ_GQA_LAUNCH(128, 1, 1);
+        else FGQ_GQA_LAUNCH(128, 1, kGqWaves);
     } else {
-        if (R <= 16) FGQ_GQA_LAUNCH(64, 1); else FGQ_GQA_LAUNCH(64, 2);
+        if (R > 16) FGQ_GQA_LAUNCH(64, 2, kGqWaves);
+        else if (p.wpi == 1) FGQ_GQA_LAUNCH(64, 1, 1);
+        else FGQ_GQA_LAUNCH(64, 1, kGqWaves);
     }
 #undef FGQ_GQA_LAUNCH
     fgq_status s = check_launch("attn_gqa_kernel");

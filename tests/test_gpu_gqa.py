@@ -144,3 +144,13 @@ def _full_size(w, t, samples):
 @pytest.mark.parametrize("kv_heads,t,samples", [(8, 2, (0, 15)), (1, 1, (5,))])
 def test_gqa_workload_full_size_sampled(kv_heads, t, samples):
     _full_size(dataclasses.replace(W["gqa"], kv_heads=kv_heads), t, samples)
+
+
+@pytest.mark.parametrize("B,Hkv,R,D,L", [(64, 32, 2, 128, 300), (64, 32, 4, 64, 257)])
+def test_gqa_one_wave_per_item_plan(B, Hkv, R, D, L):
+    """At least 2048 (sequence, K/V head) pairs: one wave per pair, no split."""
+    assert gu.fgq.fgq_decode_attn_gqa_ws_bytes(B, Hkv * R, Hkv, D, L) == 0
+    w = _shape(W["gqa"], B, Hkv, R, D, L)
+    dev, ref = _case(w)
+    for Lq in (L, L - 1, 33):
+        _check(dev, ref, w, Lq, "one wave per pair")
