@@ -86,9 +86,12 @@ __device__ __forceinline__ uint4 stream_load16(const uint8_t *p) {
     return make_uint4(v[0], v[1], v[2], v[3]);
 }
 
-// D = head_dim (64 or 128); CH = token iterations per chunk (even).
+// D = head_dim (64 or 128); CH = token iterations per chunk (even).  Short
+// chunks leave registers for four waves per SIMD (many short sequences);
+// long chunks keep more bytes in flight per wave at two (long sequences).
 template <int D, int CH>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void attn_split_kernel(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(CH <= 2 ? 4 : (CH >= 6 ? 2 : 3))))
+void attn_split_kernel(
     const uint8_t *__restrict__ kc, const uint32_t *__restrict__ km, const uint8_t *__restrict__ vc,
     const uint32_t *__restrict__ vm, const uint16_t *__restrict__ q, int H, int cap, int L, int n_split,
     int tok_per_split, int total_items, float sl2, float *__restrict__ ws, void *__restrict__ out,
@@ -322,9 +325,12 @@ __global__ __launch_bounds__(128) void attn_merge_kernel(const float *__restrict
     const int bh = blockIdx.x;
     const int d = threadIdx.x;
     const float *base = ws + (size_t)bh * n_split * (D + 4);
+    // unrolled so that the loads of several splits are in flight at once
     float mx = -INFINITY;
+#pragma unroll 8
     for (int i = 0; i < n_split; ++i) mx = fmaxf(mx, base[i * (D + 4) + D]);
     float num = 0.f, den = 0.f;
+#pragma unroll 8
     for (int i = 0; i < n_split; ++i) {
         const float w = exp2f(base[i * (D + 4) + D] - mx);
         num += w * base[i * (D + 4) + d];
@@ -337,18 +343,22 @@ __global__ __launch_bounds__(128) void attn_merge_kernel(const float *__restrict
         static_cast<float *>(out)[(size_t)bh * D + d] = v;
 }
 
-constexpr int kChunkIters = 4;
+// Token iterations per chunk: the middle setting (three waves per SIMD) when
+// a wave streams few tokens, long chunks (two waves per SIMD, more bytes in
+// flight per wave) when it streams many.
+constexpr int kChunkShort = 4, kChunkLong = 6;
+constexpr int kLongChunkTokens = 768;   // tokens per wave from which the long chunk is used
 
 }  // namespace
 
 struct AttnPlan {
     int n_split;
     int tok_per_split;
+    int chunk_iters;
 };
 
 AttnPlan attn_plan(int32_t batch, int32_t heads, int32_t head_dim, int32_t kv_len) {
     const int tpi = 64 / (head_dim / 32);
-    const int chunk = kChunkIters * tpi;
     const int64_t bh = (int64_t)batch * heads;
     const int64_t target_waves = 8LL * 4 * kNumCU;     // ~8 waves per SIMD in flight
     int n_split = 1;
@@ -358,9 +368,11 @@ AttnPlan attn_plan(int32_t batch, int32_t heads, int32_t head_dim, int32_t kv_le
         if (n_split > max_split) n_split = max_split;
     }
     int per = (kv_len + n_split - 1) / n_split;
+    const int ch = per >= kLongChunkTokens ? kChunkLong : kChunkShort;
+    const int chunk = ch * tpi;
     per = ((per + chunk - 1) / chunk) * chunk;
     n_split = (kv_len + per - 1) / per;   // drop empty splits
-    return {n_split, per};
+    return {n_split, per, ch};
 }
 
 size_t attn_ws_bytes(int32_t batch, int32_t heads, int32_t head_dim, int32_t kv_len) {
@@ -377,14 +389,17 @@ fgq_status launch_decode_attn(const fgq_kv_cache *kv, const void *q, int32_t kv_
     const float sl2 = scale * kLog2e;
     const int f16 = out_dtype == FGQ_DTYPE_F16;
     const dim3 grid((unsigned)((total + 3) / 4)), block(256);
-    if (kv->head_dim == 128)
-        attn_split_kernel<128, kChunkIters><<<grid, block, 0, stream>>>(
-            kv->k_codes, kv->k_meta, kv->v_codes, kv->v_meta, static_cast<const uint16_t *>(q), kv->heads,
-            kv->capacity, kv_len, p.n_split, p.tok_per_split, total, sl2, static_cast<float *>(ws), out, f16);
-    else
-        attn_split_kernel<64, kChunkIters><<<grid, block, 0, stream>>>(
-            kv->k_codes, kv->k_meta, kv->v_codes, kv->v_meta, static_cast<const uint16_t *>(q), kv->heads,
-            kv->capacity, kv_len, p.n_split, p.tok_per_split, total, sl2, static_cast<float *>(ws), out, f16);
+#define FGQ_ATTN_LAUNCH(D, CH)                                                                                  \
+    attn_split_kernel<D, CH><<<grid, block, 0, stream>>>(kv->k_codes, kv->k_meta, kv->v_codes, kv->v_meta,      \
+                                                         static_cast<const uint16_t *>(q), kv->heads, kv->capacity, \
+                                                         kv_len, p.n_split, p.tok_per_split, total, sl2,        \
+                                                         static_cast<float *>(ws), out, f16)
+    if (kv->head_dim == 128) {
+        if (p.chunk_iters == kChunkLong) FGQ_ATTN_LAUNCH(128, kChunkLong); else FGQ_ATTN_LAUNCH(128, kChunkShort);
+    } else {
+        if (p.chunk_iters == kChunkLong) FGQ_ATTN_LAUNCH(64, kChunkLong); else FGQ_ATTN_LAUNCH(64, kChunkShort);
+    }
+#undef FGQ_ATTN_LAUNCH
     fgq_status s = check_launch("attn_split_kernel");
     if (s != FGQ_OK || p.n_split == 1) return s;
     const dim3 mgrid((unsigned)(kv->batch * kv->heads));

@@ -204,6 +204,29 @@ def test_attention_full_size_sampled(name, t, samples):
     _full_size_attention_rows(name, t, samples)
 
 
+@pytest.mark.parametrize("B,H,D,L", [(8, 256, 64, 3100), (16, 128, 128, 4100)])
+def test_attention_long_chunk_plan_sampled(B, H, D, L):
+    """2048 (sequence, head) pairs over 3-4K positions: four splits of 775-1025
+    tokens, the long-chunk launch (ragged last chunk of every split); sampled
+    sequences against the oracle on the same codes."""
+    import dataclasses
+    w = dataclasses.replace(W["long-t3"], g=B, m=1, heads=H, head_dim=D, prompt=L, steps=1)
+    gu.note("long-chunk plan B=%d H=%d D=%d L=%d" % (B, H, D, L))
+    dev = gu.DevKV(B, H, D, L)
+    for b0 in range(0, B, 4):
+        nb = min(4, B - b0)
+        sub = gu.fgq.kv_struct(dev.k_codes[b0:b0 + nb], dev.v_codes[b0:b0 + nb], dev.k_meta[b0:b0 + nb],
+                               dev.v_meta[b0:b0 + nb], nb, H, D, L)
+        gu.fgq.fgq_kv_append(sub, gu.to_dev(synth.prompt_kv(w, "k", b0=b0, nb=nb)),
+                             gu.to_dev(synth.prompt_kv(w, "v", b0=b0, nb=nb)), 0, L)
+    q = synth.step_q(w, 1)
+    got = dev.attend(q, L)
+    for b in (0, B - 1):
+        ref = oracle.KVCache(1, H, D, L)
+        oracle.kv_append(ref, synth.prompt_kv(w, "k", b0=b, nb=1), synth.prompt_kv(w, "v", b0=b, nb=1), 0)
+        gu.assert_close(got[b:b + 1], oracle.decode_attn(ref, q[b:b + 1], L), "long-chunk seq %d" % b)
+
+
 def test_attention_result_does_not_depend_on_batch_split_plan():
     """The same sequences attended alone (long splits merged) and inside a wide
     batch (one split) agree within tolerance, and each matches the oracle."""
