@@ -16,6 +16,7 @@
 // word of codes (8 nibbles) and the segment's first lane writes the meta
 // word.  The division is the correctly rounded one (HIP default).
 #include "common.h"
+#include "fastdiv.h"
 
 namespace fgq {
 namespace {
@@ -94,22 +95,24 @@ __device__ __forceinline__ GroupOut quantize8(const uint4 raw) {
     return out;
 }
 
-__global__ __launch_bounds__(256) void quantize_g64_kernel(const uint16_t *__restrict__ x, int64_t rows,
-                                                           int64_t cols, int64_t ld,
+// One launch covers fewer than 2^31 groups, so positions are 32-bit and the
+// row of a group comes from a division by the launch-invariant group count
+// per row (multiply-high + shifts) instead of a 64-bit division.
+__global__ __launch_bounds__(256) void quantize_g64_kernel(const uint16_t *__restrict__ x, uint32_t total,
+                                                           FastDiv div_ngr, int64_t cols, int64_t ld,
                                                            uint32_t *__restrict__ codes,
                                                            uint32_t *__restrict__ meta) {
-    const int64_t ngr = cols >> 6;
-    const int64_t total = rows * ngr;
-    const int64_t gid = (int64_t)blockIdx.x * 32 + (threadIdx.x >> 3);
+    const uint32_t gid = blockIdx.x * 32u + (threadIdx.x >> 3);
     const int sub = threadIdx.x & 7;
     const bool valid = gid < total;
-    const int64_t r = valid ? gid / ngr : 0;
-    const int64_t gi = valid ? gid - r * ngr : 0;
+    const uint32_t g2 = valid ? gid : 0u;
+    const uint32_t r = fastdiv(g2, div_ngr);
+    const uint32_t gi = g2 - r * div_ngr.d;
     uint4 raw = make_uint4(0u, 0u, 0u, 0u);
-    if (valid) raw = *reinterpret_cast<const uint4 *>(x + r * ld + gi * 64 + sub * 8);
+    if (valid) raw = *reinterpret_cast<const uint4 *>(x + (int64_t)r * ld + gi * 64 + sub * 8);
     const GroupOut o = quantize8(raw);
     if (!valid) return;
-    codes[(r * (cols >> 1) + gi * 32 + sub * 4) >> 2] = o.codes;
+    codes[((int64_t)r * (cols >> 1) + gi * 32 + sub * 4) >> 2] = o.codes;
     if (sub == 0) meta[gid] = o.meta;
 }
 
@@ -117,39 +120,42 @@ __global__ __launch_bounds__(256) void quantize_g64_kernel(const uint16_t *__res
 // gid enumerates (which in {K,V}, b, head, i, group-in-head), the group
 // fastest and then the token: the groups of consecutive tokens of one head
 // are consecutive in the head-major cache, so a wave's code and meta writes
-// are contiguous runs (its reads are 128-byte slices of token rows).
+// are contiguous runs (its reads are 128-byte slices of token rows).  The
+// position is decoded with 32-bit divisions by the launch-invariant n_new and
+// head count (multiply-high + shifts); a launch covers fewer than 2^31 groups.
 __global__ __launch_bounds__(256) void kv_append_kernel(const uint16_t *__restrict__ k_new,
                                                         const uint16_t *__restrict__ v_new,
-                                                        fgq_kv_cache kv, int32_t pos, int32_t n_new) {
-    const int gph = kv.head_dim >> 6;                       // groups per head
-    const int64_t per_tensor = (int64_t)kv.batch * n_new * kv.heads * gph;
-    const int64_t gid = (int64_t)blockIdx.x * 32 + (threadIdx.x >> 3);
+                                                        fgq_kv_cache kv, int32_t pos, uint32_t total,
+                                                        FastDiv div_n, FastDiv div_h) {
+    const int lg = kv.head_dim == 128 ? 1 : 0;              // log2(groups per head)
+    const uint32_t gid = blockIdx.x * 32u + (threadIdx.x >> 3);
     const int sub = threadIdx.x & 7;
-    const bool valid = gid < 2 * per_tensor;
-    const int which = (valid && gid >= per_tensor) ? 1 : 0;
-    int64_t rem = valid ? gid - which * per_tensor : 0;
-    const int gi = (int)(rem % gph);
-    rem /= gph;
-    const int i = (int)(rem % n_new);
-    rem /= n_new;
-    const int hd = (int)(rem % kv.heads);
-    const int64_t b = rem / kv.heads;
+    const bool valid = gid < total;
+    const uint32_t g2 = valid ? gid : 0u;
+    const uint32_t gi = g2 & ((1u << lg) - 1u);
+    const uint32_t r1 = g2 >> lg;                  // (which, b, head, i)
+    const uint32_t r2 = fastdiv(r1, div_n);        // (which, b, head)
+    const uint32_t i = r1 - r2 * div_n.d;
+    const uint32_t r3 = fastdiv(r2, div_h);        // (which, b)
+    const uint32_t hd = r2 - r3 * div_h.d;
+    const int which = r3 >= (uint32_t)kv.batch ? 1 : 0;
+    const uint32_t b = r3 - (which ? (uint32_t)kv.batch : 0u);
+    const int64_t n_new = div_n.d;
     const int64_t hidden = (int64_t)kv.heads * kv.head_dim;
     const uint16_t *src = which ? v_new : k_new;
     uint4 raw = make_uint4(0u, 0u, 0u, 0u);
     if (valid)
-        raw = *reinterpret_cast<const uint4 *>(src + (b * n_new + i) * hidden + (int64_t)hd * kv.head_dim +
+        raw = *reinterpret_cast<const uint4 *>(src + ((int64_t)b * n_new + i) * hidden + (int64_t)hd * kv.head_dim +
                                                gi * 64 + sub * 8);
     const GroupOut o = quantize8(raw);
     if (!valid) return;
-    const int64_t slot = (b * kv.heads + hd) * kv.capacity + pos + i;
+    const int64_t slot = ((int64_t)b * kv.heads + hd) * kv.capacity + pos + i;
     uint8_t *cbase = which ? kv.v_codes : kv.k_codes;
     uint32_t *mbase = which ? kv.v_meta : kv.k_meta;
     *reinterpret_cast<uint32_t *>(cbase + slot * (kv.head_dim >> 1) + gi * 32 + sub * 4) = o.codes;
-    if (sub == 0) mbase[slot * gph + gi] = o.meta;
+    if (sub == 0) mbase[slot * (1 << lg) + gi] = o.meta;
 }
 
-// Weight re-layout: one thread per packed code word (kc, g, lane, j).
 __global__ __launch_bounds__(256) void pack_codes_kernel(const uint8_t *__restrict__ codes, int64_t K,
                                                          int64_t N, uint32_t *__restrict__ packed) {
     const int64_t words = K * N / 8;
@@ -233,24 +239,53 @@ __global__ __launch_bounds__(256) void pack_meta_kernel(const uint32_t *__restri
 
 }  // namespace
 
+// Launches of fewer than 2^31 groups each: the rows in chunks for the
+// quantiser, the sequences in chunks for the append.
+constexpr int64_t kMaxGroupsPerLaunch = (int64_t)1 << 30;
+
 fgq_status launch_quantize(const void *x, int64_t rows, int64_t cols, int64_t ld, uint8_t *codes,
                            uint32_t *meta, hipStream_t stream) {
-    const int64_t groups = rows * (cols / 64);
-    if (groups == 0) return FGQ_OK;
-    const int64_t blocks = (groups + 31) / 32;
-    quantize_g64_kernel<<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(
-        static_cast<const uint16_t *>(x), rows, cols, ld, reinterpret_cast<uint32_t *>(codes), meta);
-    return check_launch("quantize_g64_kernel");
+    const int64_t ngr = cols / 64;
+    if (rows == 0 || ngr == 0) return FGQ_OK;
+    const int64_t rows_per = kMaxGroupsPerLaunch / ngr > 0 ? kMaxGroupsPerLaunch / ngr : 1;
+    const FastDiv div_ngr = make_fastdiv((uint32_t)ngr);
+    for (int64_t r0 = 0; r0 < rows; r0 += rows_per) {
+        const int64_t nr = rows - r0 < rows_per ? rows - r0 : rows_per;
+        const int64_t groups = nr * ngr;
+        quantize_g64_kernel<<<dim3((unsigned)((groups + 31) / 32)), dim3(256), 0, stream>>>(
+            static_cast<const uint16_t *>(x) + r0 * ld, (uint32_t)groups, div_ngr, cols, ld,
+            reinterpret_cast<uint32_t *>(codes + r0 * (cols / 2)), meta + r0 * ngr);
+        fgq_status s = check_launch("quantize_g64_kernel");
+        if (s != FGQ_OK) return s;
+    }
+    return FGQ_OK;
 }
 
 fgq_status launch_kv_append(const fgq_kv_cache *kv, const void *k_new, const void *v_new, int32_t pos,
                             int32_t n_new, hipStream_t stream) {
-    const int64_t groups = 2LL * kv->batch * n_new * kv->heads * (kv->head_dim / 64);
-    if (groups == 0) return FGQ_OK;
-    const int64_t blocks = (groups + 31) / 32;
-    kv_append_kernel<<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(
-        static_cast<const uint16_t *>(k_new), static_cast<const uint16_t *>(v_new), *kv, pos, n_new);
-    return check_launch("kv_append_kernel");
+    const int64_t gph = kv->head_dim / 64;
+    const int64_t per_seq = 2LL * n_new * kv->heads * gph;   // groups of one sequence (K and V)
+    if (per_seq == 0 || kv->batch == 0) return FGQ_OK;
+    const int64_t seq_per = kMaxGroupsPerLaunch / per_seq > 0 ? kMaxGroupsPerLaunch / per_seq : 1;
+    const FastDiv div_n = make_fastdiv((uint32_t)n_new), div_h = make_fastdiv((uint32_t)kv->heads);
+    const int64_t hidden = (int64_t)kv->heads * kv->head_dim;
+    const int64_t rows = (int64_t)kv->heads * kv->capacity;   // cache rows of one sequence
+    for (int64_t b0 = 0; b0 < kv->batch; b0 += seq_per) {
+        const int64_t nb = kv->batch - b0 < seq_per ? kv->batch - b0 : seq_per;
+        fgq_kv_cache sub = *kv;
+        sub.batch = (int32_t)nb;
+        sub.k_codes = kv->k_codes + b0 * rows * (kv->head_dim / 2);
+        sub.v_codes = kv->v_codes + b0 * rows * (kv->head_dim / 2);
+        sub.k_meta = kv->k_meta + b0 * rows * gph;
+        sub.v_meta = kv->v_meta + b0 * rows * gph;
+        const int64_t groups = nb * per_seq;
+        kv_append_kernel<<<dim3((unsigned)((groups + 31) / 32)), dim3(256), 0, stream>>>(
+            static_cast<const uint16_t *>(k_new) + b0 * n_new * hidden,
+            static_cast<const uint16_t *>(v_new) + b0 * n_new * hidden, sub, pos, (uint32_t)groups, div_n, div_h);
+        fgq_status s = check_launch("kv_append_kernel");
+        if (s != FGQ_OK) return s;
+    }
+    return FGQ_OK;
 }
 
 fgq_status launch_pack_weight(const uint8_t *codes, const uint32_t *meta, int64_t K, int64_t N,
