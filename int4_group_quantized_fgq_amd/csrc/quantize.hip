@@ -123,15 +123,18 @@ __global__ __launch_bounds__(256) void quantize_g64_kernel(const uint16_t *__res
 // are contiguous runs (its reads are 128-byte slices of token rows).  The
 // position is decoded with 32-bit divisions by the launch-invariant n_new and
 // head count (multiply-high + shifts); a launch covers fewer than 2^31 groups.
-__global__ __launch_bounds__(256) void kv_append_kernel(const uint16_t *__restrict__ k_new,
-                                                        const uint16_t *__restrict__ v_new,
-                                                        fgq_kv_cache kv, int32_t pos, uint32_t total,
-                                                        FastDiv div_n, FastDiv div_h) {
-    const int lg = kv.head_dim == 128 ? 1 : 0;              // log2(groups per head)
-    const uint32_t gid = blockIdx.x * 32u + (threadIdx.x >> 3);
-    const int sub = threadIdx.x & 7;
-    const bool valid = gid < total;
-    const uint32_t g2 = valid ? gid : 0u;
+// A workgroup takes 32 * GPT groups: each 8-lane segment loads its GPT groups
+// first, so GPT 16-byte loads per lane are in flight at once.
+struct AppendPos {
+    const uint16_t *src;
+    int64_t slot;
+    uint32_t gi;
+    int which;
+};
+
+__device__ __forceinline__ AppendPos append_pos(uint32_t g2, const fgq_kv_cache &kv, int lg, const FastDiv &div_n,
+                                                const FastDiv &div_h, const uint16_t *k_new,
+                                                const uint16_t *v_new, int32_t pos, int sub) {
     const uint32_t gi = g2 & ((1u << lg) - 1u);
     const uint32_t r1 = g2 >> lg;                  // (which, b, head, i)
     const uint32_t r2 = fastdiv(r1, div_n);        // (which, b, head)
@@ -140,22 +143,45 @@ __global__ __launch_bounds__(256) void kv_append_kernel(const uint16_t *__restri
     const uint32_t hd = r2 - r3 * div_h.d;
     const int which = r3 >= (uint32_t)kv.batch ? 1 : 0;
     const uint32_t b = r3 - (which ? (uint32_t)kv.batch : 0u);
-    const int64_t n_new = div_n.d;
     const int64_t hidden = (int64_t)kv.heads * kv.head_dim;
-    const uint16_t *src = which ? v_new : k_new;
-    uint4 raw = make_uint4(0u, 0u, 0u, 0u);
-    if (valid)
-        raw = *reinterpret_cast<const uint4 *>(src + ((int64_t)b * n_new + i) * hidden + (int64_t)hd * kv.head_dim +
-                                               gi * 64 + sub * 8);
-    const GroupOut o = quantize8(raw);
-    if (!valid) return;
-    const int64_t slot = ((int64_t)b * kv.heads + hd) * kv.capacity + pos + i;
-    uint8_t *cbase = which ? kv.v_codes : kv.k_codes;
-    uint32_t *mbase = which ? kv.v_meta : kv.k_meta;
-    *reinterpret_cast<uint32_t *>(cbase + slot * (kv.head_dim >> 1) + gi * 32 + sub * 4) = o.codes;
-    if (sub == 0) mbase[slot * (1 << lg) + gi] = o.meta;
+    AppendPos p;
+    p.src = (which ? v_new : k_new) + ((int64_t)b * div_n.d + i) * hidden + (int64_t)hd * kv.head_dim + gi * 64 +
+            sub * 8;
+    p.slot = ((int64_t)b * kv.heads + hd) * kv.capacity + pos + i;
+    p.gi = gi;
+    p.which = which;
+    return p;
 }
 
+template <int GPT>
+__global__ __launch_bounds__(256) void kv_append_kernel(const uint16_t *__restrict__ k_new,
+                                                        const uint16_t *__restrict__ v_new,
+                                                        fgq_kv_cache kv, int32_t pos, uint32_t total,
+                                                        FastDiv div_n, FastDiv div_h) {
+    const int lg = kv.head_dim == 128 ? 1 : 0;              // log2(groups per head)
+    const int sub = threadIdx.x & 7;
+    AppendPos p[GPT];
+    uint4 raw[GPT];
+#pragma unroll
+    for (int k = 0; k < GPT; ++k) {
+        const uint32_t gid = blockIdx.x * (32u * GPT) + 32u * k + (threadIdx.x >> 3);
+        p[k] = append_pos(gid < total ? gid : 0u, kv, lg, div_n, div_h, k_new, v_new, pos, sub);
+        raw[k] = make_uint4(0u, 0u, 0u, 0u);
+        if (gid < total) raw[k] = *reinterpret_cast<const uint4 *>(p[k].src);
+    }
+#pragma unroll
+    for (int k = 0; k < GPT; ++k) {
+        const uint32_t gid = blockIdx.x * (32u * GPT) + 32u * k + (threadIdx.x >> 3);
+        const GroupOut o = quantize8(raw[k]);   // every lane of the segment takes part
+        if (gid >= total) continue;
+        uint8_t *cbase = p[k].which ? kv.v_codes : kv.k_codes;
+        uint32_t *mbase = p[k].which ? kv.v_meta : kv.k_meta;
+        *reinterpret_cast<uint32_t *>(cbase + p[k].slot * (kv.head_dim >> 1) + p[k].gi * 32 + sub * 4) = o.codes;
+        if (sub == 0) mbase[p[k].slot * (1 << lg) + p[k].gi] = o.meta;
+    }
+}
+
+// Weight re-layout: one thread per packed code word (kc, g, lane, j).
 __global__ __launch_bounds__(256) void pack_codes_kernel(const uint8_t *__restrict__ codes, int64_t K,
                                                          int64_t N, uint32_t *__restrict__ packed) {
     const int64_t words = K * N / 8;
@@ -242,6 +268,11 @@ __global__ __launch_bounds__(256) void pack_meta_kernel(const uint32_t *__restri
 // Launches of fewer than 2^31 groups each: the rows in chunks for the
 // quantiser, the sequences in chunks for the append.
 constexpr int64_t kMaxGroupsPerLaunch = (int64_t)1 << 30;
+// Bulk appends (a prompt) give each 8-lane segment FGQ_APPEND_GPT groups.
+#ifndef FGQ_APPEND_GPT
+#define FGQ_APPEND_GPT 2
+#endif
+constexpr int64_t kAppendManyGroups = (int64_t)1 << 18;
 
 fgq_status launch_quantize(const void *x, int64_t rows, int64_t cols, int64_t ld, uint8_t *codes,
                            uint32_t *meta, hipStream_t stream) {
@@ -279,9 +310,16 @@ fgq_status launch_kv_append(const fgq_kv_cache *kv, const void *k_new, const voi
         sub.k_meta = kv->k_meta + b0 * rows * gph;
         sub.v_meta = kv->v_meta + b0 * rows * gph;
         const int64_t groups = nb * per_seq;
-        kv_append_kernel<<<dim3((unsigned)((groups + 31) / 32)), dim3(256), 0, stream>>>(
-            static_cast<const uint16_t *>(k_new) + b0 * n_new * hidden,
-            static_cast<const uint16_t *>(v_new) + b0 * n_new * hidden, sub, pos, (uint32_t)groups, div_n, div_h);
+        const uint16_t *kn = static_cast<const uint16_t *>(k_new) + b0 * n_new * hidden;
+        const uint16_t *vn = static_cast<const uint16_t *>(v_new) + b0 * n_new * hidden;
+        if (groups >= kAppendManyGroups) {
+            constexpr int G2 = FGQ_APPEND_GPT;
+            kv_append_kernel<G2><<<dim3((unsigned)((groups + 32 * G2 - 1) / (32 * G2))), dim3(256), 0, stream>>>(
+                kn, vn, sub, pos, (uint32_t)groups, div_n, div_h);
+        } else {
+            kv_append_kernel<1><<<dim3((unsigned)((groups + 31) / 32)), dim3(256), 0, stream>>>(
+                kn, vn, sub, pos, (uint32_t)groups, div_n, div_h);
+        }
         fgq_status s = check_launch("kv_append_kernel");
         if (s != FGQ_OK) return s;
     }
