@@ -156,9 +156,9 @@ fgq_status fgq_decode_attn_q4kv(const fgq_kv_cache *kv, const void *q_f16, int32
  *   s_j = softmax_scale * sum_d q_{hq,d} * K^_{hq/R,j,d},  j in [0, kv_len)
  *   o_d = sum_j softmax(s)_j * V^_{hq/R,j,d}
  *   q    fp16 [batch][q_heads*head_dim];  out [batch][q_heads*head_dim] in out_dtype.
- *   Requires q_heads a multiple of kv->heads (FGQ_ERR_SHAPE) and
- *   R <= FGQ_GQA_MAX_GROUP (FGQ_ERR_UNSUPPORTED); R == 1 is
- *   fgq_decode_attn_q4kv.  softmax_scale <= 0 selects 1/sqrt(head_dim); every
+ *   Requires q_heads a multiple of kv->heads (FGQ_ERR_SHAPE),
+ *   R <= FGQ_GQA_MAX_GROUP and, for R > 1, capacity * head_dim / 2 < 2^32
+ *   (FGQ_ERR_UNSUPPORTED); R == 1 is fgq_decode_attn_q4kv.  softmax_scale <= 0 selects 1/sqrt(head_dim); every
  *   sequence attends the same kv_len positions; 1 <= kv_len <= capacity.
  *   ws / ws_bytes: at least fgq_decode_attn_gqa_ws_bytes(...) bytes (may be
  *   NULL when that is 0): per-split partial softmax states.

@@ -169,6 +169,8 @@ fgq_status fgq_decode_attn_gqa_q4kv(const fgq_kv_cache *kv, const void *q_f16, i
     if (kv_len > kv->capacity) return fail(FGQ_ERR_CAPACITY, "kv_len %d > capacity %d", kv_len, kv->capacity);
     if (!std::isfinite(softmax_scale)) return fail(FGQ_ERR_INVALID_ARG, "softmax_scale is not finite");
     if ((int64_t)kv->batch * q_heads > INT32_MAX) return fail(FGQ_ERR_SHAPE, "batch * q_heads > 2^31 - 1");
+    if (q_heads != kv->heads && (int64_t)kv->capacity * (kv->head_dim / 2) > UINT32_MAX)
+        return fail(FGQ_ERR_UNSUPPORTED, "capacity %d: one head's code rows exceed 2^32 bytes", kv->capacity);
     if (kv->batch == 0) return FGQ_OK;
     if (!q_f16 || !out) return fail(FGQ_ERR_INVALID_ARG, "NULL q or out");
     if (!aligned16(q_f16) || !aligned16(out)) return fail(FGQ_ERR_ALIGN, "q/out must be 16-byte aligned");

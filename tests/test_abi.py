@@ -123,6 +123,8 @@ def test_gqa_attention_validation_and_workspace(lib):
     assert _status(lambda: a(kv, GOOD, 8, 4, 0.0, 0, 0, 0, 0, 0)) == fgq.FGQ_ERR_INVALID_ARG
     assert _status(lambda: a(_kv(head_dim=96), GOOD, 8, 4, 0.0, GOOD, 0, 0, 0, 0)) == fgq.FGQ_ERR_SHAPE
     assert _status(lambda: a(_kv(batch=0), 0, 8, 4, 0.0, 0, 0, 0, 0, 0)) == fgq.FGQ_OK
+    huge = _kv(batch=1, heads=1, head_dim=128, cap=2 ** 27)     # 2^27 positions x 64 code bytes = 2^33
+    assert _status(lambda: a(huge, GOOD, 8, 4, 0.0, GOOD, 0, 0, 0, 0)) == fgq.FGQ_ERR_UNSUPPORTED
     # few sequences and K/V heads over a long context need split states
     B, Hq, Hkv, D, L = 2, 32, 8, 128, 16384
     need = fgq.fgq_decode_attn_gqa_ws_bytes(B, Hq, Hkv, D, L)
