@@ -135,3 +135,50 @@ def test_graph_layer_step_replays_match_eager():
         h = graph_kv.host()
         for a in h:
             assert np.array_equal(h[a], eager_cache[a]), ("cache", a, rep)
+
+
+@pytest.mark.parametrize("B2,Hkv,R,L", [(2, 2, 8, 3000), (64, 32, 2, 300)])
+def test_graph_gqa_step_replays_match_eager(B2, Hkv, R, L):
+    """A grouped-query decode step (append + attention; with splits the graph
+    also holds the split merge) captured and replayed three times with eager
+    work in between: every replay equals the eager step bit for bit."""
+    gu.torch_cuda()
+    Hq, D = Hkv * R, 128
+    gu.note("graph gqa step B=%d Hkv=%d R=%d L=%d" % (B2, Hkv, R, L))
+    pk = _f16(80, B2 * L * Hkv * D).reshape(B2, L, Hkv * D)
+    pv = _f16(81, B2 * L * Hkv * D).reshape(B2, L, Hkv * D)
+    kv_e, kv_g = gu.DevKV(B2, Hkv, D, L + 1), gu.DevKV(B2, Hkv, D, L + 1)
+    kv_e.append(pk, pv, 0)
+    kv_g.append(pk, pv, 0)
+    k1 = gu.to_dev(_f16(82, B2 * Hkv * D).reshape(B2, 1, Hkv * D))
+    v1 = gu.to_dev(_f16(83, B2 * Hkv * D).reshape(B2, 1, Hkv * D))
+    q = gu.to_dev(_f16(84, B2 * Hq * D).reshape(B2, Hq * D))
+    q_other = gu.to_dev(_f16(85, B2 * Hq * D).reshape(B2, Hq * D))
+    wsb = gu.fgq.fgq_decode_attn_gqa_ws_bytes(B2, Hq, Hkv, D, L + 1)
+    ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device="cuda")
+    out = torch.empty((B2, Hq * D), dtype=torch.float32, device="cuda")
+    out_other = torch.empty_like(out)
+
+    def enqueue(kv, qq, o):
+        s = torch.cuda.current_stream().cuda_stream
+        gu.fgq.fgq_kv_append(kv.struct, k1, v1, L, 1, s)
+        gu.fgq.fgq_decode_attn_gqa_q4kv(kv.struct, qq, Hq, L + 1, 0.0, o, gu.fgq.FGQ_DTYPE_F32, ws, ws.numel(), s)
+
+    enqueue(kv_e, q, out)
+    torch.cuda.synchronize()
+    eager = gu.to_host(out)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        enqueue(kv_g, q, out)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(gu.to_host(out), eager), ("replay", rep)
+        enqueue(kv_e, q_other, out_other)     # eager work on the same stream and workspace
+        torch.cuda.synchronize()
+    h_e, h_g = kv_e.host(), kv_g.host()
+    for a in h_e:
+        assert np.array_equal(h_e[a], h_g[a]), a
