@@ -199,7 +199,8 @@ def _full_size_attention_rows(name, t, samples):
         gu.assert_close(got[b:b + 1], exp, "%s full-size seq %d" % (name, b))
 
 
-@pytest.mark.parametrize("name,t,samples", [("opt-175b", 3, (0, 77, 143)), ("long-t3", 2, (0, 31))])
+@pytest.mark.parametrize("name,t,samples", [("opt-175b", 3, (0, 77, 143)), ("long-t3", 2, (0, 31)),
+                                           ("opt-30b", 2, (0, 50, 95)), ("opt-6.7b", 32, (0, 63))])
 def test_attention_full_size_sampled(name, t, samples):
     _full_size_attention_rows(name, t, samples)
 
@@ -365,6 +366,17 @@ def _sampled_columns_check(Wt, X, g, m, slices, what):
     y = gu.gemm(X, g, m, pc, pm, K, N)
     for n0, rc, rm in refs:
         gu.assert_close(y[:, n0:n0 + 256], oracle.dequant_gemm(X, g, m, rc, rm), "%s cols %d.." % (what, n0))
+
+
+@pytest.mark.parametrize("idx", [4, 5])
+def test_gemm_opt30b_sampled_columns(idx):
+    """OPT-30B FFN weights (7168 x 28672 and 28672 x 7168) at full size with the
+    block of M = 96 = 24 x 4 rows; the oracle recomputes three 256-column slices."""
+    w = W["opt-30b"]
+    K, N = w.weights[idx]
+    gu.note("gemm opt-30b[%d] M=%d K=%d N=%d" % (idx, w.batch, K, N))
+    _sampled_columns_check(synth.weight(w, idx), synth.gemm_x(w, idx, 1), w.g, w.m,
+                           (0, N // 2 + 64, N - 256), "opt-30b[%d]" % idx)
 
 
 @pytest.mark.parametrize("idx", [0, 4, 5])
