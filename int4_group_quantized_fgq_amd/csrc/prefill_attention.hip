@@ -40,6 +40,7 @@ constexpr int kPfWaves = 8;                  // waves per workgroup
 constexpr int kPfThreads = 64 * kPfWaves;
 constexpr int kPfRows = kPfWaves * kPfWaveRows;  // query rows per workgroup
 constexpr int kPfKeys = 64;   // keys per block
+constexpr float kPfSlack = 8.0f;   // log2-domain headroom of the lazy rescale
 
 // Global loads of key block kb (K rows by 16-byte column chunks, coalesced
 // along each row; V one key per lane so that its transposed LDS writes hit
@@ -177,6 +178,12 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2)))
                     for (int r = 0; r < 4; ++r)
                         if (kb * kPfKeys + 16 * t + 4 * g + r > qi[n]) st[t][n][r] = -INFINITY;
         }
+        // Lazy rescale: the reference max m_run only moves when a row's block
+        // max passes it by more than kPfSlack (log2 units), so most blocks skip
+        // the rescale of the output.  Meanwhile p = 2^(s - m_run) <= 2^kPfSlack
+        // = 256, well inside fp16 (P enters P.V as fp16; its relative
+        // precision does not depend on the scale), and o / l is unchanged by
+        // the choice of reference.
         float corr[QT], msc[QT];
         bool moved = false;
 #pragma unroll
@@ -187,9 +194,10 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2)))
                 mb = fmaxf(mb, fmaxf(fmaxf(st[t][n][0], st[t][n][1]), fmaxf(st[t][n][2], st[t][n][3])));
             mb = fmaxf(mb, __shfl_xor(mb, 16, 64));
             mb = fmaxf(mb, __shfl_xor(mb, 32, 64));
-            const float m_new = fmaxf(m_run[n], mb);
-            corr[n] = __builtin_amdgcn_exp2f((m_run[n] - m_new) * sl2);
-            moved |= m_new != m_run[n];
+            const bool up = mb * sl2 > m_run[n] * sl2 + kPfSlack;   // false while mb = -inf (masked rows)
+            const float m_new = up ? mb : m_run[n];
+            corr[n] = up ? __builtin_amdgcn_exp2f((m_run[n] - m_new) * sl2) : 1.0f;
+            moved |= up;
             m_run[n] = m_new;
             msc[n] = m_new * sl2;
             l_run[n] *= corr[n];
