@@ -343,11 +343,12 @@ __global__ __launch_bounds__(128) void attn_merge_kernel(const float *__restrict
         static_cast<float *>(out)[(size_t)bh * D + d] = v;
 }
 
-// Token iterations per chunk: the middle setting (three waves per SIMD) when
-// a wave streams few tokens, long chunks (two waves per SIMD, more bytes in
-// flight per wave) when it streams many.
+// Token iterations per chunk: long chunks (two waves per SIMD, more bytes in
+// flight per wave) once a wave streams a few hundred tokens, the middle
+// setting (three waves per SIMD) for short ranges, where a long chunk would
+// mostly load masked positions past the end.
 constexpr int kChunkShort = 4, kChunkLong = 6;
-constexpr int kLongChunkTokens = 768;   // tokens per wave from which the long chunk is used
+constexpr int kLongChunkTokens = 256;   // tokens per wave from which the long chunk is used
 
 }  // namespace
 
