@@ -362,10 +362,15 @@ AttnPlan attn_plan(int32_t batch, int32_t heads, int32_t head_dim, int32_t kv_le
     const int tpi = 64 / (head_dim / 32);
     const int64_t bh = (int64_t)batch * heads;
     const int64_t target_waves = 8LL * 4 * kNumCU;     // ~8 waves per SIMD in flight
+    const int64_t slots = 2LL * 4 * kNumCU;            // one wave per slot at two waves per SIMD
     int n_split = 1;
     if (bh > 0 && bh < target_waves) {
         n_split = (int)((target_waves + bh - 1) / bh);
-        const int max_split = kv_len / 256 > 1 ? kv_len / 256 : 1;   // keep >= 256 tokens per split
+        // Once the pairs alone occupy every wave slot, a split pays only if each
+        // part still streams a long run (it adds a merge and a wave's setup);
+        // with fewer pairs than slots, shorter parts are worth the occupancy.
+        const int min_tok = bh >= slots ? 768 : 256;
+        const int max_split = kv_len / min_tok > 1 ? kv_len / min_tok : 1;
         if (n_split > max_split) n_split = max_split;
     }
     int per = (kv_len + n_split - 1) / n_split;
