@@ -347,7 +347,7 @@ __global__ __launch_bounds__(128) void attn_merge_kernel(const float *__restrict
 // flight per wave) once a wave streams a few hundred tokens, the middle
 // setting (three waves per SIMD) for short ranges, where a long chunk would
 // mostly load masked positions past the end.
-constexpr int kChunkShort = 4, kChunkLong = 6;
+constexpr int kChunkShort = 4, kChunkLong = 7;
 constexpr int kLongChunkTokens = 256;   // tokens per wave from which the long chunk is used
 
 }  // namespace
