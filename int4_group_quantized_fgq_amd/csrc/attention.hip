@@ -100,6 +100,7 @@ void attn_split_kernel(
     constexpr int TPI = 64 / PARTS; // tokens per wave iteration
     constexpr int G = D / 64;       // groups per token row
     constexpr int EPL = 32 / TPI;   // output elements per lane in the final reduction
+    static_assert(CH % 2 == 0, "P.V pairs token iteration it with it + CH/2");
     __shared__ float red[4][64 * 33];
 
     const int lane = threadIdx.x & 63;
@@ -347,7 +348,7 @@ __global__ __launch_bounds__(128) void attn_merge_kernel(const float *__restrict
 // flight per wave) once a wave streams a few hundred tokens, the middle
 // setting (three waves per SIMD) for short ranges, where a long chunk would
 // mostly load masked positions past the end.
-constexpr int kChunkShort = 4, kChunkLong = 7;
+constexpr int kChunkShort = 4, kChunkLong = 6;
 constexpr int kLongChunkTokens = 256;   // tokens per wave from which the long chunk is used
 
 }  // namespace
