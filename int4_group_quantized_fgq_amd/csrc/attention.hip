@@ -305,8 +305,8 @@ void attn_split_kernel(
         for (int k = 0; k < EPL; ++k) {
             if (out_f16)
                 static_cast<_Float16 *>(out)[ob + k] = (_Float16)(val[k] * inv);
-            else
-                static_cast<float *>(out)[ob + k] = val[k] * inv;
+            else   // written once, read by a later launch: keep it out of L2
+                __builtin_nontemporal_store(val[k] * inv, static_cast<float *>(out) + ob + k);
         }
     } else {
         float *wrow = ws + ((size_t)bh * n_split + split) * (D + 4);
@@ -341,7 +341,7 @@ __global__ __launch_bounds__(128) void attn_merge_kernel(const float *__restrict
     if (out_f16)
         static_cast<_Float16 *>(out)[(size_t)bh * D + d] = (_Float16)v;
     else
-        static_cast<float *>(out)[(size_t)bh * D + d] = v;
+        __builtin_nontemporal_store(v, static_cast<float *>(out) + (size_t)bh * D + d);
 }
 
 // Token iterations per chunk: long chunks (two waves per SIMD, more bytes in
