@@ -105,6 +105,14 @@ def test_attention_validation_and_workspace(lib):
     # many sequences: one split, no workspace
     assert fgq.fgq_decode_attn_ws_bytes(144, 96, 128, 544) == 0
     assert fgq.fgq_decode_attn_ws_bytes(0, 96, 128, 544) == 0
+    # the split rule: once the (sequence, head) pairs cover every wave slot
+    # (2048 on 256 CUs at two waves per SIMD), a sequence is split only into
+    # parts of >= 768 tokens; with fewer pairs, parts of >= 256 tokens
+    ws = lambda B, H, L, n: B * H * n * (128 + 4) * 4
+    assert fgq.fgq_decode_attn_ws_bytes(64, 32, 128, 530) == 0               # 2048 pairs: none
+    assert fgq.fgq_decode_attn_ws_bytes(60, 32, 128, 530) == ws(60, 32, 530, 2)
+    assert fgq.fgq_decode_attn_ws_bytes(32, 96, 128, 4128) == ws(32, 96, 4128, 3)
+    assert fgq.fgq_decode_attn_ws_bytes(96, 56, 128, 1040) == 0              # 5376 pairs, 1040 tokens
 
 
 def test_gqa_attention_validation_and_workspace(lib):
