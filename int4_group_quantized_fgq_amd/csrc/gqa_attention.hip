@@ -532,7 +532,7 @@ struct GqaPlan {
 };
 
 // Splits of the sequence: about one resident round of workgroups (two per
-// CU with one 16-head column tile, one with two), each split long enough
+// CU up to 8 query heads per K/V head, one above), each split long enough
 // that its partial state (R rows of D + 4 floats) stays small against the
 // cache bytes it reads.
 GqaPlan gqa_plan(int32_t batch, int32_t kv_heads, int32_t group, int32_t kv_len) {
@@ -540,7 +540,7 @@ GqaPlan gqa_plan(int32_t batch, int32_t kv_heads, int32_t group, int32_t kv_len)
     // enough (sequence, K/V head) pairs for two waves per SIMD: one wave each, no splits
     if (group <= 16 && items >= FGQ_GQA_WAVE_ITEMS) return {1, kv_len, 1};
     constexpr int per_round = kGqBlock * kGqWaves;
-    const int64_t target = (group <= 16 ? 2LL : 1LL) * kNumCU;
+    const int64_t target = (group <= 8 ? 2LL : 1LL) * kNumCU;   // workgroups; fewer for wide groups
     int n_split = 1;
     if (items > 0 && items < target) {
         n_split = (int)((target + items - 1) / items);
