@@ -141,7 +141,7 @@ def _full_size(w, t, samples):
         gu.assert_close(got[b:b + 1], exp, "%s full-size seq %d" % (w.name, b))
 
 
-@pytest.mark.parametrize("kv_heads,t,samples", [(8, 2, (0, 15)), (1, 1, (5,))])
+@pytest.mark.parametrize("kv_heads,t,samples", [(8, 2, (0, 15)), (2, 3, (7,)), (1, 1, (5,))])
 def test_gqa_workload_full_size_sampled(kv_heads, t, samples):
     _full_size(dataclasses.replace(W["gqa"], kv_heads=kv_heads), t, samples)
 
