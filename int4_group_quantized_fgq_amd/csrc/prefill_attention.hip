@@ -10,14 +10,16 @@
 // with q, k, v, o token-major [batch][seq][heads*head_dim].
 //
 // Design (MFMA-bound: 4*D flops per (i, j) pair, ~2 bytes per pair of HBM):
-//  * a workgroup of 8 waves takes 256 query rows of one (b, h), a wave 32
-//    (two 16-row MFMA tiles, so every K and V fragment read from LDS feeds
-//    two MFMAs);
-//    key blocks of 64 are staged in LDS for the 8 waves: K row-major, V
+//  * a wave takes 32 query rows of one (b, h) (two 16-row MFMA tiles, so
+//    every K and V fragment read from LDS feeds two MFMAs); a workgroup of 8
+//    waves (256 rows, two waves per SIMD) for short prompts, of 12 waves
+//    (384 rows, three per SIMD) for long ones, where the Q fragments move
+//    from registers to LDS to make room for the third wave;
+//    key blocks of 64 are staged in LDS by 8 of the waves: K row-major, V
 //    transposed (d-major), the next block's global loads in flight while the
 //    current one is multiplied;
 //  * scores are formed transposed, S^T = K Q^T, on v_mfma_f32_16x16x32_f16
-//    (A = K rows from LDS, B = the wave's Q fragments held in registers), so
+//    (A = K rows from LDS, B = the wave's Q fragments), so
 //    a lane's accumulators all belong to one query: the running max, the
 //    rescale of the output and the exponentials stay in the lane, with two
 //    cross-lane steps for the row max and one pair at the end for the sum;
@@ -36,9 +38,9 @@ namespace {
 
 constexpr float kPfLog2e = 1.4426950408889634f;
 constexpr int kPfWaveRows = 32;              // query rows per wave (two 16-row MFMA tiles)
-constexpr int kPfWaves = 8;                  // waves per workgroup
-constexpr int kPfThreads = 64 * kPfWaves;
-constexpr int kPfRows = kPfWaves * kPfWaveRows;  // query rows per workgroup
+constexpr int kPfLoadWaves = 8;              // waves that stage the K/V tiles
+constexpr int kPfLoadThreads = 64 * kPfLoadWaves;
+constexpr int kPfLongPrompt = 1024;          // prompts from which 12-wave workgroups are used
 constexpr int kPfKeys = 64;   // keys per block
 constexpr float kPfSlack = 8.0f;   // log2-domain headroom of the lazy rescale
 
@@ -46,7 +48,7 @@ constexpr float kPfSlack = 8.0f;   // log2-domain headroom of the lazy rescale
 // along each row; V one key per lane so that its transposed LDS writes hit
 // consecutive halves) into registers, rows past the prompt clamped to its
 // last token.
-constexpr int pf_loads(int D) { return kPfKeys * D / 8 / kPfThreads; }   // 16-byte loads per thread per tile
+constexpr int pf_loads(int D) { return kPfKeys * D / 8 / kPfLoadThreads; }   // 16-byte loads per thread per tile
 
 template <int D>
 __device__ __forceinline__ void pf_load_tile(const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
@@ -55,12 +57,12 @@ __device__ __forceinline__ void pf_load_tile(const uint16_t *__restrict__ k, con
     constexpr int KCH = D / 8;                     // 16-byte chunks per row
 #pragma unroll
     for (int p = 0; p < pf_loads(D); ++p) {
-        const int idx = p * kPfThreads + tid;
+        const int idx = p * kPfLoadThreads + tid;
         const int row = idx / KCH, ch = idx % KCH;
         int j = kb * kPfKeys + row;
         j = j < S ? j : S - 1;
         kr[p] = *reinterpret_cast<const u32x4 *>(k + base + (size_t)j * rs + 8 * ch);
-        const int key = tid & 63, vch = (tid >> 6) + kPfWaves * p;
+        const int key = tid & 63, vch = (tid >> 6) + kPfLoadWaves * p;
         int jv = kb * kPfKeys + key;
         jv = jv < S ? jv : S - 1;
         vr[p] = *reinterpret_cast<const u32x4 *>(v + base + (size_t)jv * rs + 8 * vch);
@@ -75,10 +77,10 @@ __device__ __forceinline__ void pf_store_tile(uint16_t *ks, uint16_t *vt, int ti
     constexpr int KCH = D / 8;
 #pragma unroll
     for (int p = 0; p < pf_loads(D); ++p) {
-        const int idx = p * kPfThreads + tid;
+        const int idx = p * kPfLoadThreads + tid;
         const int row = idx / KCH, ch = idx % KCH;
         *reinterpret_cast<u32x4 *>(ks + row * KS + 8 * ch) = kr[p];
-        const int key = tid & 63, vch = (tid >> 6) + kPfWaves * p;
+        const int key = tid & 63, vch = (tid >> 6) + kPfLoadWaves * p;
         uint16_t *col = vt + 8 * vch * VS + key;
         col[0 * VS] = (uint16_t)(vr[p][0] & 0xffffu);
         col[1 * VS] = (uint16_t)(vr[p][0] >> 16);
@@ -91,8 +93,8 @@ __device__ __forceinline__ void pf_store_tile(uint16_t *ks, uint16_t *vt, int ti
     }
 }
 
-template <int D>
-__global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2))) void prefill_attn_kernel(const uint16_t *__restrict__ q,
+template <int D, int NW>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW > kPfLoadWaves ? 3 : 2))) void prefill_attn_kernel(const uint16_t *__restrict__ q,
                                                            const uint16_t *__restrict__ k,
                                                            const uint16_t *__restrict__ v, int S, int H,
                                                            float sl2, void *__restrict__ out, int out_f16) {
@@ -102,10 +104,17 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2)))
     constexpr int KSTEP = D / 32;        // MFMA k-steps over d
     constexpr int NDT = D / 16;          // output d-tiles
     constexpr int QT = kPfWaveRows / 16; // query tiles per wave
+    constexpr int NTH = 64 * NW;         // threads
+    constexpr int ROWS = NW * kPfWaveRows;   // query rows per workgroup
+    // Above 8 waves the Q fragments live in LDS (read per k-step) instead of
+    // registers, which brings a wave under 168 VGPRs: three waves per SIMD
+    constexpr bool QLDS = NW > kPfLoadWaves;
+    constexpr int QS = D + 8;            // Q row stride in halves (16-byte pad)
+    __shared__ __attribute__((aligned(16))) uint16_t qs[QLDS ? ROWS * QS : 8];
     __shared__ __attribute__((aligned(16))) uint16_t ks[kPfKeys * KS];
     __shared__ __attribute__((aligned(16))) uint16_t vt[D * VS];
 
-    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 4, c = lane & 15;
     const int nqb = gridDim.x;
     const int qb = nqb - 1 - (int)blockIdx.x;      // the longest rows first
@@ -114,18 +123,31 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2)))
     const size_t base = (size_t)b * S * rs + (size_t)h * D;
 
     // ---- the wave's Q fragments (B operands): query tile n holds query
-    // q0 + 16n + c, d = 32*s + 8*g + 0..7
-    const int q0 = qb * kPfRows + wv * kPfWaveRows;
+    // q0 + 16n + c, d = 32*s + 8*g + 0..7 (rows past the prompt clamped)
+    const int q0 = qb * ROWS + wv * kPfWaveRows;
     int qi[QT];
-    f16x8 qf[QT][KSTEP];
+    f16x8 qf[QLDS ? 1 : QT][KSTEP];
 #pragma unroll
-    for (int n = 0; n < QT; ++n) {
-        qi[n] = q0 + 16 * n + c;
-        const int qic = qi[n] < S ? qi[n] : S - 1;
+    for (int n = 0; n < QT; ++n) qi[n] = q0 + 16 * n + c;
+    if constexpr (QLDS) {
+        constexpr int QCH = D / 8;
+        for (int idx = tid; idx < ROWS * QCH; idx += NTH) {
+            const int row = idx / QCH, ch = idx % QCH;
+            int qr = qb * ROWS + row;
+            qr = qr < S ? qr : S - 1;
+            *reinterpret_cast<u32x4 *>(qs + row * QS + 8 * ch) =
+                *reinterpret_cast<const u32x4 *>(q + base + (size_t)qr * rs + 8 * ch);
+        }
+    } else {
 #pragma unroll
-        for (int s = 0; s < KSTEP; ++s)
-            qf[n][s] = *reinterpret_cast<const f16x8 *>(q + base + (size_t)qic * rs + 32 * s + 8 * g);
+        for (int n = 0; n < QT; ++n) {
+            const int qic = qi[n] < S ? qi[n] : S - 1;
+#pragma unroll
+            for (int s = 0; s < KSTEP; ++s)
+                qf[n][s] = *reinterpret_cast<const f16x8 *>(q + base + (size_t)qic * rs + 32 * s + 8 * g);
+        }
     }
+    const uint16_t *qw = qs + (wv * kPfWaveRows + c) * QS + 8 * g;   // this lane's Q in LDS (QLDS)
 
     u32x4 kr[NP], vr[NP];
     f32x4 o[NDT][QT];
@@ -141,30 +163,49 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2)))
     }
 
     // key blocks holding a key <= the workgroup's last query (and < S)
-    const int q_last = min(qb * kPfRows + kPfRows, S) - 1;
+    const int q_last = min(qb * ROWS + ROWS, S) - 1;
     const int kb_last = q_last / kPfKeys;
     const int wave_q_last = q0 + kPfWaveRows - 1;
-    pf_load_tile<D>(k, v, base, rs, S, 0, tid, kr, vr);
+    const bool loader = NW == kPfLoadWaves || wv < kPfLoadWaves;   // this wave stages K/V tiles
+    if (loader) pf_load_tile<D>(k, v, base, rs, S, 0, tid, kr, vr);
     for (int kb = 0; kb <= kb_last; ++kb) {
         __syncthreads();                           // every wave is done with the previous tile
-        pf_store_tile<D, KS, VS>(ks, vt, tid, kr, vr);
+        if (loader) pf_store_tile<D, KS, VS>(ks, vt, tid, kr, vr);
         __syncthreads();
-        if (kb < kb_last) pf_load_tile<D>(k, v, base, rs, S, kb + 1, tid, kr, vr);   // in flight during the MFMAs
+        if (kb < kb_last && loader) pf_load_tile<D>(k, v, base, rs, S, kb + 1, tid, kr, vr);   // in flight during the MFMAs
         if (kb * kPfKeys > wave_q_last) continue;  // every key of the block is past this wave's queries
 
         // ---- S^T = K Q^T: st[t][n] holds keys 16t + 4g + r (r = 0..3) of query tile n
         f32x4 st[4][QT];
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
+        for (int t = 0; t < 4; ++t)
 #pragma unroll
             for (int n = 0; n < QT; ++n) st[t][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if constexpr (QLDS) {
+            // k-step outer: only one k-step of Q fragments is held at a time
 #pragma unroll
             for (int s = 0; s < KSTEP; ++s) {
-                const f16x8 a = *reinterpret_cast<const f16x8 *>(ks + (16 * t + c) * KS + 32 * s + 8 * g);
+                f16x8 qs_s[QT];
 #pragma unroll
-                for (int n = 0; n < QT; ++n)
-                    st[t][n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, qf[n][s], st[t][n], 0, 0, 0);
+                for (int n = 0; n < QT; ++n) qs_s[n] = *reinterpret_cast<const f16x8 *>(qw + 16 * n * QS + 32 * s);
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    const f16x8 a = *reinterpret_cast<const f16x8 *>(ks + (16 * t + c) * KS + 32 * s + 8 * g);
+#pragma unroll
+                    for (int n = 0; n < QT; ++n)
+                        st[t][n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, qs_s[n], st[t][n], 0, 0, 0);
+                }
             }
+        } else {
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+#pragma unroll
+                for (int s = 0; s < KSTEP; ++s) {
+                    const f16x8 a = *reinterpret_cast<const f16x8 *>(ks + (16 * t + c) * KS + 32 * s + 8 * g);
+#pragma unroll
+                    for (int n = 0; n < QT; ++n)
+                        st[t][n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, qf[QLDS ? 0 : n][s], st[t][n], 0, 0, 0);
+                }
         }
         // ---- causal mask (only blocks that reach past the wave's first query
         // need it), running max on the raw scores (the scale is positive);
@@ -266,15 +307,24 @@ fgq_status launch_prefill_attn(const void *q, const void *k, const void *v, int3
                                int32_t heads, int32_t head_dim, float scale, void *out, int32_t out_dtype,
                                hipStream_t stream) {
     if (batch == 0 || seq == 0 || heads == 0) return FGQ_OK;
-    const dim3 grid((unsigned)((seq + kPfRows - 1) / kPfRows), (unsigned)heads, (unsigned)batch);
     const float sl2 = scale * kPfLog2e;
     const int f16 = out_dtype == FGQ_DTYPE_F16;
     const uint16_t *qh = static_cast<const uint16_t *>(q), *kh = static_cast<const uint16_t *>(k),
                    *vh = static_cast<const uint16_t *>(v);
-    if (head_dim == 128)
-        prefill_attn_kernel<128><<<grid, dim3(kPfThreads), 0, stream>>>(qh, kh, vh, seq, heads, sl2, out, f16);
-    else
-        prefill_attn_kernel<64><<<grid, dim3(kPfThreads), 0, stream>>>(qh, kh, vh, seq, heads, sl2, out, f16);
+    // 12-wave workgroups (384 rows, three waves per SIMD) once the prompt is
+    // long enough that the last, partly filled block of rows costs little;
+    // 8 waves (256 rows, two per SIMD) below
+    const bool wide = seq >= kPfLongPrompt;
+    const int rows = (wide ? 12 : 8) * kPfWaveRows;
+    const dim3 grid((unsigned)((seq + rows - 1) / rows), (unsigned)heads, (unsigned)batch);
+#define FGQ_PF_LAUNCH(D, NW) \
+    prefill_attn_kernel<D, NW><<<grid, dim3(64 * NW), 0, stream>>>(qh, kh, vh, seq, heads, sl2, out, f16)
+    if (head_dim == 128) {
+        if (wide) FGQ_PF_LAUNCH(128, 12); else FGQ_PF_LAUNCH(128, 8);
+    } else {
+        if (wide) FGQ_PF_LAUNCH(64, 12); else FGQ_PF_LAUNCH(64, 8);
+    }
+#undef FGQ_PF_LAUNCH
     return check_launch("prefill_attn_kernel");
 }
 

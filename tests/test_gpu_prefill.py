@@ -1,6 +1,7 @@
 """GPU parity of prefill attention over fp16 (through the C ABI) against the
 oracle on the same seeded inputs: ragged prompt lengths that span several
-64-row query blocks and 64-key blocks, both head sizes, fp16 output, the
+query blocks (256 rows below 1024 tokens, 384 from there) and 64-key blocks,
+both head sizes, fp16 output, the
 scale argument, a workload-shaped launch (OPT-175B heads, prompt 512) on
 sampled rows, and bitwise repeatability.  Bar: max-abs 1e-2 and rel-L2 1e-3.
 """
@@ -38,7 +39,8 @@ def _gpu(q, k, v, H, scale=0.0, out_f16=False):
 
 
 @pytest.mark.parametrize("B,s,H,D", [(1, 1, 1, 64), (2, 37, 3, 64), (2, 64, 2, 128), (1, 65, 2, 128),
-                                     (2, 200, 3, 128), (1, 513, 2, 128), (3, 130, 4, 64)])
+                                     (2, 200, 3, 128), (1, 513, 2, 128), (3, 130, 4, 64),
+                                     (1, 1024, 1, 64), (1, 1100, 2, 128)])
 def test_prefill_against_oracle(B, s, H, D):
     q, k, v = _qkv(B, s, H, D, 0)
     gu.note("prefill B=%d s=%d H=%d D=%d" % (B, s, H, D))
@@ -69,6 +71,20 @@ def test_prefill_workload_shape_sampled_rows():
     for r0, r1 in ((0, 3), (255, 257), (s - 3, s)):
         exp = oracle.prefill_attn(q, k, v, H, rows=(r0, r1))
         gu.assert_close(got[:, r0:r1], exp[:, r0:r1], "opt-175b rows %d..%d" % (r0, r1 - 1))
+
+
+def test_prefill_long_prompt_sampled_rows():
+    """OPT-175B heads at a 2048-token prompt (the 12-wave launch): the first,
+    middle and last rows of each sequence, every head, against the oracle."""
+    w = synth.WORKLOADS["opt-175b"]
+    B, s, H = 1, 2048, w.heads
+    q, k, v = _qkv(B, s, H, w.head_dim, 30)
+    gu.note("prefill long prompt B=%d s=%d" % (B, s))
+    got = _gpu(q, k, v, H)
+    assert np.all(np.isfinite(got))
+    for r0, r1 in ((0, 2), (383, 386), (1151, 1153), (s - 2, s)):
+        exp = oracle.prefill_attn(q, k, v, H, rows=(r0, r1))
+        gu.assert_close(got[:, r0:r1], exp[:, r0:r1], "long prompt rows %d..%d" % (r0, r1 - 1))
 
 
 def test_prefill_repeatable_bitwise():
