@@ -2,21 +2,31 @@
 """Decode-step benchmark of the int4 group-wise (g=64) compressed layer.
 
 One step = one decode step of one OPT-shaped layer for the whole block of
-B = g*m sequences, entirely in HBM:
-  fgq_kv_append (the step's K and V rows into the compressed cache)
-  fgq_decode_attn_q4kv (attend over prompt + t positions)
-  fgq_dequant_gemm x 4 (Wq|Wk|Wv as one [h][3h] matrix, since the three
-  projections share their input; Wout; W1; W2), one weight read per block.
+B = g*m sequences, entirely in HBM, with the layer's real data flow (each
+launch reads what the previous one wrote, fp16 hand-offs):
+  Y  = X0 * [Wq|Wk|Wv]               fgq_dequant_gemm (one [h][3h] launch: the
+                                      three projections share their input)
+  fgq_kv_append_ld                    K and V of Y into the compressed cache
+  A  = fgq_decode_attn_q4kv_ld        q of Y over prompt + t positions
+  A * Wout, then * W1, then * W2      fgq_dequant_gemm x 3
+The weights are read once per block; the layer's norms, residual sums and
+FFN activation are not part of the compressed path and are not applied.
 Decode step t cycles through 1..32 (the pages' 32 generated tokens), so the
-attended length runs from prompt+1 to prompt+32.  Inputs are seeded synthetic
-draws (synth), already resident in HBM when the timed region starts.
+attended length runs from prompt+1 to prompt+32.  Inputs are seeded
+synthetic draws (synth), already resident in HBM when the timed region
+starts.
 
-Prints one JSON line.  The steps are timed twice: an eager pass with HIP
-events recorded on the launch stream around every call (the per-kernel
-durations and the roofline come from it), then the same steps replayed as HIP
-graphs, one per (decode step, layer instance), which gives value and
-ms_per_step (--no-graph: the eager pass gives them).  The CPU baseline is the
-oracle on a bounded sample of one step.
+Prints one JSON line.  Each timed pass starts after a warm-up of at least
+--warmup steps and at least --min-warmup-ms of steady work (the clock of a
+short burst runs lower).  The steps are timed twice: an eager pass with HIP
+events recorded on the launch stream around every call (per-kernel
+durations and the rooflines), then the same steps replayed as HIP graphs,
+one per (decode step, layer instance), which gives value and ms_per_step
+(--no-graph: the eager pass gives them).  The GEMM runs over the offline
+packed weight layout (--gemm-layout packed, the default) or straight from
+the quantiser's codes (canonical); both are timed.  The other workloads get
+a graph-replayed step each (side entries), and the CPU baseline is the
+oracle on a bounded sample of the step.
 """
 from __future__ import annotations
 
@@ -24,6 +34,7 @@ import argparse
 import json
 import os
 import sys
+import threading
 import time
 
 import numpy as np
@@ -38,6 +49,7 @@ from int4_group_quantized_fgq_amd import accounting as acc  # noqa: E402
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 MFMA_F16_PEAK_TFLOPS = 2516.6  # MI355X dense fp16 matrix peak, TFLOP/s
 METRIC = "q4-KV decode attn + dequant-GEMM: tokens/s/layer, % HBM BW, % MFMA peak"
+SIDE_CONFIGS = ("tiny", "opt-6.7b", "opt-30b", "opt-175b", "long-t3")
 
 
 def log(msg: str) -> None:
@@ -49,10 +61,17 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=96)
     ap.add_argument("--warmup", type=int, default=32)
+    ap.add_argument("--min-warmup-ms", type=float, default=400.0,
+                    help="each timed pass starts after at least this much warm-up work")
     ap.add_argument("--config", default="opt-175b", choices=sorted(synth.WORKLOADS))
+    ap.add_argument("--gemm-layout", default="packed", choices=("packed", "canonical"),
+                    help="weight layout of the headline step (the other one is timed beside it)")
     ap.add_argument("--rotate", type=int, default=0,
                     help="layer instances cycled through (0: at least 3, and enough to exceed the 256 MB "
                          "last-level cache three times over)")
+    ap.add_argument("--no-side-configs", action="store_true", help="skip the other workloads' step lines")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the lines beside the step (prefill, bulk append, top-K, grouped-query, streaming)")
     ap.add_argument("--no-stream", action="store_true",
                     help="skip the weight-streaming measurement (packed weights from pinned host memory)")
     ap.add_argument("--no-graph", action="store_true",
@@ -72,6 +91,9 @@ def parse():
     ap.add_argument("--summarize-pmc", nargs=4, metavar=("KERNEL_FETCH", "KERNEL_WRITE", "COPY_FETCH", "COPY_WRITE"),
                     help="only summarise four rocprofv3 --pmc output folders (FETCH_SIZE / WRITE_SIZE of the "
                          "bench and of --calibrate-copy) into the HBM-traffic profile text")
+    ap.add_argument("--summarize-counters", nargs="+", metavar="DIR",
+                    help="only summarise rocprofv3 --pmc folders of this bench (any mix of SQ/GRBM counters) "
+                         "into per-kernel unit-utilisation figures")
     ap.add_argument("--kernel", default="dq_gemm_kernel", help="kernel summarised by --summarize-pmc")
     ap.add_argument("--summarize-trace", metavar="DIR",
                     help="only summarise a rocprofv3 --kernel-trace --stats output folder of this bench: the "
@@ -201,25 +223,6 @@ def calibrate_copy(torch, mib: int) -> None:
                       "bytes_written_per_copy": mib * 2 ** 20}), flush=True)
 
 
-class Layer:
-    """One layer instance: packed weights and a compressed KV cache in HBM."""
-
-    def __init__(self, torch, fgq, w, inst, host_weights, prompt_chunks):
-        B, H, D, cap = w.batch, w.heads, w.head_dim, w.capacity
-        dev = "cuda"
-        # zero-filled: a position not yet appended reconstructs to 0 (min 0, step 0)
-        self.k_codes = torch.zeros((B, H, cap, D // 2), dtype=torch.uint8, device=dev)
-        self.v_codes = torch.zeros_like(self.k_codes)
-        self.k_meta = torch.zeros((B, H, cap, D // 64), dtype=torch.int32, device=dev)
-        self.v_meta = torch.zeros_like(self.k_meta)
-        self.kv = fgq.kv_struct(self.k_codes, self.v_codes, self.k_meta, self.v_meta, B, H, D, cap)
-        for b0, nb, kd, vd in prompt_chunks:
-            sub = fgq.kv_struct(self.k_codes[b0:b0 + nb], self.v_codes[b0:b0 + nb], self.k_meta[b0:b0 + nb],
-                                self.v_meta[b0:b0 + nb], nb, H, D, cap)
-            fgq.fgq_kv_append(sub, kd, vd, 0, w.prompt)
-        self.packed = [(pc.clone(), pm.clone()) for pc, pm in host_weights]
-
-
 def launch_plan(w):
     """The step's GEMM launches as (name, K, N, weight indices).  Weights whose
     projections read the same input (Wq, Wk, Wv of an OPT layer: the first
@@ -234,76 +237,563 @@ def launch_plan(w):
     return [("w%d" % i, K, N, (i,)) for i, (K, N) in enumerate(ws)]
 
 
-def build_weights(torch, fgq, w):
-    """Quantise and pack every weight of the layer once (offline step)."""
-    out = []
-    for name, K, N, idx in launch_plan(w):
+def layer_input(w, t: int) -> np.ndarray:
+    """The layer input of decode step t: fp16 [B][hidden] ~ N(0, 1)."""
+    key = synth.stream_key(w.cid, synth.T_GEMM_X, 0, t)
+    return synth.to_f16(synth.normal(key, w.batch * w.hidden)).reshape(w.batch, w.hidden)
+
+
+def rotation(w, layouts) -> int:
+    """Layer instances cycled through: at least 3, and enough that one cycle
+    moves three times the 256 MB last-level cache (capped at 8)."""
+    per_layer = acc.packed_bytes(sum(K * N for K, N in w.weights)) * len(layouts) + \
+        2 * acc.packed_bytes(w.batch * w.hidden * w.capacity)
+    return max(3, min(8, int(np.ceil(3 * 256e6 / per_layer)))), per_layer
+
+
+class Chain:
+    """R instances of one layer of workload w in HBM (the weights in each
+    requested layout, a compressed cache holding the prompt) and the
+    buffers of the chained decode step.  Instance 0 is built from the
+    seeded draws; the others are device copies of it (separate memory, so
+    no cache level serves one instance's bytes to the next)."""
+
+    def __init__(self, torch, fgq, w, layouts, R):
+        self.torch, self.fgq, self.w, self.R = torch, fgq, w, R
+        B, H, D, h, cap = w.batch, w.heads, w.head_dim, w.hidden, w.capacity
+        dev = "cuda"
+        self.plan = launch_plan(w)
+        self.opt = len(self.plan) == 4 and self.plan[0][0] == "qkv"
         t0 = time.time()
-        wd = torch.cat([torch.from_numpy(synth.weight(w, i)).to("cuda") for i in idx], dim=1).contiguous()
-        codes = torch.empty((K, N // 2), dtype=torch.uint8, device="cuda")
-        meta = torch.empty((K, N // 64), dtype=torch.int32, device="cuda")
-        fgq.fgq_quantize_g64(wd, K, N, N, codes, meta)
-        pc = torch.empty(K * N // 8, dtype=torch.int32, device="cuda")
-        pm = torch.empty(fgq.fgq_pack_weight_meta_words(K, N), dtype=torch.int32, device="cuda")
-        fgq.fgq_pack_weight_g64(codes, meta, K, N, pc, pm)
+        base = []
+        for name, K, N, idx in self.plan:
+            wd = torch.cat([torch.from_numpy(synth.weight(w, i)).to(dev) for i in idx], dim=1).contiguous()
+            codes = torch.empty((K, N // 2), dtype=torch.uint8, device=dev)
+            meta = torch.empty((K, N // 64), dtype=torch.int32, device=dev)
+            fgq.fgq_quantize_g64(wd, K, N, N, codes, meta)
+            entry = {"canonical": (codes, meta)}
+            if "packed" in layouts:
+                pc = torch.empty(K * N // 8, dtype=torch.int32, device=dev)
+                pm = torch.empty(fgq.fgq_pack_weight_meta_words(K, N), dtype=torch.int32, device=dev)
+                fgq.fgq_pack_weight_g64(codes, meta, K, N, pc, pm)
+                entry["packed"] = (pc, pm)
+            if "canonical" not in layouts:
+                del entry["canonical"]
+            torch.cuda.synchronize()
+            del wd
+            base.append(entry)
+        self.weights = [base] + [[{k: (a.clone(), b.clone()) for k, (a, b) in e.items()} for e in base]
+                                 for _ in range(R - 1)]
+        # caches: zero-filled (a position not yet appended reconstructs to 0)
+        self.caches = []
+        k0 = torch.zeros((B, H, cap, D // 2), dtype=torch.uint8, device=dev)
+        v0 = torch.zeros_like(k0)
+        km0 = torch.zeros((B, H, cap, D // 64), dtype=torch.int32, device=dev)
+        vm0 = torch.zeros_like(km0)
+        for b0 in range(0, B, 8):
+            nb = min(8, B - b0)
+            sub = fgq.kv_struct(k0[b0:b0 + nb], v0[b0:b0 + nb], km0[b0:b0 + nb], vm0[b0:b0 + nb], nb, H, D, cap)
+            kd = torch.from_numpy(synth.prompt_kv(w, "k", b0=b0, nb=nb)).to(dev)
+            vd = torch.from_numpy(synth.prompt_kv(w, "v", b0=b0, nb=nb)).to(dev)
+            fgq.fgq_kv_append(sub, kd, vd, 0, w.prompt)
+            torch.cuda.synchronize()
+            del kd, vd
+        for r in range(R):
+            arrs = (k0, v0, km0, vm0) if r == 0 else tuple(a.clone() for a in (k0, v0, km0, vm0))
+            self.caches.append((arrs, fgq.kv_struct(*arrs, B, H, D, cap)))
+        # inputs of the decode steps
+        self.inp = []
+        for t in range(1, w.steps + 1):
+            if self.opt:
+                self.inp.append({"x0": torch.from_numpy(layer_input(w, t)).to(dev)})
+            else:
+                self.inp.append({"k": torch.from_numpy(synth.step_kv(w, "k", t)).to(dev),
+                                 "v": torch.from_numpy(synth.step_kv(w, "v", t)).to(dev),
+                                 "q": torch.from_numpy(synth.step_q(w, t)).to(dev)})
+        f16 = torch.float16
+        self.qkv = torch.empty((B, 3 * h), dtype=f16, device=dev) if self.opt else None
+        self.attn = torch.empty((B, h), dtype=f16 if self.plan else torch.float32, device=dev)
+        self.ys = [torch.empty((B, N), dtype=f16, device=dev) for _, _, N, _ in self.plan]
+        aws = max(fgq.fgq_decode_attn_ws_bytes(B, H, D, L) for L in range(w.prompt + 1, cap + 1))
+        gws = max([fgq.fgq_dequant_gemm_ws_bytes(B, K, N) for _, K, N, _ in self.plan] + [0])
+        self.aws = torch.empty(max(aws, 16), dtype=torch.uint8, device=dev)
+        self.gws = torch.empty(max(gws, 16), dtype=torch.uint8, device=dev)
+        if self.opt:
+            self.ops = ["gemm_qkv", "append", "attention", "gemm_out", "gemm_ffn1", "gemm_ffn2"]
+        else:
+            self.ops = ["append", "attention"] + ["gemm_" + p[0] for p in self.plan]
         torch.cuda.synchronize()
-        del wd, codes, meta
-        out.append((pc, pm))
-        log("weight %s (%dx%d) quantised+packed in %.1fs" % (name, K, N, time.time() - t0))
+        log("%s: %d layer instance(s) ready in %.1fs" % (w.name, R, time.time() - t0))
+
+    def gemm(self, inst, wi, layout, x, y, sh):
+        w, fgq = self.w, self.fgq
+        _, K, N, _ = self.plan[wi]
+        a, b = self.weights[inst][wi][layout]
+        f = fgq.fgq_dequant_gemm if layout == "canonical" else fgq.fgq_dequant_gemm_packed
+        f(x, w.g, w.m, K, N, a, b, y, fgq.FGQ_DTYPE_F16, self.gws, self.gws.numel(), sh)
+
+    def enqueue(self, i, layout, sh, ev=None, stream=None):
+        """Decode step i % steps + 1 on layer instance i % R; with ev, HIP
+        events are recorded on `stream` around every launch."""
+        w, fgq = self.w, self.fgq
+        t = i % w.steps + 1
+        inst = i % self.R
+        d = self.inp[t - 1]
+        kv = self.caches[inst][1]
+        h = w.hidden
+        L = w.prompt + t
+        n = [0]
+
+        def rec():
+            if ev is not None:
+                ev[n[0]].record(stream)
+                n[0] += 1
+        rec()
+        if self.opt:
+            self.gemm(inst, 0, layout, d["x0"], self.qkv, sh)
+            rec()
+            fgq.fgq_kv_append_ld(kv, self.qkv[:, h:2 * h], self.qkv[:, 2 * h:], 3 * h, L - 1, 1, sh)
+            rec()
+            fgq.fgq_decode_attn_q4kv_ld(kv, self.qkv, 3 * h, L, 0.0, self.attn, fgq.FGQ_DTYPE_F16, self.aws,
+                                        self.aws.numel(), sh)
+            rec()
+            x = self.attn
+            for wi in (1, 2, 3):
+                self.gemm(inst, wi, layout, x, self.ys[wi], sh)
+                x = self.ys[wi]
+                rec()
+        else:
+            fgq.fgq_kv_append(kv, d["k"], d["v"], L - 1, 1, sh)
+            rec()
+            fgq.fgq_decode_attn_q4kv(kv, d["q"], L, 0.0, self.attn,
+                                     fgq.FGQ_DTYPE_F16 if self.plan else fgq.FGQ_DTYPE_F32, self.aws,
+                                     self.aws.numel(), sh)
+            rec()
+            x = self.attn
+            for wi in range(len(self.plan)):
+                self.gemm(inst, wi, layout, x, self.ys[wi], sh)
+                x = self.ys[wi]
+                rec()
+
+    def free(self):
+        del self.weights, self.caches, self.inp, self.qkv, self.attn, self.ys, self.aws, self.gws
+        self.torch.cuda.empty_cache()
+
+
+class ClockSampler:
+    """Samples the GPU's current graphics clock (MHz, via torch/amdsmi) every
+    few ms from a background thread while a timed region runs."""
+
+    def __init__(self, torch):
+        self.torch, self.samples, self._stop = torch, [], threading.Event()
+        try:
+            torch.cuda.clock_rate(0)
+            self.ok = True
+        except Exception:   # no SMI library on this machine
+            self.ok = False
+
+    def _run(self):
+        while not self._stop.is_set():
+            try:
+                self.samples.append(float(self.torch.cuda.clock_rate(0)))
+            except Exception:
+                return
+            time.sleep(0.002)
+
+    def __enter__(self):
+        if self.ok:
+            self._thr = threading.Thread(target=self._run, daemon=True)
+            self._thr.start()
+        return self
+
+    def __exit__(self, *a):
+        self._stop.set()
+        if self.ok:
+            self._thr.join()
+
+    def summary(self):
+        s = [v for v in self.samples if v > 0]
+        if not s:
+            return None
+        return {"median_MHz": float(np.median(s)), "min_MHz": float(np.min(s)), "max_MHz": float(np.max(s)),
+                "samples": len(s)}
+
+
+def warm_up(torch, run, first: int, min_steps: int, min_ms: float) -> tuple:
+    """Runs steps first, first+1, ... (in batches of 8, synchronising after
+    each) until at least min_steps ran and at least min_ms of wall time
+    passed; returns (steps run, ms)."""
+    t0 = time.perf_counter()
+    n = 0
+    while n < min_steps or (time.perf_counter() - t0) * 1e3 < min_ms:
+        for _ in range(8):
+            run(first + n)
+            n += 1
+        torch.cuda.synchronize()
+    return n, (time.perf_counter() - t0) * 1e3
+
+
+def eager_pass(torch, ch, layout, steps, warmup, min_ms, first=0):
+    """Warm-up, then `steps` eager steps with HIP events on the launch stream
+    around every launch; returns per-op ms, the total ms, the decode steps
+    timed and the warm-up actually run."""
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+    nw, wms = warm_up(torch, lambda i: ch.enqueue(i, layout, sh), first, warmup, min_ms)
+    n_ev = len(ch.ops) + 1
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(steps)]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(steps):
+        ch.enqueue(first + nw + i, layout, sh, ev=events[i], stream=stream)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    op_ms = {o: 0.0 for o in ch.ops}
+    for ev in events:
+        for j, o in enumerate(ch.ops):
+            op_ms[o] += ev[j].elapsed_time(ev[j + 1])
+    ts = [(first + nw + i) % ch.w.steps + 1 for i in range(steps)]
+    return {"op_ms": op_ms, "total_ms": start.elapsed_time(stop), "ts": ts, "warmup_steps": nw,
+            "warmup_ms": wms}
+
+
+def graph_pass(torch, ch, layout, steps, warmup, min_ms):
+    """The same steps captured as HIP graphs (one per decode step and layer
+    instance, through the same C-ABI calls on a capture stream) and replayed;
+    returns the timed ms, the warm-up run and the clock samples."""
+    stream = torch.cuda.current_stream()
+    cap = torch.cuda.Stream()      # capture needs a stream other than the default one
+    graphs = {}
+    n_keys = int(np.lcm(ch.w.steps, ch.R))
+    for i in range(n_keys):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=cap):
+            ch.enqueue(i, layout, cap.cuda_stream)
+        graphs[i] = g
+    torch.cuda.synchronize()
+    nw, wms = warm_up(torch, lambda i: graphs[i % n_keys].replay(), 0, warmup, min_ms)
+    g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    clock = ClockSampler(torch)
+    torch.cuda.synchronize()
+    with clock:
+        wall0 = time.perf_counter()
+        g0.record(stream)
+        for i in range(steps):
+            graphs[(nw + i) % n_keys].replay()
+        g1.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - wall0
+    ms = g0.elapsed_time(g1)
+    ts = [(nw + i) % ch.w.steps + 1 for i in range(steps)]
+    del graphs
+    return {"total_ms": ms, "wall_s": wall, "ts": ts, "warmup_steps": nw, "warmup_ms": wms,
+            "clock": clock.summary(), "graphs": n_keys}
+
+
+def kernel_lines(ch, ep, steps) -> dict:
+    """Per-launch durations and rates of one eager pass."""
+    w = ch.w
+    B, h = w.batch, w.hidden
+    op = ep["op_ms"]
+    ts = ep["ts"]
+    out = {}
+    attn_bytes = sum(acc.attention_bytes(B, h, w.kv_len(t), out_bytes=2 if ch.plan else 4) for t in ts)
+    gbs = attn_bytes / (op["attention"] * 1e-3) / 1e9
+    out["append"] = {"us_per_launch": 1e3 * op["append"] / steps,
+                     "GB_per_s": steps * acc.append_bytes(B, h) / (op["append"] * 1e-3) / 1e9}
+    out["attention"] = {"us_per_launch": 1e3 * op["attention"] / steps, "GB_per_s": gbs,
+                        "frac_hbm_peak": gbs / HBM_PEAK_GBS,
+                        "TFLOP_per_s": sum(acc.attention_flops(B, h, w.kv_len(t)) for t in ts) /
+                        (op["attention"] * 1e-3) / 1e12}
+    for name, K, N, _ in ch.plan:
+        ms = op["gemm_" + name]
+        f = steps * acc.gemm_flops(B, K, N)
+        by = steps * acc.gemm_bytes(B, K, N, y_bytes=2)
+        out["gemm_%s_%dx%d" % (name, K, N)] = {
+            "us_per_launch": 1e3 * ms / steps, "TFLOP_per_s": f / (ms * 1e-3) / 1e12,
+            "frac_mfma_peak": f / (ms * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS,
+            "GB_per_s": by / (ms * 1e-3) / 1e9, "frac_hbm_peak": by / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
     return out
 
 
-def prompt_chunks(torch, w, chunk=8):
-    for b0 in range(0, w.batch, chunk):
-        nb = min(chunk, w.batch - b0)
-        kd = torch.from_numpy(synth.prompt_kv(w, "k", b0=b0, nb=nb)).to("cuda")
-        vd = torch.from_numpy(synth.prompt_kv(w, "v", b0=b0, nb=nb)).to("cuda")
-        yield b0, nb, kd, vd
+def gemm_totals(ch, ep, steps):
+    """All GEMM launches of the eager pass together: ms, TFLOP/s, GB/s."""
+    w = ch.w
+    ms = sum(ep["op_ms"]["gemm_" + p[0]] for p in ch.plan)
+    fl = steps * sum(acc.gemm_flops(w.batch, K, N) for _, K, N, _ in ch.plan)
+    by = steps * sum(acc.gemm_bytes(w.batch, K, N, y_bytes=2) for _, K, N, _ in ch.plan)
+    return ms, (fl / (ms * 1e-3) / 1e12 if ms else 0.0), (by / (ms * 1e-3) / 1e9 if ms else 0.0)
+
+
+def side_config_line(torch, fgq, name, layout, args) -> dict:
+    """A graph-replayed chained step of another workload and its per-launch
+    rates (one full generation of 32 decode steps timed)."""
+    w = synth.WORKLOADS[name]
+    R, per_layer = rotation(w, (layout,))
+    ch = Chain(torch, fgq, w, (layout,), R)
+    steps = 32
+    ep = eager_pass(torch, ch, layout, steps, 8, args.min_warmup_ms)
+    line = {"workload": w.name, "batch": w.batch, "heads_x_head_dim": "%dx%d" % (w.heads, w.head_dim),
+            "prompt": w.prompt, "layer_instances": R, "gemm_layout": layout, "steps_timed": steps,
+            "eager_ms_per_step": ep["total_ms"] / steps}
+    if not args.no_graph:
+        gp = graph_pass(torch, ch, layout, steps, 8, args.min_warmup_ms)
+        line["ms_per_step"] = gp["total_ms"] / steps
+        line["gpu_clock"] = gp["clock"]
+    else:
+        line["ms_per_step"] = ep["total_ms"] / steps
+    line["tokens_per_s_per_layer"] = w.batch / (line["ms_per_step"] * 1e-3)
+    if w.name == "tiny":
+        line["us_per_step"] = 1e3 * line["ms_per_step"]
+    line["kernels"] = kernel_lines(ch, ep, steps)
+    if ch.plan:
+        ms, tf, gbs = gemm_totals(ch, ep, steps)
+        line["gemm_all"] = {"TFLOP_per_s": tf, "frac_mfma_peak": tf / MFMA_F16_PEAK_TFLOPS, "GB_per_s": gbs,
+                            "frac_hbm_peak": gbs / HBM_PEAK_GBS}
+    ch.free()
+    del ch
+    torch.cuda.empty_cache()
+    return line
+
+
+def cpu_info() -> dict:
+    """Host CPU model, sockets and threads (lscpu), for the baseline line."""
+    import subprocess
+    info = {}
+    try:
+        out = subprocess.run(["lscpu"], stdout=subprocess.PIPE, stderr=subprocess.DEVNULL, text=True).stdout
+        for line in out.splitlines():
+            k, _, v = line.partition(":")
+            if k.strip() in ("Model name", "Socket(s)", "Thread(s) per core", "Core(s) per socket", "CPU(s)"):
+                info[k.strip()] = v.strip()
+    except OSError:
+        pass
+    info["threads_available"] = len(os.sched_getaffinity(0))
+    return info
+
+
+def _omp_threads(n: int) -> None:
+    import ctypes
+    try:
+        ctypes.CDLL("libgomp.so.1").omp_set_num_threads(int(n))
+    except OSError:
+        pass
 
 
 def cpu_baseline(w, args):
-    """The oracle (never tuned) on a bounded sample of one decode step (t = 1),
-    scaled to the whole step: a few sequences of append and attention, a few
-    256-column slices of every weight GEMM with all g*m rows."""
+    """The oracle (never tuned) on a bounded sample of the chained decode step
+    at t = 1 and t = 32: append + attention on a few sequences, every weight
+    GEMM on a 256-column slice with all g*m rows; each part scaled to the
+    full step.  Also the OPT-6.7B attention of one step on a single core."""
     import oracle
     S = min(args.cpu_sample_seqs, w.batch)
-    H, D = w.heads, w.head_dim
-    t = 1
-    secs = {}
-    # append + attention on S sequences (their prompt is appended untimed)
+    H, D, h = w.heads, w.head_dim, w.hidden
+    cores = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
+    _omp_threads(cores)
+    # the GEMM slices do not depend on t: time them once per t anyway (same work)
+    slices = []
+    for i, (K, N) in enumerate(w.weights):
+        ncol = min(args.cpu_sample_cols, N)
+        c, m = oracle.quantize_g64(np.ascontiguousarray(synth.weight(w, i)[:, :ncol]))
+        slices.append((i, K, N, ncol, c, m))
     ref = oracle.KVCache(S, H, D, w.capacity)
     oracle.kv_append(ref, synth.prompt_kv(w, "k", nb=S), synth.prompt_kv(w, "v", nb=S), 0)
-    sk, sv = synth.step_kv(w, "k", t)[:S], synth.step_kv(w, "v", t)[:S]
-    q = synth.step_q(w, t)[:S]
-    t0 = time.perf_counter()
-    oracle.kv_append(ref, sk, sv, w.prompt + t - 1)
-    secs["append"] = (time.perf_counter() - t0) * w.batch / S
-    t0 = time.perf_counter()
-    oracle.decode_attn(ref, q, w.kv_len(t))
-    secs["attention"] = (time.perf_counter() - t0) * w.batch / S
-    gemm_s = 0.0
-    cols = args.cpu_sample_cols
-    for i, (K, N) in enumerate(w.weights):
-        ncol = min(cols, N)
-        wt = synth.weight(w, i)[:, :ncol]
-        c, m = oracle.quantize_g64(np.ascontiguousarray(wt))
-        x = synth.gemm_x(w, i, t)
+    for t in range(1, w.steps):       # positions of the earlier decode steps (untimed)
+        oracle.kv_append(ref, synth.step_kv(w, "k", t)[:S], synth.step_kv(w, "v", t)[:S], w.prompt + t - 1)
+    per_t = {}
+    for t in (1, w.steps):
+        secs = {}
+        sk, sv = synth.step_kv(w, "k", t)[:S], synth.step_kv(w, "v", t)[:S]
+        q = synth.step_q(w, t)[:S]
         t0 = time.perf_counter()
-        oracle.dequant_gemm(x, w.g, w.m, c, m)
-        gemm_s += (time.perf_counter() - t0) * N / ncol
-    secs["gemm"] = gemm_s
-    total = sum(secs.values())
-    cores = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
+        oracle.kv_append(ref, sk, sv, w.prompt + t - 1)
+        secs["append"] = (time.perf_counter() - t0) * w.batch / S
+        t0 = time.perf_counter()
+        oracle.decode_attn(ref, q, w.kv_len(t))
+        secs["attention"] = (time.perf_counter() - t0) * w.batch / S
+        g = 0.0
+        for i, K, N, ncol, c, m in slices:
+            x = synth.gemm_x(w, i, t)
+            t0 = time.perf_counter()
+            oracle.dequant_gemm(x, w.g, w.m, c, m)
+            g += (time.perf_counter() - t0) * N / ncol
+        secs["gemm"] = g
+        tot = sum(secs.values())
+        per_t["t=%d" % t] = {"tokens_per_s_per_layer": w.batch / tot,
+                             "seconds_per_step": {k: round(v, 4) for k, v in secs.items()}}
+    # OPT-6.7B attention (B = 64, 32 heads, kv_len 513) on one core, 8 sequences scaled to 64
+    w2 = synth.WORKLOADS["opt-6.7b"]
+    S2 = 8
+    ref2 = oracle.KVCache(S2, w2.heads, w2.head_dim, w2.capacity)
+    oracle.kv_append(ref2, synth.prompt_kv(w2, "k", nb=S2), synth.prompt_kv(w2, "v", nb=S2), 0)
+    oracle.kv_append(ref2, synth.step_kv(w2, "k", 1)[:S2], synth.step_kv(w2, "v", 1)[:S2], w2.prompt)
+    _omp_threads(1)
+    t0 = time.perf_counter()
+    oracle.decode_attn(ref2, synth.step_q(w2, 1)[:S2], w2.kv_len(1))
+    one_core = (time.perf_counter() - t0) * w2.batch / S2
+    _omp_threads(cores)
+    mean_step = float(np.mean([sum(v["seconds_per_step"].values()) for v in per_t.values()]))
     return {
-        "value": w.batch / total,
+        "value": w.batch / mean_step,
         "unit": "tokens/s/layer",
         "cores": cores,
         "kind": "oracle",
-        "sample": "decode step t=1 of %s: append+attention on %d of %d sequences, every weight GEMM on a "
-                  "%d-column slice with all %d rows; each part scaled to the full step" %
-                  (w.name, S, w.batch, cols, w.batch),
-        "seconds_per_step": {k: round(v, 4) for k, v in secs.items()},
+        "sample": "decode steps t=1 and t=%d of %s (value: their mean step time): append+attention on %d of %d "
+                  "sequences, every weight GEMM on a %d-column slice with all %d rows; each part scaled to the "
+                  "full step" % (w.steps, w.name, S, w.batch, args.cpu_sample_cols, w.batch),
+        "per_step": per_t,
+        "opt67b_attention_one_core": {"seconds_per_step": round(one_core, 4),
+                                      "GB_per_s": acc.attention_bytes(w2.batch, w2.hidden, w2.kv_len(1)) /
+                                      one_core / 1e9,
+                                      "sample": "8 of 64 sequences, kv_len 513, scaled"},
+        "cpu": cpu_info(),
     }
+
+
+def prefill_and_bulk_lines(torch, fgq, w, ch, stream) -> dict:
+    """Prompt-side launches beside the decode step: the bulk compression of 8
+    sequences' prompt K and V into layer instance 0, and causal prefill
+    attention over the same sequences' fp16 prompt, which precedes it."""
+    B, H, D, h = w.batch, w.heads, w.head_dim, w.hidden
+    sh = stream.cuda_stream
+    nb = min(8, B)
+    kd = torch.from_numpy(synth.prompt_kv(w, "k", nb=nb)).to("cuda")
+    vd = torch.from_numpy(synth.prompt_kv(w, "v", nb=nb)).to("cuda")
+    (kc, vc, km, vm), _ = ch.caches[0]
+    sub = fgq.kv_struct(kc[:nb], vc[:nb], km[:nb], vm[:nb], nb, H, D, w.capacity)
+    fgq.fgq_kv_append(sub, kd, vd, 0, w.prompt, sh)
+    torch.cuda.synchronize()
+    b0, b1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 10
+    b0.record(stream)
+    for _ in range(reps):
+        fgq.fgq_kv_append(sub, kd, vd, 0, w.prompt, sh)
+    b1.record(stream)
+    torch.cuda.synchronize()
+    bulk_us = 1e3 * b0.elapsed_time(b1) / reps
+    qd = torch.from_numpy(synth.prompt_q(w, nb=nb)).to("cuda")
+    pf_out = torch.empty((nb, w.prompt, h), dtype=torch.float32, device="cuda")
+    fgq.fgq_prefill_attn_f16(qd, kd, vd, nb, w.prompt, H, D, 0.0, pf_out, fgq.FGQ_DTYPE_F32, sh)
+    torch.cuda.synchronize()
+    b0.record(stream)
+    for _ in range(reps):
+        fgq.fgq_prefill_attn_f16(qd, kd, vd, nb, w.prompt, H, D, 0.0, pf_out, fgq.FGQ_DTYPE_F32, sh)
+    b1.record(stream)
+    torch.cuda.synchronize()
+    pf_us = 1e3 * b0.elapsed_time(b1) / reps
+    pf_flops = acc.prefill_attention_flops(nb, h, w.prompt)
+    ab = acc.append_bytes(nb, h, w.prompt)
+    del kd, vd, qd, pf_out
+    return {
+        "prefill_attention": {"sequences": nb, "tokens_per_sequence": w.prompt, "us_per_launch": pf_us,
+                              "TFLOP_per_s": pf_flops / (pf_us * 1e-6) / 1e12,
+                              "frac_mfma_peak": pf_flops / (pf_us * 1e-6) / 1e12 / MFMA_F16_PEAK_TFLOPS,
+                              "us_whole_block_estimate": pf_us * B / nb},
+        "prompt_bulk_append": {"sequences": nb, "tokens_per_sequence": w.prompt, "us_per_launch": bulk_us,
+                               "GB_per_s": ab / (bulk_us * 1e-6) / 1e9,
+                               "frac_hbm_peak": ab / (bulk_us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+                               "us_whole_block_estimate": bulk_us * B / nb}}
+
+
+def topk_line(torch, fgq, w, ch, stream, steps, warmup) -> dict:
+    """Top-K sparse attention (keep the top tenth of the positions, read only
+    their V rows) over the same caches and decode steps, queries drawn per
+    step."""
+    B, h = w.batch, w.hidden
+    sh = stream.cuda_stream
+    tk_out = torch.empty((B, h), dtype=torch.float32, device="cuda")
+    qs = [torch.from_numpy(synth.step_q(w, t)).to("cuda") for t in range(1, w.steps + 1)]
+
+    def launch(i):
+        t = i % w.steps + 1
+        L_t = w.prompt + t
+        fgq.fgq_decode_attn_topk_q4kv(ch.caches[i % ch.R][1], qs[t - 1], L_t, -(-L_t // 10), 0.0, tk_out,
+                                      fgq.FGQ_DTYPE_F32, None, sh)
+
+    for i in range(min(warmup, 8)):
+        launch(i)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    for i in range(steps):
+        ev[i][0].record(stream)
+        launch(min(warmup, 8) + i)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    ms = sum(a.elapsed_time(b) for a, b in ev)
+    ts = [(min(warmup, 8) + i) % w.steps + 1 for i in range(steps)]
+    by = sum(acc.topk_attention_bytes(B, h, w.kv_len(t), -(-w.kv_len(t) // 10)) for t in ts)
+    line = {"kept": "ceil(kv_len/10)", "us_per_launch": 1e3 * ms / steps, "GB_per_s": by / (ms * 1e-3) / 1e9,
+            "frac_hbm_peak": by / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+    tr = committed_traffic("attn_topk_wave_kernel", w.name)
+    if tr is not None and w.kv_len(w.steps) <= 2048:
+        line["traffic_bytes_per_launch"] = tr["bytes_per_launch"]
+        line["traffic_vs_algorithmic"] = tr["ratio"]
+    del qs, tk_out
+    return line
+
+
+def weight_streaming(torch, fgq, ch, stream) -> dict:
+    """The chained step with the layer's packed weights arriving from pinned
+    host memory every step (the offloading setting compression was made
+    for): two device buffers, the next step's weights copied on a second
+    stream (default priority) while this step computes; the KV cache stays
+    in HBM.  Also times the plain host-to-device copy of the same bytes and
+    of the fp16 weights they replace."""
+    w = ch.w
+    B = w.batch
+    src = [e["packed"] for e in ch.weights[0]]
+    host = [(pc.cpu().pin_memory(), pm.cpu().pin_memory()) for pc, pm in src]
+    nbytes = sum(a.numel() * 4 + b.numel() * 4 for a, b in host)
+    bufs = [[{"packed": (torch.empty_like(pc), torch.empty_like(pm))} for pc, pm in src] for _ in range(2)]
+    cstream = torch.cuda.Stream()
+    sh = stream.cuda_stream
+    copied = [torch.cuda.Event() for _ in range(2)]
+    freed = [torch.cuda.Event() for _ in range(2)]
+    n = 8
+    saved_w, saved_r = ch.weights, ch.R
+
+    def copy(i):
+        k = i % 2
+        with torch.cuda.stream(cstream):
+            cstream.wait_event(freed[k])
+            for (hc, hm), e in zip(host, bufs[k]):
+                dc, dm = e["packed"]
+                dc.copy_(hc, non_blocking=True)
+                dm.copy_(hm, non_blocking=True)
+            copied[k].record(cstream)
+
+    for k in range(2):
+        freed[k].record(stream)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ch.weights, ch.R = bufs, 2        # instance k of the chain = device buffer k (cache of instance 0 or 1)
+    copy(0)
+    e0.record(stream)
+    for i in range(n):
+        if i + 1 < n:
+            copy(i + 1)
+        stream.wait_event(copied[i % 2])
+        ch.enqueue(i, "packed", sh)
+        freed[i % 2].record(stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ch.weights, ch.R = saved_w, saved_r
+    ms = e0.elapsed_time(e1) / n
+    nel = sum(K * N for _, K, N, _ in ch.plan)
+    f16 = torch.empty(nel, dtype=torch.float16).pin_memory()
+    dev16 = torch.empty_like(f16, device="cuda")
+    g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    g0.record(stream)
+    dev16.copy_(f16, non_blocking=True)
+    g1.record(stream)
+    torch.cuda.synchronize()
+    f16_ms = g0.elapsed_time(g1)
+    del dev16, f16, bufs, host
+    return {"steps": n, "packed_bytes_per_step": nbytes, "ms_per_step": ms,
+            "tokens_per_s_per_layer": B / (ms * 1e-3), "h2d_GB_per_s": nbytes / (ms * 1e-3) / 1e9,
+            "fp16_weights_copy_ms": f16_ms, "fp16_over_packed_bytes": 2.0 * nel / nbytes}
 
 
 def short_name(kernel_name: str) -> str:
@@ -311,60 +801,163 @@ def short_name(kernel_name: str) -> str:
     return n.split("(")[0].replace("fgq::", "").strip()
 
 
-def summarize_trace(folder: str, w, steps: int) -> None:
-    """Markdown: rocprofv3's kernel statistics, then the mean duration of each
-    launch of a step over the last `steps` steps (a step starts with the KV
-    append; the split-K reduction is listed with the GEMM launch it ends)."""
+def _read_csvs(folder: str, pattern: str):
     import csv
     import glob
+    files = glob.glob(os.path.join(folder, "**", pattern), recursive=True)
+    if not files:
+        raise SystemExit("no %s under %s" % (pattern, folder))
+    rows = []
+    for f in files:
+        with open(f) as fh:
+            rows.extend(csv.DictReader(fh))
+    return rows
 
-    def one(pattern):
-        f = glob.glob(os.path.join(folder, "**", pattern), recursive=True)
-        if not f:
-            raise SystemExit("no %s under %s" % (pattern, folder))
-        with open(f[0]) as fh:
-            return list(csv.DictReader(fh))
 
-    stats = one("*kernel_stats.csv")
+def summarize_trace(folder: str, w, steps: int) -> None:
+    """Markdown: rocprofv3's kernel statistics, then the mean duration of each
+    launch of the chained step over the last `steps` steps of the headline
+    layout (a GEMM launch includes its split-K reduction, attention its
+    merge).  A step is located by its decode-time KV append: the GEMM launch
+    before it is the Q/K/V product, and attention and the other products
+    follow it."""
+    stats = _read_csvs(folder, "*kernel_stats.csv")
     print("| kernel | calls | average us | total ms | % of GPU time |")
     print("|---|---|---|---|---|")
-    for r in stats[:12]:
+    for r in stats[:14]:
         print("| %s | %s | %.1f | %.2f | %.1f |" % (short_name(r["Name"]), r["Calls"], float(r["AverageNs"]) / 1e3,
                                                   float(r["TotalDurationNs"]) / 1e6, float(r["Percentage"])))
-    trace = sorted(one("*kernel_trace.csv"), key=lambda r: int(r["Start_Timestamp"]))
-    names = ["append", "attention"] + ["gemm_" + p[0] for p in launch_plan(w)]
+    trace = sorted(_read_csvs(folder, "*kernel_trace.csv"), key=lambda r: int(r["Start_Timestamp"]))
+    recs = [(short_name(r["Kernel_Name"]), (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3,
+             int(r["Grid_Size_X"])) for r in trace]
+    # merge each split-K reduction / split merge into the launch before it
+    ops = []
+    for n, d, g in recs:
+        if (n.startswith("splitk_reduce_kernel") or n.startswith("attn_merge_kernel")) and ops:
+            ops[-1][1] += d
+        else:
+            ops.append([n, d, g])
+    names = ["gemm_qkv", "append", "attention", "gemm_out", "gemm_ffn1", "gemm_ffn2"]
+    want = ["dq_gemm_kernel", "kv_append_kernel", "attn_split_kernel", "dq_gemm_kernel", "dq_gemm_kernel",
+            "dq_gemm_kernel"]
     stepl = []
-    cur = None
-    for r in trace:
-        n = short_name(r["Kernel_Name"])
-        d = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
-        if n.startswith("kv_append_kernel") and int(r["Grid_Size_X"]) == w.batch * w.hidden // 4:
-            cur = {"ops": [], "kernels": {}}
-            stepl.append(cur)
-            cur["ops"].append(["append", d])
-        elif cur is None:
-            continue
-        elif n.startswith("attn_split_kernel"):
-            cur["ops"].append(["attention", d])
-        elif n.startswith("attn_merge_kernel"):
-            cur["ops"][-1][1] += d
-        elif n.startswith("dq_gemm_kernel"):
-            cur["ops"].append([names[len(cur["ops"])] if len(cur["ops"]) < len(names) else "?", d])
-        elif n.startswith("splitk_reduce_kernel"):
-            cur["ops"][-1][1] += d
-    good = [st for st in stepl if [o[0] for o in st["ops"]] == names][-steps:]
+    for a in range(1, len(ops) - 4):
+        if ops[a][0].startswith("kv_append_kernel") and ops[a][2] == w.batch * w.hidden // 4:
+            seq = ops[a - 1:a + 5]
+            if [s[0].split("<")[0] for s in seq] == want:
+                stepl.append(seq)
+    layout_steps = [st for st in stepl if "false" in st[0][0]] or stepl
+    good = layout_steps[-steps:]
     print()
-    print("Steady state, mean of the last %d steps (us per launch; a GEMM launch includes its split-K "
-          "reduction, attention its merge):" % len(good))
+    print("Steady state, mean of the last %d chained steps of the packed layout (us per launch; a GEMM launch "
+          "includes its split-K reduction, attention its merge):" % len(good))
     print()
-    print("| launch | us |")
-    print("|---|---|")
+    print("| launch | kernel | us |")
+    print("|---|---|---|")
     tot = 0.0
     for i, nm in enumerate(names):
-        v = float(np.mean([st["ops"][i][1] for st in good])) if good else float("nan")
+        v = float(np.mean([st[i][1] for st in good])) if good else float("nan")
         tot += v
-        print("| %s | %.1f |" % (nm, v))
-    print("| step (sum) | %.1f |" % tot)
+        print("| %s | %s | %.1f |" % (nm, good[0][i][0] if good else "?", v))
+    print("| step (sum) | | %.1f |" % tot)
+
+
+# Unit-utilisation figures from raw counters (per dispatch, summed over the
+# counter's dimensions), with rocprofv3's own derived-metric formulas:
+#   MfmaUtil  = 100 * SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE * SIMD_NUM)
+#   VALUBusy  = 100 * SQ_ACTIVE_INST_VALU / CU_NUM / GRBM_GUI_ACTIVE
+#   Occupancy = 400 * SQ_WAVE_CYCLES / GRBM_GUI_ACTIVE / CU_NUM / 32   (% of 32 wave slots per CU)
+#   LdsBankConflict (% of LDS-active cycles stalled) = 100 * SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE
+#   LdsUtil   = 100 * SQ_LDS_IDX_ACTIVE / (GRBM_GUI_ACTIVE * CU_NUM)
+CU_NUM, SIMD_NUM = 256, 1024
+
+
+def summarize_counters(folders, kernels) -> None:
+    """Markdown of per-kernel counter figures from rocprofv3 --pmc folders of
+    this bench (one folder per counter pass)."""
+    per = {}
+    durs = {}
+    for folder in folders:
+        for r in _read_csvs(folder, "*counter_collection.csv"):
+            name = short_name(r["Kernel_Name"])
+            key = (folder, int(r["Dispatch_Id"]))
+            d = per.setdefault(name, {}).setdefault(key, {})
+            d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+            if "Start_Timestamp" in r and r.get("End_Timestamp"):
+                durs.setdefault(name, {})[key] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+    print("| kernel | dispatches | GUI_ACTIVE cycles | MFMA busy % | VALU busy % | VALU insts per MFMA | "
+          "LDS insts per MFMA | occupancy % of 32 slots | LDS util % | LDS bank-conflict % of LDS-active | "
+          "MFMA-VALU co-issue % | waves waiting on LDS % |")
+    print("|---|---|---|---|---|---|---|---|---|---|---|---|")
+    out = {}
+    for name in sorted(per):
+        if kernels and not any(k in name for k in kernels):
+            continue
+        disp = per[name]
+        tot = {}
+        cnt = {}
+        for vals in disp.values():
+            for c, v in vals.items():
+                tot[c] = tot.get(c, 0.0) + v
+                cnt[c] = cnt.get(c, 0) + 1
+        m = {c: tot[c] / cnt[c] for c in tot}      # mean per dispatch
+
+        def g(c):
+            return m.get(c)
+
+        def pct(a, b, f=1.0):
+            return "%.1f" % (100.0 * f * a / b) if a is not None and b else "-"
+        gui = g("GRBM_GUI_ACTIVE")
+        mf = g("SQ_INSTS_MFMA")
+        valu = g("SQ_INSTS_VALU")
+        row = {
+            "dispatches": max(cnt.values()),
+            "gui_active": gui,
+            "mfma_busy": pct(g("SQ_VALU_MFMA_BUSY_CYCLES"), gui and gui * SIMD_NUM),
+            "valu_busy": pct(g("SQ_ACTIVE_INST_VALU"), gui and gui * CU_NUM),
+            "valu_per_mfma": "%.2f" % ((valu - mf) / mf) if valu is not None and mf else "-",
+            "lds_per_mfma": "%.2f" % (g("SQ_INSTS_LDS") / mf) if g("SQ_INSTS_LDS") is not None and mf else "-",
+            "occupancy": pct(g("SQ_WAVE_CYCLES"), gui and gui * CU_NUM * 32, 4.0),
+            "lds_util": pct(g("SQ_LDS_IDX_ACTIVE"), gui and gui * CU_NUM),
+            "lds_conflict": pct(g("SQ_LDS_BANK_CONFLICT"), g("SQ_LDS_IDX_ACTIVE")),
+            "coexec": pct(g("SQ_VALU_MFMA_COEXEC_CYCLES"), g("SQ_VALU_MFMA_BUSY_CYCLES")),
+            "wait_lds": pct(g("SQ_WAIT_INST_LDS"), g("SQ_WAVE_CYCLES")),
+        }
+        out[name] = row
+        print("| %s | %d | %s | %s | %s | %s | %s | %s | %s | %s | %s | %s |" % (
+            name, row["dispatches"], "%.4g" % gui if gui else "-", row["mfma_busy"], row["valu_busy"],
+            row["valu_per_mfma"], row["lds_per_mfma"], row["occupancy"], row["lds_util"], row["lds_conflict"],
+            row["coexec"], row["wait_lds"]))
+        dd = durs.get(name)
+        if dd and gui:
+            mean_us = float(np.mean(list(dd.values())))
+            print("|  (%s: mean %.1f us per dispatch under counters, %.2f GHz from GUI_ACTIVE) |" %
+                  (name, mean_us, gui / (mean_us * 1e3)))
+    print()
+    print("counters-json: " + json.dumps(out))
+
+
+def algorithmic_bytes_per_launch(kernel: str, w, n_steps: int = 0, warmup: int = 0) -> float:
+    """Mean algorithmic HBM bytes of one launch of the kernel over the
+    chained step (fp16 hand-offs) or the grouped workload."""
+    if kernel == "dq_gemm_kernel":
+        plan = launch_plan(w)
+        return float(np.mean([acc.gemm_bytes(w.batch, K, N, y_bytes=2) for _, K, N, _ in plan]))
+    if kernel == "attn_gqa_kernel":
+        g = synth.WORKLOADS["gqa"]
+        n = n_steps or g.steps
+        ts = [i % g.steps + 1 for i in range(n)]
+        return float(np.mean([acc.gqa_attention_bytes(g.batch, g.heads, g.n_kv_heads, g.head_dim, g.kv_len(t))
+                              for t in ts]))
+    if kernel == "attn_topk_wave_kernel":
+        n = n_steps or w.steps
+        ts = [i % w.steps + 1 for i in range(min(warmup, 8))] + \
+            [(warmup + i) % w.steps + 1 for i in range(n - warmup)]
+        return float(np.mean([acc.topk_attention_bytes(w.batch, w.hidden, w.kv_len(t), -(-w.kv_len(t) // 10))
+                              for t in ts]))
+    ts = [i % w.steps + 1 for i in range(n_steps or w.steps)]
+    return float(np.mean([acc.attention_bytes(w.batch, w.hidden, w.kv_len(t), out_bytes=2 if w.weights else 4)
+                          for t in ts]))
 
 
 def summarize_gqa_trace(folder: str) -> None:
@@ -409,97 +1002,6 @@ def summarize_gqa_trace(folder: str) -> None:
         ms = [d for k, d in merge if k == key]
         print("| %s | %d | %d | %.1f | %s |" % (key[0], key[1], len(ds), float(np.mean(ds)),
                                               "%.1f" % float(np.mean(ms)) if ms else "-"))
-
-
-def algorithmic_bytes_per_launch(kernel: str, w, n_steps: int = 0, warmup: int = 0) -> float:
-    """Mean algorithmic HBM bytes of one launch of the kernel over the first
-    n_steps bench steps (0: one full cycle of decode steps); the top-K kernel
-    runs min(warmup, 8) untimed launches and then one per timed step."""
-    if kernel == "dq_gemm_kernel":
-        plan = launch_plan(w)
-        return float(np.mean([acc.gemm_bytes(w.batch, K, N) for _, K, N, _ in plan]))
-    if kernel == "attn_gqa_kernel":
-        g = synth.WORKLOADS["gqa"]
-        n = n_steps or g.steps
-        ts = [i % g.steps + 1 for i in range(n)]
-        return float(np.mean([acc.gqa_attention_bytes(g.batch, g.heads, g.n_kv_heads, g.head_dim, g.kv_len(t))
-                              for t in ts]))
-    if kernel == "attn_topk_wave_kernel":
-        n = n_steps or w.steps
-        ts = [i % w.steps + 1 for i in range(min(warmup, 8))] + \
-            [(warmup + i) % w.steps + 1 for i in range(n - warmup)]
-        return float(np.mean([acc.topk_attention_bytes(w.batch, w.hidden, w.kv_len(t), -(-w.kv_len(t) // 10))
-                              for t in ts]))
-    ts = [i % w.steps + 1 for i in range(n_steps or w.steps)]
-    return float(np.mean([acc.attention_bytes(w.batch, w.hidden, w.kv_len(t)) for t in ts]))
-
-
-def weight_streaming(torch, fgq, w, layers, plan, steps_in, attn_out, ys, attn_ws, attn_ws_b, gemm_ws, gemm_ws_b,
-                     stream, args):
-    """The layer step with the layer's packed weights arriving from pinned host
-    memory each step (the offloading setting compression was made for): two
-    device buffers, the next step's weights copied on a second stream while
-    this step computes; the KV cache stays in HBM.  Also times the plain
-    host-to-device copy of the same bytes and of the fp16 weights they replace."""
-    B = w.batch
-    host = [(pc.cpu().pin_memory(), pm.cpu().pin_memory()) for pc, pm in layers[0].packed]
-    nbytes = sum(a.numel() * 4 + b.numel() * 4 for a, b in host)
-    bufs = [[(torch.empty_like(pc), torch.empty_like(pm)) for pc, pm in layers[0].packed] for _ in range(2)]
-    cstream = torch.cuda.Stream()
-    ch = stream.cuda_stream
-    copied = [torch.cuda.Event() for _ in range(2)]
-    freed = [torch.cuda.Event() for _ in range(2)]
-    L = layers[0]
-    n = 8
-
-    def copy(i):
-        k = i % 2
-        with torch.cuda.stream(cstream):
-            cstream.wait_event(freed[k])
-            for (hc, hm), (dc, dm) in zip(host, bufs[k]):
-                dc.copy_(hc, non_blocking=True)
-                dm.copy_(hm, non_blocking=True)
-            copied[k].record(cstream)
-
-    def step(i):
-        k = i % 2
-        t = i % w.steps + 1
-        d = steps_in[t - 1]
-        stream.wait_event(copied[k])
-        fgq.fgq_kv_append(L.kv, d["k"], d["v"], w.prompt + t - 1, 1, ch)
-        fgq.fgq_decode_attn_q4kv(L.kv, d["q"], w.prompt + t, 0.0, attn_out, fgq.FGQ_DTYPE_F32, attn_ws, attn_ws_b, ch)
-        for wi, (_, K, N, _) in enumerate(plan):
-            dc, dm = bufs[k][wi]
-            fgq.fgq_dequant_gemm(d["x"][wi], w.g, w.m, K, N, dc, dm, ys[wi], fgq.FGQ_DTYPE_F32, gemm_ws, gemm_ws_b, ch)
-        freed[k].record(stream)
-
-    for k in range(2):
-        freed[k].record(stream)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    copy(0)
-    e0.record(stream)
-    for i in range(n):
-        if i + 1 < n:
-            copy(i + 1)
-        step(i)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / n
-    # the plain copy of the packed bytes, and of fp16 weights of the same matrices
-    f16 = torch.empty(sum(K * N for _, K, N, _ in plan), dtype=torch.float16).pin_memory()
-    dev16 = torch.empty_like(f16, device="cuda")
-    g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    g0.record(stream)
-    dev16.copy_(f16, non_blocking=True)
-    g1.record(stream)
-    torch.cuda.synchronize()
-    f16_ms = g0.elapsed_time(g1)
-    del dev16, f16, bufs, host
-    return {"steps": n, "packed_bytes_per_step": nbytes, "ms_per_step": ms,
-            "tokens_per_s_per_layer": B / (ms * 1e-3), "h2d_GB_per_s": nbytes / (ms * 1e-3) / 1e9,
-            "fp16_weights_copy_ms": f16_ms, "fp16_over_packed_bytes": 2.0 * sum(K * N for _, K, N, _ in plan) / nbytes}
 
 
 def gqa_attention_line(torch, fgq, stream, steps: int, warmup: int, sweep_heads=(32, 16, 8, 4, 2, 1)) -> dict:
@@ -610,6 +1112,10 @@ def main():
     if args.summarize_gqa_trace:
         summarize_gqa_trace(args.summarize_gqa_trace)
         return
+    if args.summarize_counters:
+        summarize_counters(args.summarize_counters, ("dq_gemm_kernel", "attn_split_kernel", "attn_merge_kernel",
+                                                     "kv_append_kernel", "splitk_reduce_kernel"))
+        return
     if args.summarize_pmc:
         w = synth.WORKLOADS[args.config]
         fac, res = summarize_pmc(args)
@@ -654,240 +1160,64 @@ def main():
         return
     w = synth.WORKLOADS[args.config]
     B, H, D, h = w.batch, w.heads, w.head_dim, w.hidden
-    M = B
-
-    # ---------------- setup (untimed): weights, caches, per-step inputs
-    t_setup = time.time()
-    plan = launch_plan(w)
-    weights = build_weights(torch, fgq, w)
-    per_layer = acc.packed_bytes(sum(K * N for K, N in w.weights)) + \
-        2 * acc.packed_bytes(B * h * w.capacity)
-    R = args.rotate or max(3, min(8, int(np.ceil(3 * 256e6 / per_layer))))
-    layers = []
-    for inst in range(R):
-        layers.append(Layer(torch, fgq, w, inst, weights, prompt_chunks(torch, w)))
-        log("layer instance %d ready (%.1fs)" % (inst, time.time() - t_setup))
-    del weights
-    steps_in = []
-    for t in range(1, w.steps + 1):
-        d = {
-            "k": torch.from_numpy(synth.step_kv(w, "k", t)).to("cuda"),
-            "v": torch.from_numpy(synth.step_kv(w, "v", t)).to("cuda"),
-            "q": torch.from_numpy(synth.step_q(w, t)).to("cuda"),
-            "x": [torch.from_numpy(synth.gemm_x(w, idx[0], t)).to("cuda") for _, _, _, idx in plan],
-        }
-        steps_in.append(d)
-    attn_out = torch.empty((B, h), dtype=torch.float32, device="cuda")
-    ys = [torch.empty((M, N), dtype=torch.float32, device="cuda") for _, _, N, _ in plan]
-    attn_ws_b = max(fgq.fgq_decode_attn_ws_bytes(B, H, D, L) for L in range(w.prompt + 1, w.capacity + 1))
-    gemm_ws_b = max([fgq.fgq_dequant_gemm_ws_bytes(M, K, N) for _, K, N, _ in plan] + [0])
-    attn_ws = torch.empty(max(attn_ws_b, 16), dtype=torch.uint8, device="cuda")
-    gemm_ws = torch.empty(max(gemm_ws_b, 16), dtype=torch.uint8, device="cuda")
-    torch.cuda.synchronize()
-    log("setup %.1fs, %d layer instance(s), %.2f GB per instance" % (time.time() - t_setup, R, per_layer / 1e9))
-
+    other = "canonical" if args.gemm_layout == "packed" else "packed"
+    layouts = (args.gemm_layout, other) if w.weights else (args.gemm_layout,)
+    R, per_layer = rotation(w, layouts)
+    R = args.rotate or R
+    ch = Chain(torch, fgq, w, layouts, R)
     stream = torch.cuda.current_stream()
-    sh = stream.cuda_stream
-    ops = ["append", "attention"] + ["gemm_" + p[0] for p in plan]
-
-    def run_step(i, ev=None, sh=sh):
-        t = i % w.steps + 1
-        L = layers[i % R]
-        d = steps_in[t - 1]
-        if ev is not None:
-            ev[0].record(stream)
-        fgq.fgq_kv_append(L.kv, d["k"], d["v"], w.prompt + t - 1, 1, sh)
-        if ev is not None:
-            ev[1].record(stream)
-        fgq.fgq_decode_attn_q4kv(L.kv, d["q"], w.prompt + t, 0.0, attn_out, fgq.FGQ_DTYPE_F32, attn_ws,
-                                 attn_ws_b, sh)
-        if ev is not None:
-            ev[2].record(stream)
-        for wi, (_, K, N, _) in enumerate(plan):
-            pc, pm = L.packed[wi]
-            fgq.fgq_dequant_gemm(d["x"][wi], w.g, w.m, K, N, pc, pm, ys[wi], fgq.FGQ_DTYPE_F32, gemm_ws,
-                                 gemm_ws_b, sh)
-            if ev is not None:
-                ev[3 + wi].record(stream)
-
-    for i in range(args.warmup):
-        run_step(i)
-    torch.cuda.synchronize()
-
-    n_ev = 3 + len(plan)
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(args.steps)]
-    start = torch.cuda.Event(enable_timing=True)
-    stop = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    start.record(stream)
-    for i in range(args.steps):
-        run_step(args.warmup + i, events[i])
-    stop.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    total_ms = start.elapsed_time(stop)
-
-    # ---------------- the same steps as HIP graphs: one graph per (decode step,
-    # layer instance), captured once, replayed with every input already in place
-    graph_ms = None
-    if not args.no_graph:
-        graphs = {}
-        cap = torch.cuda.Stream()      # capture needs a stream other than the default one
-        for i in range(args.warmup + args.steps):
-            key = (i % w.steps, i % R)
-            if key not in graphs:
-                g = torch.cuda.CUDAGraph()
-                with torch.cuda.graph(g, stream=cap):
-                    run_step(i, sh=cap.cuda_stream)
-                graphs[key] = g
-        torch.cuda.synchronize()
-        for i in range(args.warmup):
-            graphs[(i % w.steps, i % R)].replay()
-        torch.cuda.synchronize()
-        gstart = torch.cuda.Event(enable_timing=True)
-        gstop = torch.cuda.Event(enable_timing=True)
-        wall0 = time.perf_counter()
-        gstart.record(stream)
-        for i in range(args.steps):
-            j = args.warmup + i
-            graphs[(j % w.steps, j % R)].replay()
-        gstop.record(stream)
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - wall0
-        graph_ms = gstart.elapsed_time(gstop)
-        log("%d graphs captured; graph pass %.3f ms/step, eager pass %.3f ms/step" %
-            (len(graphs), graph_ms / args.steps, total_ms / args.steps))
-
-    op_ms = {o: 0.0 for o in ops}
-    for ev in events:
-        op_ms["append"] += ev[0].elapsed_time(ev[1])
-        op_ms["attention"] += ev[1].elapsed_time(ev[2])
-        for wi, p in enumerate(plan):
-            op_ms["gemm_" + p[0]] += ev[2 + wi].elapsed_time(ev[3 + wi])
-
-    # ---------------- accounting
     K_steps = args.steps
-    ts = [(args.warmup + i) % w.steps + 1 for i in range(K_steps)]
-    attn_bytes = sum(acc.attention_bytes(B, h, w.kv_len(t)) for t in ts)
-    attn_flops = sum(acc.attention_flops(B, h, w.kv_len(t)) for t in ts)
-    app_bytes = K_steps * acc.append_bytes(B, h)
-    gemm_flops = K_steps * acc.layer_gemm_flops(M, w.weights)
-    gemm_bytes = K_steps * sum(acc.gemm_bytes(M, K, N) for _, K, N, _ in plan)
-    gemm_ms = sum(op_ms["gemm_" + p[0]] for p in plan)
-    attn_gbs = attn_bytes / (op_ms["attention"] * 1e-3) / 1e9
-    gemm_tflops = gemm_flops / (gemm_ms * 1e-3) / 1e12 if gemm_ms > 0 else 0.0
-    step_total_ms = total_ms if graph_ms is None else graph_ms
-    ms_per_step = step_total_ms / K_steps
-    value = B * K_steps / (step_total_ms * 1e-3)
 
-    kernels = {
-        "append": {"us_per_launch": 1e3 * op_ms["append"] / K_steps,
-                   "GB_per_s": app_bytes / (op_ms["append"] * 1e-3) / 1e9},
-        "attention": {"us_per_launch": 1e3 * op_ms["attention"] / K_steps, "GB_per_s": attn_gbs,
-                      "frac_hbm_peak": attn_gbs / HBM_PEAK_GBS,
-                      "TFLOP_per_s": attn_flops / (op_ms["attention"] * 1e-3) / 1e12},
-    }
-    for name, K, N, _ in plan:
-        ms = op_ms["gemm_" + name]
-        f = K_steps * acc.gemm_flops(M, K, N)
-        kernels["gemm_%s_%dx%d" % (name, K, N)] = {
-            "us_per_launch": 1e3 * ms / K_steps,
-            "TFLOP_per_s": f / (ms * 1e-3) / 1e12,
-            "frac_mfma_peak": f / (ms * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS,
-            "GB_per_s": K_steps * acc.gemm_bytes(M, K, N) / (ms * 1e-3) / 1e9,
-        }
+    # ---------------- the chained step, each layout: eager (per-launch events), then HIP graphs
+    passes = {}
+    for layout in layouts:
+        ep = eager_pass(torch, ch, layout, K_steps, args.warmup, args.min_warmup_ms)
+        gp = None if args.no_graph else graph_pass(torch, ch, layout, K_steps, args.warmup, args.min_warmup_ms)
+        passes[layout] = (ep, gp)
+        log("%s layout: eager %.4f ms/step%s (warm-up %d steps, %.0f ms)" % (
+            layout, ep["total_ms"] / K_steps, "" if gp is None else ", graphs %.4f ms/step" %
+            (gp["total_ms"] / K_steps), ep["warmup_steps"], ep["warmup_ms"]))
+    ep, gp = passes[args.gemm_layout]
+    kernels = kernel_lines(ch, ep, K_steps)
+    step_ms = ep["total_ms"] if gp is None else gp["total_ms"]
+    ms_per_step = step_ms / K_steps
+    value = B * K_steps / (step_ms * 1e-3)
+    attn_gbs = kernels["attention"]["GB_per_s"]
+    gemm_ms, gemm_tflops, gemm_gbs = gemm_totals(ch, ep, K_steps) if w.weights else (0.0, 0.0, 0.0)
+    if w.weights:
+        ep2, gp2 = passes[other]
+        k2 = kernel_lines(ch, ep2, K_steps)
+        ms2, tf2, gb2 = gemm_totals(ch, ep2, K_steps)
+        kernels["gemm_%s_layout" % other] = {
+            "what": "the same chained step with fgq_dequant_gemm%s" % ("" if other == "canonical" else "_packed"),
+            "ms_per_step": (ep2["total_ms"] if gp2 is None else gp2["total_ms"]) / K_steps,
+            "gemm_TFLOP_per_s": tf2, "gemm_frac_mfma_peak": tf2 / MFMA_F16_PEAK_TFLOPS,
+            "launches": {k: v for k, v in k2.items() if k.startswith("gemm_")}}
 
-    # prompt bulk compression (the prefill side of the cache, reported beside the
-    # decode step): the first 8 sequences' prompt K and V rewritten into layer 0
-    nb = min(8, B)
-    kd = torch.from_numpy(synth.prompt_kv(w, "k", nb=nb)).to("cuda")
-    vd = torch.from_numpy(synth.prompt_kv(w, "v", nb=nb)).to("cuda")
-    L0 = layers[0]
-    sub = fgq.kv_struct(L0.k_codes[:nb], L0.v_codes[:nb], L0.k_meta[:nb], L0.v_meta[:nb], nb, H, D, w.capacity)
-    fgq.fgq_kv_append(sub, kd, vd, 0, w.prompt, sh)
-    torch.cuda.synchronize()
-    b0, b1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    reps = 10
-    b0.record(stream)
-    for _ in range(reps):
-        fgq.fgq_kv_append(sub, kd, vd, 0, w.prompt, sh)
-    b1.record(stream)
-    torch.cuda.synchronize()
-    bulk_us = 1e3 * b0.elapsed_time(b1) / reps
-    # prefill attention over the same sequences' fp16 prompt (causal), which
-    # precedes that compression in a prefill step
-    qd = torch.from_numpy(synth.prompt_q(w, nb=nb)).to("cuda")
-    pf_out = torch.empty((nb, w.prompt, h), dtype=torch.float32, device="cuda")
-    fgq.fgq_prefill_attn_f16(qd, kd, vd, nb, w.prompt, H, D, 0.0, pf_out, fgq.FGQ_DTYPE_F32, sh)
-    torch.cuda.synchronize()
-    b0.record(stream)
-    for _ in range(reps):
-        fgq.fgq_prefill_attn_f16(qd, kd, vd, nb, w.prompt, H, D, 0.0, pf_out, fgq.FGQ_DTYPE_F32, sh)
-    b1.record(stream)
-    torch.cuda.synchronize()
-    pf_us = 1e3 * b0.elapsed_time(b1) / reps
-    pf_flops = acc.prefill_attention_flops(nb, h, w.prompt)
-    kernels["prefill_attention"] = {
-        "sequences": nb, "tokens_per_sequence": w.prompt, "us_per_launch": pf_us,
-        "TFLOP_per_s": pf_flops / (pf_us * 1e-6) / 1e12,
-        "frac_mfma_peak": pf_flops / (pf_us * 1e-6) / 1e12 / MFMA_F16_PEAK_TFLOPS,
-        "us_whole_block_estimate": pf_us * B / nb}
-    del kd, vd, qd, pf_out
-    kernels["prompt_bulk_append"] = {
-        "sequences": nb, "tokens_per_sequence": w.prompt, "us_per_launch": bulk_us,
-        "GB_per_s": acc.append_bytes(nb, h, w.prompt) / (bulk_us * 1e-6) / 1e9,
-        "frac_hbm_peak": acc.append_bytes(nb, h, w.prompt) / (bulk_us * 1e-6) / 1e9 / HBM_PEAK_GBS,
-        "us_whole_block_estimate": bulk_us * B / nb}
-
-    # top-K sparse attention (the pages' optional approximation: keep the top
-    # tenth of the positions, read only their V rows), over the same decode steps
-    tk_out = torch.empty((B, h), dtype=torch.float32, device="cuda")
-
-    def topk_launch(i):
-        t = i % w.steps + 1
-        L_t = w.prompt + t
-        fgq.fgq_decode_attn_topk_q4kv(layers[i % R].kv, steps_in[t - 1]["q"], L_t, -(-L_t // 10), 0.0, tk_out,
-                                      fgq.FGQ_DTYPE_F32, None, sh)
-
-    for i in range(min(args.warmup, 8)):
-        topk_launch(i)
-    tk_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K_steps)]
-    torch.cuda.synchronize()
-    for i in range(K_steps):
-        tk_ev[i][0].record(stream)
-        topk_launch(args.warmup + i)
-        tk_ev[i][1].record(stream)
-    torch.cuda.synchronize()
-    tk_ms = sum(a.elapsed_time(b) for a, b in tk_ev)
-    tk_bytes = sum(acc.topk_attention_bytes(B, h, w.kv_len(t), -(-w.kv_len(t) // 10)) for t in ts)
-    kernels["topk_attention"] = {
-        "kept": "ceil(kv_len/10)", "us_per_launch": 1e3 * tk_ms / K_steps,
-        "GB_per_s": tk_bytes / (tk_ms * 1e-3) / 1e9,
-        "frac_hbm_peak": tk_bytes / (tk_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-        "time_vs_dense_attention": tk_ms / op_ms["attention"]}
-    tk_tr = committed_traffic("attn_topk_wave_kernel", w.name)
-    if tk_tr is not None and w.kv_len(w.steps) <= 2048:
-        kernels["topk_attention"]["traffic_bytes_per_launch"] = tk_tr["bytes_per_launch"]
-        kernels["topk_attention"]["traffic_vs_algorithmic"] = tk_tr["ratio"]
-
-    if not args.no_gqa:
+    if not args.no_extras:
+        kernels.update(prefill_and_bulk_lines(torch, fgq, w, ch, stream))
+        kernels["topk_attention"] = topk_line(torch, fgq, w, ch, stream, K_steps, args.warmup)
+        kernels["topk_attention"]["time_vs_dense_attention"] = \
+            kernels["topk_attention"]["us_per_launch"] / kernels["attention"]["us_per_launch"]
+        if w.weights and "packed" in layouts and not args.no_stream:
+            kernels["weight_streaming"] = weight_streaming(torch, fgq, ch, stream)
+    ch.free()
+    del ch
+    torch.cuda.empty_cache()
+    if not args.no_extras and not args.no_gqa:
         t0 = time.time()
         kernels["gqa_attention"] = gqa_attention_line(torch, fgq, stream, 32, 8,
                                                       () if args.no_gqa_sweep else (32, 16, 8, 4, 2, 1))
         log("gqa attention line %.1fs" % (time.time() - t0))
 
-    if w.weights and not args.no_stream:
-        kernels["weight_streaming"] = weight_streaming(torch, fgq, w, layers, plan, steps_in, attn_out, ys, attn_ws,
-                                                       attn_ws_b, gemm_ws, gemm_ws_b, stream, args)
-
-    if w.weights and gemm_ms >= op_ms["attention"]:
+    if w.weights and gemm_ms >= 1e-3 * kernels["attention"]["us_per_launch"] * K_steps:
         kname = "dq_gemm_kernel"
-        roof = {"bound": "mfma", "kernel": kname + " (all %d weight GEMM launches of the step)" % len(plan),
+        roof = {"bound": "mfma", "kernel": kname + " (all %d weight GEMM launches of the step, %s layout)" %
+                (len(launch_plan(w)), args.gemm_layout),
                 "achieved": gemm_tflops, "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": gemm_tflops / MFMA_F16_PEAK_TFLOPS, "traffic": None,
                 "algorithmic_per_launch": "2*M*K*N flops, M=%d; mean algorithmic bytes per launch %.4g" %
-                                          (M, algorithmic_bytes_per_launch(kname, w))}
+                                          (B, algorithmic_bytes_per_launch(kname, w))}
     else:
         kname = "attn_split_kernel"
         roof = {"bound": "hbm", "kernel": kname, "achieved": attn_gbs, "peak": HBM_PEAK_GBS,
@@ -898,6 +1228,15 @@ def main():
     if tr is not None:
         roof["traffic"] = tr["bytes_per_launch"]
         roof["traffic_source"] = "rocprofv3 FETCH_SIZE + WRITE_SIZE per launch, copy-calibrated (profiles/)"
+
+    side = {}
+    if not args.no_side_configs:
+        for name in SIDE_CONFIGS:
+            if name == w.name:
+                continue
+            t0 = time.time()
+            side[name] = side_config_line(torch, fgq, name, args.gemm_layout, args)
+            log("side config %s: %.4f ms/step (%.1fs)" % (name, side[name]["ms_per_step"], time.time() - t0))
 
     result = {
         "metric": METRIC,
@@ -911,28 +1250,32 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f16",
-        "data": "synthetic (seeded Philox draws: KV and activations N(0,1), weights N(0,0.02))",
+        "data": "synthetic (seeded Philox draws: prompt KV and layer input N(0,1), weights N(0,0.02))",
         "config": {"workload": w.name, "batch_g_x_m": "%dx%d" % (w.g, w.m), "global_batch": B,
                    "heads": H, "head_dim": D, "hidden": h, "prompt": w.prompt, "decode_steps": w.steps,
                    "weights": ["%dx%d" % kn for kn in w.weights],
-                   "gemm_launches": ["%s %dx%d" % (p[0], p[1], p[2]) for p in plan], "layer_instances": R,
-                   "parallelism": "single GPU"},
+                   "step": "chained: Q|K|V product -> KV append -> attention -> Wout -> W1 -> W2, fp16 hand-offs"
+                   if w.weights else "append -> attention",
+                   "gemm_launches": ["%s %dx%d" % (p[0], p[1], p[2]) for p in launch_plan(w)],
+                   "gemm_layout": args.gemm_layout, "layer_instances": R, "parallelism": "single GPU"},
         "roofline": roof,
         "hbm_roofline_attention": {"achieved": attn_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                    "frac": attn_gbs / HBM_PEAK_GBS},
         "mfma_roofline_gemm": {"achieved": gemm_tflops, "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                               "frac": gemm_tflops / MFMA_F16_PEAK_TFLOPS,
-                               "GB_per_s": gemm_bytes / (gemm_ms * 1e-3) / 1e9 if gemm_ms else 0.0},
-        "step_launch": "eager" if graph_ms is None else "hip-graph replay (one graph per decode step and layer "
-                                                           "instance)",
-        "eager_ms_per_step": total_ms / K_steps,
+                               "frac": gemm_tflops / MFMA_F16_PEAK_TFLOPS, "GB_per_s": gemm_gbs},
+        "step_launch": "eager" if gp is None else "hip-graph replay (one graph per decode step and layer instance)",
+        "eager_ms_per_step": ep["total_ms"] / K_steps,
+        "warmup_run": {"eager": {"steps": ep["warmup_steps"], "ms": round(ep["warmup_ms"], 1)},
+                       "graph": None if gp is None else {"steps": gp["warmup_steps"], "ms": round(gp["warmup_ms"], 1)}},
+        "gpu_clock_during_timed_steps": None if gp is None else gp["clock"],
         "kernels": kernels,
-        "wall_s_timed_region": wall,
+        "configs": side,
+        "wall_s_timed_region": None if gp is None else gp["wall_s"],
         "context": "pages' end-to-end FlexGen 4-bit OPT-175B on one T4 with offloading: 1.12 token/s "
                    "(all 96 layers, prefill included) - not comparable to this per-layer in-HBM rate",
     }
     result["measured_ceilings"] = measured_ceilings(torch)
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and w.weights:
         t0 = time.time()
         result["cpu_baseline"] = cpu_baseline(w, args)
         log("cpu baseline %.1fs" % (time.time() - t0))

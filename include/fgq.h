@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define FGQ_ABI_VERSION 2
+#define FGQ_ABI_VERSION 3
 
 typedef int32_t fgq_status;
 #define FGQ_OK 0
@@ -126,6 +126,22 @@ fgq_status fgq_kv_append(const fgq_kv_cache *kv, const void *k_new_f16, const vo
                          int32_t pos, int32_t n_new, void *stream);
 
 /*
+ * fgq_kv_append_ld - fgq_kv_append over K and V rows that sit ld_new
+ * elements apart: row (b * n_new + i) of k_new starts at element
+ * (b * n_new + i) * ld_new.  This is how one fused projection writes them:
+ * for a [rows][3 * hidden] output holding q | k | v side by side, pass
+ * k_new = out + hidden, v_new = out + 2 * hidden, ld_new = 3 * hidden, so
+ * the layer's Q/K/V product feeds the cache directly (the layer's output
+ * feeds the next operation and its K and V persist in the cache:
+ * paper-graph-ui FlexGen summary, section 3 "Technical Approach", the
+ * computational graph of Figure 2).  Requires ld_new >= heads * head_dim
+ * (FGQ_ERR_SHAPE) and ld_new % 8 == 0 (FGQ_ERR_ALIGN); otherwise as
+ * fgq_kv_append, which is this call with ld_new = heads * head_dim.
+ */
+fgq_status fgq_kv_append_ld(const fgq_kv_cache *kv, const void *k_new_f16, const void *v_new_f16,
+                            int64_t ld_new, int32_t pos, int32_t n_new, void *stream);
+
+/*
  * fgq_decode_attn_q4kv - one decode step of attention for every sequence over
  * the compressed cache: for each (sequence, head)
  *   s_j = softmax_scale * sum_d q_d * K^_{j,d},  j in [0, kv_len)
@@ -144,6 +160,19 @@ size_t fgq_decode_attn_ws_bytes(int32_t batch, int32_t heads, int32_t head_dim, 
 fgq_status fgq_decode_attn_q4kv(const fgq_kv_cache *kv, const void *q_f16, int32_t kv_len,
                                 float softmax_scale, void *out, int32_t out_dtype,
                                 void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * fgq_decode_attn_q4kv_ld - fgq_decode_attn_q4kv with the query of sequence b
+ * at q_f16 + b * ld_q (elements), e.g. the q part of a fused [rows][3 *
+ * hidden] Q/K/V product (ld_q = 3 * hidden).  Requires ld_q >= heads *
+ * head_dim (FGQ_ERR_SHAPE) and ld_q % 8 == 0 (FGQ_ERR_ALIGN); out stays
+ * [batch][heads*head_dim].  fgq_decode_attn_q4kv is this call with
+ * ld_q = heads * head_dim.  batch * heads must stay below 2^31
+ * (FGQ_ERR_SHAPE).
+ */
+fgq_status fgq_decode_attn_q4kv_ld(const fgq_kv_cache *kv, const void *q_f16, int64_t ld_q, int32_t kv_len,
+                                   float softmax_scale, void *out, int32_t out_dtype,
+                                   void *ws, size_t ws_bytes, void *stream);
 
 /*
  * fgq_decode_attn_gqa_q4kv - decode attention with grouped K/V heads (GQA) or
@@ -220,9 +249,35 @@ fgq_status fgq_prefill_attn_f16(const void *q_f16, const void *k_f16, const void
                                 int32_t out_dtype, void *stream);
 
 /*
- * fgq_pack_weight_g64 - one-time re-layout of a compressed weight (codes and
- * meta as fgq_quantize_g64 writes them for W [K][N]) into the tile order the
- * GEMM consumes.
+ * fgq_dequant_gemm - Y = X * W^ for one block of m GPU batches of g rows that
+ * share one read of the compressed weight (paper-graph-ui FlexGen summary,
+ * section 3.4 "Compute Schedule"; FlexGen review on jaehun.me, "A block is
+ * the unit of weight reuse": B = g*m), straight from the weight's codes and
+ * metadata as fgq_quantize_g64 writes them for W [K = in][N = out] (groups
+ * of 64 output channels: FlexGen review on jaehun.me, "Is 4-bit compression
+ * the same as integer-arithmetic acceleration?").
+ *   x       fp16 [g*m][K], GPU batch j in rows j*g .. j*g+g-1;
+ *   w_codes uint8 [K][N/2], w_meta uint32 [K][N/64] (half2 {min, step});
+ *   y       [g*m][N] in y_dtype.
+ * W^ = fp16(min + q*step) (one rounding) is multiplied on the fp16 matrix
+ * cores with fp32 accumulation.  Requires K % 64 == 0, N % 64 == 0,
+ * K <= 2^23 and N <= 2^27 (FGQ_ERR_SHAPE otherwise); g*m == 0 is a no-op.
+ *   ws / ws_bytes: at least fgq_dequant_gemm_ws_bytes(g*m, K, N) bytes of
+ *   workspace (split-K partial sums; may be NULL when that is 0).
+ * stream is a hipStream_t.
+ */
+size_t fgq_dequant_gemm_ws_bytes(int64_t M, int64_t K, int64_t N);
+fgq_status fgq_dequant_gemm(const void *x_f16, int32_t g, int32_t m, int64_t K, int64_t N,
+                            const uint8_t *w_codes, const void *w_meta, void *y, int32_t y_dtype,
+                            void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * fgq_pack_weight_g64 - part of the offline weight compression: a one-time
+ * re-layout of a compressed weight (codes and meta as fgq_quantize_g64
+ * writes them for W [K][N]) into the tile order of fgq_dequant_gemm_packed.
+ * The codes are only moved; the metadata are rescaled by powers of two (and
+ * rounded to fp16 again, which changes a value only when it falls below the
+ * fp16 normal range).
  *   packed_codes uint32 [K/32][N/64][64][4]: word (kc, g, lane, j) holds the
  *     codes of W[k][n], n = 64g + 16j + lane%16, k = 32kc + 8(lane/16) + i for
  *     i = 0..7, code i in nibble [0,4,1,5,2,6,3,7][i] of the word (same byte
@@ -243,24 +298,16 @@ fgq_status fgq_pack_weight_g64(const uint8_t *codes, const uint32_t *meta, int64
                                uint32_t *packed_codes, uint32_t *packed_meta, void *stream);
 
 /*
- * fgq_dequant_gemm - Y = X * W^ for one block of m GPU batches of g rows that
- * share one read of the compressed weight (paper-graph-ui FlexGen summary,
- * section 3.4 "Compute Schedule"; FlexGen review on jaehun.me, "A block is
- * the unit of weight reuse": B = g*m).
- *   x  fp16 [g*m][K], GPU batch j in rows j*g .. j*g+g-1;
- *   packed_codes / packed_meta from fgq_pack_weight_g64 for W [K][N];
- *   y  [g*m][N] in y_dtype.
- * W^ is restored to fp16 (W^ = fp16(min + q*step)) and multiplied on the
- * fp16 matrix cores with fp32 accumulation.  Requires K % 32 == 0,
- * N % 64 == 0, K <= 2^23 and N <= 2^28 (FGQ_ERR_SHAPE otherwise); g*m == 0
- * is a no-op.
- *   ws / ws_bytes: at least fgq_dequant_gemm_ws_bytes(g*m, K, N) bytes of
- *   workspace (split-K partial sums; may be NULL when that is 0).
+ * fgq_dequant_gemm_packed - fgq_dequant_gemm over the packed layout that
+ * fgq_pack_weight_g64 makes offline (same block semantics and workspace
+ * query).  The restored weight is 2^e_g * fp16(2^-e_g * min + q * 2^-e_g *
+ * step), which equals fp16(min + q*step) unless 2^-e_g * W^ falls below the
+ * fp16 normal range (then within 2^(e_g - 25)).  Requires K % 32 == 0,
+ * N % 64 == 0, K <= 2^23 and N <= 2^28 (FGQ_ERR_SHAPE otherwise).
  */
-size_t fgq_dequant_gemm_ws_bytes(int64_t M, int64_t K, int64_t N);
-fgq_status fgq_dequant_gemm(const void *x_f16, int32_t g, int32_t m, int64_t K, int64_t N,
-                            const uint32_t *packed_codes, const uint32_t *packed_meta,
-                            void *y, int32_t y_dtype, void *ws, size_t ws_bytes, void *stream);
+fgq_status fgq_dequant_gemm_packed(const void *x_f16, int32_t g, int32_t m, int64_t K, int64_t N,
+                                   const uint32_t *packed_codes, const uint32_t *packed_meta,
+                                   void *y, int32_t y_dtype, void *ws, size_t ws_bytes, void *stream);
 
 #ifdef __cplusplus
 }

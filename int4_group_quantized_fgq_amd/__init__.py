@@ -63,8 +63,10 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
         "fgq_last_error": ([], ctypes.c_char_p),
         "fgq_quantize_g64": ([vp, i64, i64, i64, vp, vp, vp], i32),
         "fgq_kv_append": ([kvp, vp, vp, i32, i32, vp], i32),
+        "fgq_kv_append_ld": ([kvp, vp, vp, i64, i32, i32, vp], i32),
         "fgq_decode_attn_ws_bytes": ([i32, i32, i32, i32], sz),
         "fgq_decode_attn_q4kv": ([kvp, vp, i32, f32, vp, i32, vp, sz, vp], i32),
+        "fgq_decode_attn_q4kv_ld": ([kvp, vp, i64, i32, f32, vp, i32, vp, sz, vp], i32),
         "fgq_decode_attn_topk_q4kv": ([kvp, vp, i32, i32, f32, vp, i32, vp, vp], i32),
         "fgq_decode_attn_gqa_ws_bytes": ([i32, i32, i32, i32, i32], sz),
         "fgq_decode_attn_gqa_q4kv": ([kvp, vp, i32, i32, f32, vp, i32, vp, sz, vp], i32),
@@ -73,6 +75,7 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
         "fgq_pack_weight_g64": ([vp, vp, i64, i64, vp, vp, vp], i32),
         "fgq_dequant_gemm_ws_bytes": ([i64, i64, i64], sz),
         "fgq_dequant_gemm": ([vp, i32, i32, i64, i64, vp, vp, vp, i32, vp, sz, vp], i32),
+        "fgq_dequant_gemm_packed": ([vp, i32, i32, i64, i64, vp, vp, vp, i32, vp, sz, vp], i32),
     }
     for name, (args, res) in sig.items():
         f = getattr(lib, name)
@@ -140,6 +143,11 @@ def fgq_kv_append(kv: fgq_kv_cache, k_new, v_new, pos, n_new, stream=None) -> No
            "fgq_kv_append")
 
 
+def fgq_kv_append_ld(kv: fgq_kv_cache, k_new, v_new, ld_new, pos, n_new, stream=None) -> None:
+    _check(load().fgq_kv_append_ld(ctypes.byref(kv), _ptr(k_new), _ptr(v_new), ld_new, pos, n_new, _stream(stream)),
+           "fgq_kv_append_ld")
+
+
 def fgq_decode_attn_ws_bytes(batch, heads, head_dim, kv_len) -> int:
     return load().fgq_decode_attn_ws_bytes(batch, heads, head_dim, kv_len)
 
@@ -148,6 +156,12 @@ def fgq_decode_attn_q4kv(kv: fgq_kv_cache, q, kv_len, softmax_scale, out, out_dt
                          stream=None) -> None:
     _check(load().fgq_decode_attn_q4kv(ctypes.byref(kv), _ptr(q), kv_len, softmax_scale, _ptr(out), out_dtype,
                                        _ptr(ws), ws_bytes, _stream(stream)), "fgq_decode_attn_q4kv")
+
+
+def fgq_decode_attn_q4kv_ld(kv: fgq_kv_cache, q, ld_q, kv_len, softmax_scale, out, out_dtype, ws, ws_bytes,
+                            stream=None) -> None:
+    _check(load().fgq_decode_attn_q4kv_ld(ctypes.byref(kv), _ptr(q), ld_q, kv_len, softmax_scale, _ptr(out),
+                                          out_dtype, _ptr(ws), ws_bytes, _stream(stream)), "fgq_decode_attn_q4kv_ld")
 
 
 def fgq_decode_attn_gqa_ws_bytes(batch, q_heads, kv_heads, head_dim, kv_len) -> int:
@@ -185,6 +199,11 @@ def fgq_dequant_gemm_ws_bytes(M, K, N) -> int:
     return load().fgq_dequant_gemm_ws_bytes(M, K, N)
 
 
-def fgq_dequant_gemm(x, g, m, K, N, packed_codes, packed_meta, y, y_dtype, ws, ws_bytes, stream=None) -> None:
-    _check(load().fgq_dequant_gemm(_ptr(x), g, m, K, N, _ptr(packed_codes), _ptr(packed_meta), _ptr(y), y_dtype,
+def fgq_dequant_gemm(x, g, m, K, N, w_codes, w_meta, y, y_dtype, ws, ws_bytes, stream=None) -> None:
+    _check(load().fgq_dequant_gemm(_ptr(x), g, m, K, N, _ptr(w_codes), _ptr(w_meta), _ptr(y), y_dtype,
                                    _ptr(ws), ws_bytes, _stream(stream)), "fgq_dequant_gemm")
+
+
+def fgq_dequant_gemm_packed(x, g, m, K, N, packed_codes, packed_meta, y, y_dtype, ws, ws_bytes, stream=None) -> None:
+    _check(load().fgq_dequant_gemm_packed(_ptr(x), g, m, K, N, _ptr(packed_codes), _ptr(packed_meta), _ptr(y),
+                                          y_dtype, _ptr(ws), ws_bytes, _stream(stream)), "fgq_dequant_gemm_packed")

@@ -11,13 +11,13 @@ namespace fgq {
 
 fgq_status launch_quantize(const void *x, int64_t rows, int64_t cols, int64_t ld, uint8_t *codes,
                            uint32_t *meta, hipStream_t stream);
-fgq_status launch_kv_append(const fgq_kv_cache *kv, const void *k_new, const void *v_new, int32_t pos,
+fgq_status launch_kv_append(const fgq_kv_cache *kv, const void *k_new, const void *v_new, int64_t ld, int32_t pos,
                             int32_t n_new, hipStream_t stream);
 fgq_status launch_pack_weight(const uint8_t *codes, const uint32_t *meta, int64_t K, int64_t N,
                               uint32_t *packed_codes, uint32_t *packed_meta, hipStream_t stream);
 size_t attn_ws_bytes(int32_t batch, int32_t heads, int32_t head_dim, int32_t kv_len);
-fgq_status launch_decode_attn(const fgq_kv_cache *kv, const void *q, int32_t kv_len, float scale, void *out,
-                              int32_t out_dtype, void *ws, hipStream_t stream);
+fgq_status launch_decode_attn(const fgq_kv_cache *kv, const void *q, int64_t ld_q, int32_t kv_len, float scale,
+                              void *out, int32_t out_dtype, void *ws, hipStream_t stream);
 size_t gqa_ws_bytes(int32_t batch, int32_t q_heads, int32_t kv_heads, int32_t head_dim, int32_t kv_len);
 fgq_status launch_decode_attn_gqa(const fgq_kv_cache *kv, const void *q, int32_t q_heads, int32_t kv_len,
                                   float scale, void *out, int32_t out_dtype, void *ws, hipStream_t stream);
@@ -28,8 +28,8 @@ fgq_status launch_prefill_attn(const void *q, const void *k, const void *v, int3
                                int32_t heads, int32_t head_dim, float scale, void *out, int32_t out_dtype,
                                hipStream_t stream);
 size_t gemm_ws_bytes(int64_t M, int64_t K, int64_t N);
-fgq_status launch_dequant_gemm(const void *x, int64_t M, int64_t K, int64_t N, const uint32_t *pc,
-                               const uint32_t *pm, void *y, int32_t y_dtype, void *ws, hipStream_t stream);
+fgq_status launch_dequant_gemm(const void *x, int64_t M, int64_t K, int64_t N, const void *wc, const uint32_t *wm,
+                               bool canonical, void *y, int32_t y_dtype, void *ws, hipStream_t stream);
 
 static thread_local char g_err[512];
 
@@ -100,18 +100,28 @@ fgq_status fgq_quantize_g64(const void *x_f16, int64_t rows, int64_t cols, int64
     return launch_quantize(x_f16, rows, cols, ld_x, codes, meta, static_cast<hipStream_t>(stream));
 }
 
-fgq_status fgq_kv_append(const fgq_kv_cache *kv, const void *k_new_f16, const void *v_new_f16, int32_t pos,
-                         int32_t n_new, void *stream) {
+fgq_status fgq_kv_append_ld(const fgq_kv_cache *kv, const void *k_new_f16, const void *v_new_f16, int64_t ld_new,
+                            int32_t pos, int32_t n_new, void *stream) {
     g_err[0] = 0;
     fgq_status s = check_kv(kv);
     if (s != FGQ_OK) return s;
     if (pos < 0 || n_new < 0) return fail(FGQ_ERR_INVALID_ARG, "negative pos or n_new");
     if ((int64_t)pos + n_new > kv->capacity)
         return fail(FGQ_ERR_CAPACITY, "pos %d + n_new %d > capacity %d", pos, n_new, kv->capacity);
+    const int64_t hidden = (int64_t)kv->heads * kv->head_dim;
+    if (ld_new < hidden) return fail(FGQ_ERR_SHAPE, "ld_new %lld < heads * head_dim %lld", (long long)ld_new,
+                                     (long long)hidden);
     if (n_new == 0 || kv->batch == 0 || kv->heads == 0) return FGQ_OK;
     if (!k_new_f16 || !v_new_f16) return fail(FGQ_ERR_INVALID_ARG, "NULL k_new or v_new");
-    if (!aligned16(k_new_f16) || !aligned16(v_new_f16)) return fail(FGQ_ERR_ALIGN, "k_new/v_new must be 16-byte aligned");
-    return launch_kv_append(kv, k_new_f16, v_new_f16, pos, n_new, static_cast<hipStream_t>(stream));
+    if (!aligned16(k_new_f16) || !aligned16(v_new_f16) || ld_new % 8 != 0)
+        return fail(FGQ_ERR_ALIGN, "k_new/v_new and their rows must be 16-byte aligned");
+    return launch_kv_append(kv, k_new_f16, v_new_f16, ld_new, pos, n_new, static_cast<hipStream_t>(stream));
+}
+
+fgq_status fgq_kv_append(const fgq_kv_cache *kv, const void *k_new_f16, const void *v_new_f16, int32_t pos,
+                         int32_t n_new, void *stream) {
+    const int64_t hidden = kv ? (int64_t)kv->heads * kv->head_dim : 0;
+    return fgq_kv_append_ld(kv, k_new_f16, v_new_f16, hidden, pos, n_new, stream);
 }
 
 size_t fgq_decode_attn_ws_bytes(int32_t batch, int32_t heads, int32_t head_dim, int32_t kv_len) {
@@ -119,8 +129,9 @@ size_t fgq_decode_attn_ws_bytes(int32_t batch, int32_t heads, int32_t head_dim, 
     return attn_ws_bytes(batch, heads, head_dim, kv_len);
 }
 
-fgq_status fgq_decode_attn_q4kv(const fgq_kv_cache *kv, const void *q_f16, int32_t kv_len, float softmax_scale,
-                                void *out, int32_t out_dtype, void *ws, size_t ws_bytes, void *stream) {
+fgq_status fgq_decode_attn_q4kv_ld(const fgq_kv_cache *kv, const void *q_f16, int64_t ld_q, int32_t kv_len,
+                                   float softmax_scale, void *out, int32_t out_dtype, void *ws, size_t ws_bytes,
+                                   void *stream) {
     g_err[0] = 0;
     fgq_status s = check_kv(kv);
     if (s != FGQ_OK) return s;
@@ -129,9 +140,14 @@ fgq_status fgq_decode_attn_q4kv(const fgq_kv_cache *kv, const void *q_f16, int32
     if (kv_len < 1) return fail(FGQ_ERR_SHAPE, "kv_len %d < 1", kv_len);
     if (kv_len > kv->capacity) return fail(FGQ_ERR_CAPACITY, "kv_len %d > capacity %d", kv_len, kv->capacity);
     if (!std::isfinite(softmax_scale)) return fail(FGQ_ERR_INVALID_ARG, "softmax_scale is not finite");
+    const int64_t hidden = (int64_t)kv->heads * kv->head_dim;
+    if (ld_q < hidden) return fail(FGQ_ERR_SHAPE, "ld_q %lld < heads * head_dim %lld", (long long)ld_q,
+                                   (long long)hidden);
+    if ((int64_t)kv->batch * kv->heads > INT32_MAX) return fail(FGQ_ERR_SHAPE, "batch * heads > 2^31 - 1");
     if (kv->batch == 0 || kv->heads == 0) return FGQ_OK;
     if (!q_f16 || !out) return fail(FGQ_ERR_INVALID_ARG, "NULL q or out");
-    if (!aligned16(q_f16) || !aligned16(out)) return fail(FGQ_ERR_ALIGN, "q/out must be 16-byte aligned");
+    if (!aligned16(q_f16) || !aligned16(out) || ld_q % 8 != 0)
+        return fail(FGQ_ERR_ALIGN, "q (and its rows) and out must be 16-byte aligned");
     const size_t need = attn_ws_bytes(kv->batch, kv->heads, kv->head_dim, kv_len);
     if (need > 0) {
         if (!ws || ws_bytes < need)
@@ -139,7 +155,13 @@ fgq_status fgq_decode_attn_q4kv(const fgq_kv_cache *kv, const void *q_f16, int32
         if (!aligned16(ws)) return fail(FGQ_ERR_ALIGN, "workspace must be 16-byte aligned");
     }
     const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt((float)kv->head_dim);
-    return launch_decode_attn(kv, q_f16, kv_len, scale, out, out_dtype, ws, static_cast<hipStream_t>(stream));
+    return launch_decode_attn(kv, q_f16, ld_q, kv_len, scale, out, out_dtype, ws, static_cast<hipStream_t>(stream));
+}
+
+fgq_status fgq_decode_attn_q4kv(const fgq_kv_cache *kv, const void *q_f16, int32_t kv_len, float softmax_scale,
+                                void *out, int32_t out_dtype, void *ws, size_t ws_bytes, void *stream) {
+    const int64_t hidden = kv ? (int64_t)kv->heads * kv->head_dim : 0;
+    return fgq_decode_attn_q4kv_ld(kv, q_f16, hidden, kv_len, softmax_scale, out, out_dtype, ws, ws_bytes, stream);
 }
 
 size_t fgq_decode_attn_gqa_ws_bytes(int32_t batch, int32_t q_heads, int32_t kv_heads, int32_t head_dim,
@@ -183,7 +205,9 @@ fgq_status fgq_decode_attn_gqa_q4kv(const fgq_kv_cache *kv, const void *q_f16, i
         if (!aligned16(ws)) return fail(FGQ_ERR_ALIGN, "workspace must be 16-byte aligned");
     }
     const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt((float)kv->head_dim);
-    if (mha) return launch_decode_attn(kv, q_f16, kv_len, scale, out, out_dtype, ws, static_cast<hipStream_t>(stream));
+    if (mha)
+        return launch_decode_attn(kv, q_f16, (int64_t)kv->heads * kv->head_dim, kv_len, scale, out, out_dtype, ws,
+                                  static_cast<hipStream_t>(stream));
     return launch_decode_attn_gqa(kv, q_f16, q_heads, kv_len, scale, out, out_dtype, ws,
                                   static_cast<hipStream_t>(stream));
 }
@@ -259,19 +283,27 @@ size_t fgq_dequant_gemm_ws_bytes(int64_t M, int64_t K, int64_t N) {
     return gemm_ws_bytes(M, K, N);
 }
 
-fgq_status fgq_dequant_gemm(const void *x_f16, int32_t g, int32_t m, int64_t K, int64_t N,
-                            const uint32_t *packed_codes, const uint32_t *packed_meta, void *y, int32_t y_dtype,
-                            void *ws, size_t ws_bytes, void *stream) {
-    g_err[0] = 0;
+// Shared validation of the two GEMM entry points; kmult is the K granule
+// (64 for the canonical layout, 32 for the packed one), nmax the largest N.
+static fgq_status check_gemm(const void *x_f16, int32_t g, int32_t m, int64_t K, int64_t N, const void *wc,
+                             const void *wm, void *y, int32_t y_dtype, void *ws, size_t ws_bytes, int64_t kmult,
+                             int64_t nmax, bool *noop) {
+    *noop = false;
     if (g < 0 || m < 0 || K < 0 || N < 0) return fail(FGQ_ERR_INVALID_ARG, "negative size");
-    if (K % 32 != 0 || N % 64 != 0) return fail(FGQ_ERR_SHAPE, "K %% 32 and N %% 64 must be 0");
+    if (K % kmult != 0 || N % 64 != 0)
+        return fail(FGQ_ERR_SHAPE, "K %% %lld and N %% 64 must be 0 (K=%lld N=%lld)", (long long)kmult, (long long)K,
+                    (long long)N);
     if (y_dtype != FGQ_DTYPE_F32 && y_dtype != FGQ_DTYPE_F16) return fail(FGQ_ERR_DTYPE, "y_dtype %d", y_dtype);
     const int64_t M = (int64_t)g * m;
     if (M > (int64_t)1 << 30) return fail(FGQ_ERR_SHAPE, "g*m too large");
-    if (K > (int64_t)1 << 23 || N > (int64_t)1 << 28) return fail(FGQ_ERR_SHAPE, "K > 2^23 or N > 2^28");
-    if (M == 0 || N == 0) return FGQ_OK;
-    if (!y || (K > 0 && (!x_f16 || !packed_codes || !packed_meta))) return fail(FGQ_ERR_INVALID_ARG, "NULL array");
-    if (!aligned16(y) || (K > 0 && (!aligned16(x_f16) || !aligned16(packed_codes) || !aligned16(packed_meta))))
+    if (K > (int64_t)1 << 23 || N > nmax)
+        return fail(FGQ_ERR_SHAPE, "K > 2^23 or N > %lld", (long long)nmax);
+    if (M == 0 || N == 0) {
+        *noop = true;
+        return FGQ_OK;
+    }
+    if (!y || (K > 0 && (!x_f16 || !wc || !wm))) return fail(FGQ_ERR_INVALID_ARG, "NULL array");
+    if (!aligned16(y) || (K > 0 && (!aligned16(x_f16) || !aligned16(wc) || !aligned16(wm))))
         return fail(FGQ_ERR_ALIGN, "arrays must be 16-byte aligned");
     const size_t need = gemm_ws_bytes(M, K, N);
     if (need > 0) {
@@ -279,7 +311,29 @@ fgq_status fgq_dequant_gemm(const void *x_f16, int32_t g, int32_t m, int64_t K, 
             return fail(FGQ_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws ? ws_bytes : (size_t)0, need);
         if (!aligned16(ws)) return fail(FGQ_ERR_ALIGN, "workspace must be 16-byte aligned");
     }
-    return launch_dequant_gemm(x_f16, M, K, N, packed_codes, packed_meta, y, y_dtype, ws,
+    return FGQ_OK;
+}
+
+fgq_status fgq_dequant_gemm(const void *x_f16, int32_t g, int32_t m, int64_t K, int64_t N, const uint8_t *w_codes,
+                            const void *w_meta, void *y, int32_t y_dtype, void *ws, size_t ws_bytes, void *stream) {
+    g_err[0] = 0;
+    bool noop = false;
+    const fgq_status s = check_gemm(x_f16, g, m, K, N, w_codes, w_meta, y, y_dtype, ws, ws_bytes, 64,
+                                    (int64_t)1 << 27, &noop);
+    if (s != FGQ_OK || noop) return s;
+    return launch_dequant_gemm(x_f16, (int64_t)g * m, K, N, w_codes, static_cast<const uint32_t *>(w_meta), true, y,
+                               y_dtype, ws, static_cast<hipStream_t>(stream));
+}
+
+fgq_status fgq_dequant_gemm_packed(const void *x_f16, int32_t g, int32_t m, int64_t K, int64_t N,
+                                   const uint32_t *packed_codes, const uint32_t *packed_meta, void *y, int32_t y_dtype,
+                                   void *ws, size_t ws_bytes, void *stream) {
+    g_err[0] = 0;
+    bool noop = false;
+    const fgq_status s = check_gemm(x_f16, g, m, K, N, packed_codes, packed_meta, y, y_dtype, ws, ws_bytes, 32,
+                                    (int64_t)1 << 28, &noop);
+    if (s != FGQ_OK || noop) return s;
+    return launch_dequant_gemm(x_f16, (int64_t)g * m, K, N, packed_codes, packed_meta, false, y, y_dtype, ws,
                                static_cast<hipStream_t>(stream));
 }
 

@@ -27,6 +27,7 @@
 //  * Scores of a 64-token chunk are formed first, the chunk max is taken over
 //    the wave, then the exponentials and the P.V pass run with that max: the
 //    running accumulators are rescaled once per chunk, not per token.
+#include <climits>
 #include <type_traits>
 
 #include "common.h"
@@ -93,7 +94,7 @@ template <int D, int CH>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(CH <= 2 ? 4 : (CH >= 6 ? 2 : 3))))
 void attn_split_kernel(
     const uint8_t *__restrict__ kc, const uint32_t *__restrict__ km, const uint8_t *__restrict__ vc,
-    const uint32_t *__restrict__ vm, const uint16_t *__restrict__ q, int H, int cap, int L, int n_split,
+    const uint32_t *__restrict__ vm, const uint16_t *__restrict__ q, int64_t ld_q, int H, int cap, int L, int n_split,
     int tok_per_split, int total_items, float sl2, float *__restrict__ ws, void *__restrict__ out,
     int out_f16) {
     constexpr int PARTS = D / 32;   // lanes per token row
@@ -116,7 +117,7 @@ void attn_split_kernel(
     const int slot = lane / PARTS, part = lane % PARTS, grp = part >> 1;
 
     // ---- query: 32 fp16 values of this lane's part, arranged as dot2 pairs
-    const uint4 *qp = reinterpret_cast<const uint4 *>(q + ((size_t)b * H + hh) * D + part * 32);
+    const uint4 *qp = reinterpret_cast<const uint4 *>(q + (size_t)b * ld_q + (size_t)hh * D + part * 32);
     uint32_t qw[16];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -388,17 +389,20 @@ size_t attn_ws_bytes(int32_t batch, int32_t heads, int32_t head_dim, int32_t kv_
     return (size_t)batch * heads * p.n_split * (head_dim + 4) * sizeof(float);
 }
 
-fgq_status launch_decode_attn(const fgq_kv_cache *kv, const void *q, int32_t kv_len, float scale, void *out,
-                              int32_t out_dtype, void *ws, hipStream_t stream) {
-    const AttnPlan p = attn_plan(kv->batch, kv->heads, kv->head_dim, kv_len);
-    const int total = kv->batch * kv->heads * p.n_split;
+fgq_status launch_decode_attn(const fgq_kv_cache *kv, const void *q, int64_t ld_q, int32_t kv_len, float scale,
+                              void *out, int32_t out_dtype, void *ws, hipStream_t stream) {
     if (kv->batch == 0 || kv->heads == 0) return FGQ_OK;
+    const AttnPlan p = attn_plan(kv->batch, kv->heads, kv->head_dim, kv_len);
+    const int64_t total64 = (int64_t)kv->batch * kv->heads * p.n_split;
+    if (total64 > INT32_MAX - 3)
+        return fail(FGQ_ERR_SHAPE, "batch * heads * splits = %lld work items exceeds 2^31", (long long)total64);
+    const int total = (int)total64;
     const float sl2 = scale * kLog2e;
     const int f16 = out_dtype == FGQ_DTYPE_F16;
     const dim3 grid((unsigned)((total + 3) / 4)), block(256);
 #define FGQ_ATTN_LAUNCH(D, CH)                                                                                  \
     attn_split_kernel<D, CH><<<grid, block, 0, stream>>>(kv->k_codes, kv->k_meta, kv->v_codes, kv->v_meta,      \
-                                                         static_cast<const uint16_t *>(q), kv->heads, kv->capacity, \
+                                                         static_cast<const uint16_t *>(q), ld_q, kv->heads, kv->capacity, \
                                                          kv_len, p.n_split, p.tok_per_split, total, sl2,        \
                                                          static_cast<float *>(ws), out, f16)
     if (kv->head_dim == 128) {

@@ -6,6 +6,13 @@
 // review on blog.gzher.com, section 3.4) and fed to the fp16 matrix cores
 // (v_mfma_f32_16x16x32_f16) with fp32 accumulation.
 //
+// Two weight layouts share one kernel template:
+//  * CANON: the codes [K][N/2] and metadata [K][N/64] exactly as the
+//    quantiser writes them (groups of 64 output channels at one input k);
+//  * packed: a one-time re-layout of the same codes and metadata made
+//    offline with the quantisation (word-per-fragment codes, steps
+//    pre-scaled for the subnormal code placement below).
+//
 // Tiling (gfx950, 64-wide waves):
 //  * a wave owns one weight group column (64 output channels = 4 MFMA
 //    n-tiles) and every row of its M block (up to 9 m-tiles = 144 rows), so
@@ -15,18 +22,25 @@
 //    are summed through LDS at the end, and all waves share the X rows of
 //    each K chunk through LDS;
 //  * every operand reaches LDS through gfx950's direct global->LDS loads
-//    (global_load_lds_dwordx4, scalar base + loop-invariant lane offset, so
-//    no vector ALU work) into a ring of two-chunk slots (the X rows, each
-//    wave's packed code words and its group metadata) as deep as the LDS
-//    allows, all but one slot in flight, one barrier per slot;
-//  * the packed weight layout puts the 8 k-values of one output channel in
-//    one 32-bit word, in a nibble order where one AND leaves two codes in
-//    the mantissas of two fp16 subnormals (q * 2^-24 or q * 2^-20); the
-//    packed metadata holds the steps pre-scaled to match and everything
-//    scaled by a per-column-group power of two 2^-e that keeps the scaled
-//    steps finite, so one packed FMA gives two values 2^-e * W^ (W^ itself
-//    rounded once) and the epilogue multiplies by 2^e; the next chunk is
-//    dequantised between the current chunk's MFMAs;
+//    (global_load_lds_dword[x4], scalar base + loop-invariant lane offset,
+//    so no vector ALU work) into a ring of two-chunk slots (the X rows, the
+//    code words and the group metadata) as deep as the LDS allows, all but
+//    one slot in flight, one barrier per slot;
+//  * packed layout: the 8 k-values of one output channel sit in one 32-bit
+//    word, in a nibble order where one AND leaves two codes in the mantissas
+//    of two fp16 subnormals (q * 2^-24 or q * 2^-20); the packed metadata
+//    holds the steps pre-scaled to match and everything scaled by a
+//    per-column-group power of two 2^-e that keeps the scaled steps finite,
+//    so one packed FMA gives two values 2^-e * W^ and the epilogue
+//    multiplies by 2^e;
+//  * canonical layout: the code rows of a chunk land in LDS as they are
+//    (an XOR swizzle of their 16-byte pieces keeps the reads conflict-free);
+//    MFMA column c of n-tile j is output channel 4c + j of the group, so a
+//    lane's four n-tiles are the four nibbles of one 16-bit read per k row;
+//    an AND-OR places a code in the mantissa of 1024 + q (or 64 + q), one
+//    packed subtract leaves q exactly, and one packed FMA with the row's
+//    step and minimum gives W^ rounded once;
+//  * the next chunk is dequantised between the current chunk's MFMAs;
 //  * A fragments stream three m-tiles ahead across chunk and slot boundaries;
 //    X rows sit in LDS with a 16-byte-slot XOR swizzle, so the rows of an A
 //    fragment read hit distinct banks;
@@ -69,6 +83,12 @@ __device__ __forceinline__ void dma16(const void *sbase, uint32_t voff, uint32_t
     asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(m0v)
                  : "memory", "m0");
 }
+// The same with 4 bytes per lane: lane i's dword lands at lds + 4*i.
+__device__ __forceinline__ void dma4(const void *sbase, uint32_t voff, uint32_t lds) {
+    const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds);
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(sbase), "s"(m0v)
+                 : "memory", "m0");
+}
 #pragma clang diagnostic pop
 
 // Barrier that does not wait for outstanding direct-to-LDS loads (each wave
@@ -85,10 +105,11 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 
 // Wait until at most `SLOTS` ring slots of this wave's loads are
-// outstanding; a wave issues `cnt` (2..7) load instructions per slot.
+// outstanding; a wave issues `cnt` (1..7) load instructions per slot.
 template <int SLOTS>
 __device__ __forceinline__ void wait_slots(int cnt) {
     switch (cnt) {
+        case 1: wait_vmcnt<1 * SLOTS>(); break;
         case 2: wait_vmcnt<2 * SLOTS>(); break;
         case 3: wait_vmcnt<3 * SLOTS>(); break;
         case 4: wait_vmcnt<4 * SLOTS>(); break;
@@ -104,6 +125,19 @@ __device__ __forceinline__ void wait_slots(int cnt) {
 // slots, so the 8 lanes of one 128-byte bank cycle hit distinct banks.  The
 // swizzle repeats every 8 rows, so it is the same for every 16-row m-tile.
 __device__ __forceinline__ int xswz(int row) { return (row >> 1) & 3; }
+
+// Canonical layout: a chunk's code rows (32 k rows x CG groups x 32 bytes)
+// sit in LDS row-major, 16-byte piece p of row r stored at piece p ^ cswz(r).
+// A 16-bit read of one k row by the lanes of an A/B fragment touches rows
+// r, r+8, r+16, r+24 and the two pieces of one group: the swizzle gives the
+// four rows four different piece pairs, so the eight pieces land on eight
+// different 16-byte bank ranges.
+__device__ __forceinline__ int cswz(int row) { return ((row >> 3) & 3) << 1; }
+// Canonical layout: a chunk's metadata rows (32 k rows x CG groups, one
+// dword each) sit row-major, group c of row r stored at c ^ mswz(r), so the
+// four rows r, r+8, r+16, r+24 that a 32-bit read by one wave touches fall
+// on four different banks.
+__device__ __forceinline__ int mswz(int row) { return (row >> 3) & 3; }
 
 // Ring and LDS layout of a workgroup with MT m-tiles and KP k-phases: the
 // 8 waves are CG = 8/KP column groups x KP phases; phase p multiplies the
@@ -131,13 +165,27 @@ struct Cfg {
     static_assert(LDS <= 160 * 1024, "LDS budget");
 };
 
-template <int MT, int KP>
+// Raw B operands of one chunk as read from LDS, before dequantisation.
+struct BRawPacked {
+    uint4 cw, ms, mm;        // code word (4 n-tiles), scaled step pairs, scaled minimum pairs
+};
+struct BRawCanon {
+    uint32_t v[4];           // k rows (2p, 2p+1) of the lane's 8: nibble j of each half is n-tile j
+    uint32_t sp[4], mp[4];   // fp16 (step, step) and (min, min) of rows 2p, 2p+1
+};
+
+// wc / wm: the weight's codes and metadata, canonical (CANON: uint8 codes
+// [K][N/2], uint32 meta [K][N/64]) or packed.
+template <int MT, int KP, bool CANON>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void dq_gemm_kernel(const uint16_t *__restrict__ x, int M, int64_t K, int64_t N,
-                    const uint32_t *__restrict__ pc, const uint32_t *__restrict__ pm, int chunks_per_split,
+                    const void *__restrict__ wc, const uint32_t *__restrict__ wm, int chunks_per_split,
                     float *__restrict__ part, void *__restrict__ y, int y_f16, int ksplit) {
     using C = Cfg<MT, KP>;
     constexpr int CG = C::CG, LC = C::LC, NR = C::NR;
+    using BRaw = std::conditional_t<CANON, BRawCanon, BRawPacked>;
+    const uint32_t *pc = static_cast<const uint32_t *>(wc);
+    const uint8_t *cc = static_cast<const uint8_t *>(wc);
     __shared__ __attribute__((aligned(1024))) uint8_t lds[C::LDS];
     const uint32_t lds0 = lds_addr(lds);
 
@@ -174,7 +222,11 @@ void dq_gemm_kernel(const uint16_t *__restrict__ x, int M, int64_t K, int64_t N,
     constexpr int XBLK = MT * kSC;
     constexpr int XT = (XBLK + kWaves - 1) / kWaves;
     const int nx = XBLK / kWaves + (wv < XBLK % kWaves ? 1 : 0);
-    const int cnt = nx + LC + 1;                 // load instructions per slot for this wave
+    // Canonical metadata of a slot (kSC chunks x 32 rows x CG groups x 4 B)
+    // goes in 256-byte instructions, instruction e by wave e.
+    constexpr int NMETA = kSC * 32 * CG * 4 / 256;
+    const int nm = CANON ? (wv < NMETA ? 1 : 0) : 1;
+    const int cnt = nx + LC + nm;                // load instructions per slot for this wave
 
     // Loop-invariant lane offsets of the loads (the per-chunk part of every
     // address is wave-uniform and stays in SGPRs).  X rows past M are
@@ -190,7 +242,34 @@ void dq_gemm_kernel(const uint16_t *__restrict__ x, int M, int64_t K, int64_t N,
         xoff[t] = (uint32_t)(grow * K * 2 + (((lane & 3) ^ xswz(row)) * 16));
     }
     const uint32_t coff = (uint32_t)lane * 16;
-    const uint32_t moff = (uint32_t)((lane >> 3) * KP * ng * 128 + (lane & 7) * 16);
+    uint32_t moff = (uint32_t)((lane >> 3) * KP * ng * 128 + (lane & 7) * 16);
+    constexpr int RPM = 64 / CG;                 // canonical metadata rows per instruction
+    int mchunk = 0;                              // chunk of the slot that this wave's instruction fills
+    if constexpr (CANON) {
+        const int srow = wv * RPM + lane / CG;   // row of the slot (0..63)
+        const int row = srow % 32;
+        int64_t grp = (int64_t)bx * CG + ((lane % CG) ^ mswz(row));
+        if (grp >= ng) grp = ng - 1;
+        moff = (uint32_t)((row * ng + grp) * 4);
+        mchunk = (wv * RPM) / 32;
+    }
+    // Canonical codes: the workgroup's code rows of a slot (kSC chunks x 32
+    // rows x CG groups x 32 bytes) are loaded 1 KB per instruction, RPD rows
+    // each, instruction d by wave d / LC.  Lane l takes 16-byte piece
+    // (l % (2 CG)) ^ cswz(row) of row l / (2 CG), so the pieces land
+    // swizzled; pieces of groups past N re-read the last group.
+    constexpr int RPD = 32 / CG;
+    const int64_t halfN = N >> 1;
+    uint32_t ccoff[LC];
+#pragma unroll
+    for (int lc = 0; lc < LC; ++lc) {
+        const int d = wv * LC + lc;
+        const int row = (d * RPD) % 32 + lane / (2 * CG);
+        const int p = (lane % (2 * CG)) ^ cswz(row);
+        int64_t grp = (int64_t)bx * CG + (p >> 1);
+        if (grp >= ng) grp = ng - 1;
+        ccoff[lc] = (uint32_t)(row * halfN + grp * 32 + (p & 1) * 16);
+    }
 
     f32x4 acc[MT][4];
 #pragma unroll
@@ -199,6 +278,13 @@ void dq_gemm_kernel(const uint16_t *__restrict__ x, int M, int64_t K, int64_t N,
         for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     const int arow = lane & 15, akq = lane >> 4;
+    // The AND-OR masks and magic numbers of the canonical dequantisation, held
+    // in VGPRs so that each AND-OR is one three-operand bit operation (two of
+    // its operands could not both be scalar or literal).
+    uint32_t kmask[2] = {0x000F000Fu, 0x00F000F0u}, kmagic[2] = {0x64006400u, 0x54005400u};
+    if constexpr (CANON) {
+        asm volatile("" : "+v"(kmask[0]), "+v"(kmask[1]), "+v"(kmagic[0]), "+v"(kmagic[1]));
+    }
     const int aoff = phase * C::XCHUNK + arow * 64 + ((akq ^ xswz(arow)) * 16);
 
     // Issue this wave's direct-to-LDS loads for the slot of kSC chunks that
@@ -220,35 +306,77 @@ void dq_gemm_kernel(const uint16_t *__restrict__ x, int M, int64_t K, int64_t N,
         const int k1 = kc0 + phase;              // this wave's first chunk of the slot
 #pragma unroll
         for (int lc = 0; lc < LC; ++lc) {
-            int kc = k1 + lc * KP;
-            if (kc >= c_end) kc = c_end - 1;
-            dma16(pc + ((int64_t)kc * ng + gl) * 256, coff, sb + C::XBYTES + (wv * LC + lc) * 1024);
+            if constexpr (CANON) {
+                const int d = wv * LC + lc;
+                int kc = kc0 + (d * RPD) / 32;
+                if (kc >= c_end) kc = c_end - 1;
+                dma16(cc + (int64_t)kc * 32 * halfN, ccoff[lc], sb + C::XBYTES + d * 1024);
+            } else {
+                int kc = k1 + lc * KP;
+                if (kc >= c_end) kc = c_end - 1;
+                dma16(pc + ((int64_t)kc * ng + gl) * 256, coff, sb + C::XBYTES + (wv * LC + lc) * 1024);
+            }
         }
         const int kc = k1 < c_end ? k1 : c_end - 1;
         const int left = (c_end - kc + KP - 1) / KP;     // own chunks left from kc on (>= 1)
-        const int nmeta = 8 * (left < LC ? left : LC);
-        if (lane < nmeta) dma16(pm + ((int64_t)kc * ng + gl) * 32, moff, sb + C::XBYTES + C::BBYTES + wv * LC * 128);
+        // canonical: instruction wv fills bytes [256 wv, 256 wv + 256) of the
+        // slot's metadata; packed: each wave's 128 bytes per own chunk
+        const uint32_t mdst = sb + C::XBYTES + C::BBYTES + wv * (CANON ? 256 : LC * 128);
+        if constexpr (CANON) {
+            if (wv < NMETA) {
+                int mk = kc0 + mchunk;
+                if (mk >= c_end) mk = c_end - 1;
+                dma4(wm + (int64_t)mk * 32 * ng, moff, mdst);
+            }
+        } else {
+            const int nmeta = 8 * (left < LC ? left : LC);
+            if (lane < nmeta) dma16(wm + ((int64_t)kc * ng + gl) * 32, moff, mdst);
+        }
     };
 
     // Half h (0..7) of the dequantisation of one chunk's B fragments: n-tile
-    // j = h/2, k-values 0..3 (h even) or 4..7 (h odd) of the packed word.
-    // One AND leaves a code pair in the mantissas of two fp16 subnormals:
-    // q * 2^-24 (codes 0, 1 of the pair of pairs) or q * 2^-20 (codes 2, 3).
-    // The packed steps are pre-scaled by 2^(24 - e) and 2^(20 - e) and the
-    // minima by 2^-e, so one packed FMA gives 2^-e * fp16(min + q * step)
-    // with a single rounding (the product is exact); the epilogue multiplies
-    // by 2^e.
-    auto dequant_half = [&](const uint4 cw, const uint4 ms, const uint4 mm, int h, u32x4(&b)[4]) {
+    // j = h/2, k-values 0..3 (h even) or 4..7 (h odd).
+    //  * packed: one AND leaves a code pair in the mantissas of two fp16
+    //    subnormals, q * 2^-24 (codes 0, 1 of the pair of pairs) or q * 2^-20
+    //    (codes 2, 3); the packed steps are pre-scaled by 2^(24 - e) and
+    //    2^(20 - e) and the minima by 2^-e, so one packed FMA gives
+    //    2^-e * fp16(min + q * step) with a single rounding (the product is
+    //    exact); the epilogue multiplies by 2^e.
+    //  * canonical: nibble j of a row's 16-bit read is the code of output
+    //    channel 4c + j.  An AND-OR puts it in the mantissa of 1024 + q
+    //    (nibbles 0, 2: bits 0-3) or 64 + q (nibbles 1, 3: bits 4-7), an
+    //    exact packed subtract leaves q, and one packed FMA gives
+    //    fp16(min + q * step) rounded once, for two k rows at a time.
+    auto dequant_half = [&](const BRaw &raw, int h, u32x4(&b)[4]) {
         const int j = h >> 1;
-        const uint32_t W[4] = {cw.x, cw.y, cw.z, cw.w};
-        const uint32_t w = (h & 1) ? W[j] >> 8 : W[j];
-        const uint32_t s0 = (h & 1) ? ms.z : ms.x, s1 = (h & 1) ? ms.w : ms.y;
-        const uint32_t n0 = (h & 1) ? mm.z : mm.x, n1 = (h & 1) ? mm.w : mm.y;
-        const f16x2 c0 = as_f16x2(w & 0x000F000Fu);
-        const f16x2 c1 = as_f16x2(w & 0x00F000F0u);
-        const f16x2 w0 = __builtin_elementwise_fma(c0, as_f16x2(s0), as_f16x2(n0));
-        const f16x2 w1 = __builtin_elementwise_fma(c1, as_f16x2(s1), as_f16x2(n1));
-        const uint32_t u0 = __builtin_bit_cast(uint32_t, w0), u1 = __builtin_bit_cast(uint32_t, w1);
+        uint32_t u0, u1;
+        if constexpr (CANON) {
+            const bool odd = j & 1;
+            const uint32_t mask = odd ? kmask[1] : kmask[0];
+            const uint32_t magic = odd ? kmagic[1] : kmagic[0];
+            const _Float16 bias = odd ? (_Float16)64.0f : (_Float16)1024.0f;
+            const f16x2 b2 = {bias, bias};
+            uint32_t uu[2];
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const int p = (h & 1) * 2 + e;
+                const uint32_t src = j >= 2 ? raw.v[p] >> 8 : raw.v[p];
+                const f16x2 q = as_f16x2((src & mask) | magic) - b2;
+                uu[e] = as_u32(__builtin_elementwise_fma(q, as_f16x2(raw.sp[p]), as_f16x2(raw.mp[p])));
+            }
+            u0 = uu[0];
+            u1 = uu[1];
+        } else {
+            const uint4 cw = raw.cw, ms = raw.ms, mm = raw.mm;
+            const uint32_t W[4] = {cw.x, cw.y, cw.z, cw.w};
+            const uint32_t w = (h & 1) ? W[j] >> 8 : W[j];
+            const uint32_t s0 = (h & 1) ? ms.z : ms.x, s1 = (h & 1) ? ms.w : ms.y;
+            const uint32_t n0 = (h & 1) ? mm.z : mm.x, n1 = (h & 1) ? mm.w : mm.y;
+            const f16x2 c0 = as_f16x2(w & 0x000F000Fu);
+            const f16x2 c1 = as_f16x2(w & 0x00F000F0u);
+            u0 = as_u32(__builtin_elementwise_fma(c0, as_f16x2(s0), as_f16x2(n0)));
+            u1 = as_u32(__builtin_elementwise_fma(c1, as_f16x2(s1), as_f16x2(n1)));
+        }
         // An empty use pins the values here: the next chunk may be past the
         // end of the split, and without it the compiler sinks this work past
         // that test, out of the MFMA shadow.
@@ -256,14 +384,40 @@ void dq_gemm_kernel(const uint16_t *__restrict__ x, int M, int64_t K, int64_t N,
         b[j][(h & 1) * 2] = u0;
         b[j][(h & 1) * 2 + 1] = u1;
     };
-    // Packed code words and (step, min) pairs of this wave's chunk lc of ring
-    // slot `slot`.
-    auto load_b = [&](int slot, int lc, uint4 &cw, uint4 &ms, uint4 &mm) {
+    // Canonical layout: lane (q = lane/16, c = lane%16) reads bytes 2c, 2c+1
+    // of its group's 32 bytes in k rows 8q..8q+7 of a chunk (rows CG*32
+    // bytes apart, pieces swizzled by cswz(8q + i) = 2q).
+    const int cboff = akq * 8 * CG * 32 + (((2 * cg + (arow >> 3)) ^ (2 * akq)) * 16) + ((2 * arow) & 15);
+    // ... and the metadata of its group in those rows (mswz(8q + i) = q).
+    const int cmoff = (akq * 8 * CG + (cg ^ akq)) * 4;
+    // Raw B operands of this wave's chunk lc of ring slot `slot`: the packed
+    // code words and (step, min) pairs, or the canonical code rows and
+    // metadata words.
+    auto load_b = [&](int slot, int lc, BRaw &raw) {
         const uint8_t *base = lds + slot * C::SLOT;
-        cw = *reinterpret_cast<const uint4 *>(base + C::XBYTES + (wv * LC + lc) * 1024 + lane * 16);
         const uint8_t *mb = base + C::XBYTES + C::BBYTES + (wv * LC + lc) * 128 + akq * 32;
-        ms = *reinterpret_cast<const uint4 *>(mb);
-        mm = *reinterpret_cast<const uint4 *>(mb + 16);
+        if constexpr (CANON) {
+            const uint8_t *mc = base + C::XBYTES + C::BBYTES + (phase + lc * KP) * 32 * CG * 4 + cmoff;
+            const uint8_t *cb = base + C::XBYTES + (phase + lc * KP) * CG * 1024 + cboff;
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+                const uint32_t lo = *reinterpret_cast<const uint16_t *>(cb + (2 * p) * CG * 32);
+                const uint32_t hi = *reinterpret_cast<const uint16_t *>(cb + (2 * p + 1) * CG * 32);
+                raw.v[p] = __builtin_amdgcn_perm(hi, lo, 0x05040100u);   // (lo.b0, lo.b1, hi.b0, hi.b1)
+            }
+            uint32_t mw[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) mw[i] = *reinterpret_cast<const uint32_t *>(mc + i * CG * 4);
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+                raw.sp[p] = __builtin_amdgcn_perm(mw[2 * p + 1], mw[2 * p], 0x07060302u);   // (step, step)
+                raw.mp[p] = __builtin_amdgcn_perm(mw[2 * p + 1], mw[2 * p], 0x05040100u);   // (min, min)
+            }
+        } else {
+            raw.cw = *reinterpret_cast<const uint4 *>(base + C::XBYTES + (wv * LC + lc) * 1024 + lane * 16);
+            raw.ms = *reinterpret_cast<const uint4 *>(mb);
+            raw.mm = *reinterpret_cast<const uint4 *>(mb + 16);
+        }
     };
     // A fragment of m-tile i of this wave's chunk lc of ring slot `slot`.
     auto a_frag = [&](int slot, int lc, int i) {
@@ -290,10 +444,10 @@ void dq_gemm_kernel(const uint16_t *__restrict__ x, int M, int64_t K, int64_t N,
         for (int r = 0; r < NR - 1; ++r) issue(c_begin + r * kSC, r);
         wait_slots<NR - 2>(cnt);                 // this wave's loads of the first slot
         lds_barrier();                           // ... and every wave's
-        uint4 cw, ms, mm;
-        load_b(0, 0, cw, ms, mm);
+        BRaw raw;
+        load_b(0, 0, raw);
 #pragma unroll
-        for (int h = 0; h < 8; ++h) dequant_half(cw, ms, mm, h, bf[0]);
+        for (int h = 0; h < 8; ++h) dequant_half(raw, h, bf[0]);
 #pragma unroll
         for (int d = 0; d < PD; ++d) ap[d] = a_frag(0, 0, d);
     }
@@ -314,20 +468,35 @@ void dq_gemm_kernel(const uint16_t *__restrict__ x, int M, int64_t K, int64_t N,
                 // last slot, which takes no barrier.
                 if (st * kSC + phase + lc * KP >= nmine) break;
                 // The next chunk's B words: in this slot, or (last chunk of
-                // the slot) this wave's own loads of the next slot, for which
-                // its vmcnt is enough.  Slot st+1 is only certain to have
-                // landed once this slot's refill is issued (at most NR-2
-                // slots outstanding after it), so in a slot's first chunk
-                // that load waits for the refill and the dequantisation
-                // starts one m-tile later.
+                // the slot) this wave's own loads of the next slot (packed),
+                // for which its vmcnt is enough.  Slot st+1 is only certain
+                // to have landed once this slot's refill is issued (at most
+                // NR-2 slots outstanding after it), so in a slot's first
+                // chunk that load waits for the refill and the
+                // dequantisation starts one m-tile later.  The canonical
+                // code rows and metadata of a slot come from every wave's
+                // loads, so there a barrier publishes the next slot first
+                // (the barrier later in the chunk still frees this slot).
                 const bool last = lc + 1 == LC;
                 const bool late = last && lc == 0;
-                uint4 cw, ms, mm;
-                if (!last) {
-                    load_b(r, lc + 1, cw, ms, mm);
-                } else if (!late) {
+                BRaw raw;
+                auto load_next_slot = [&]() {
                     wait_slots<NR - 2>(cnt);
-                    load_b((r + 1) % NR, 0, cw, ms, mm);
+                    if constexpr (CANON) {
+                        if (st + 1 < nslots) {
+                            lds_barrier();
+                            load_b((r + 1) % NR, 0, raw);
+                        } else {
+                            raw = BRaw{};
+                        }
+                    } else {
+                        load_b((r + 1) % NR, 0, raw);
+                    }
+                };
+                if (!last) {
+                    load_b(r, lc + 1, raw);
+                } else if (!late) {
+                    load_next_slot();
                 }
                 const int bi = (u * LC + lc) % 2;
                 const u32x4(&bcur)[4] = bf[bi];
@@ -353,15 +522,12 @@ void dq_gemm_kernel(const uint16_t *__restrict__ x, int M, int64_t K, int64_t N,
                             ap[0], __builtin_bit_cast(f16x8, bcur[j]), acc[i][j], 0, 0, 0);
                     if (lc == 0 && i == 0) {
                         issue(c_begin + (st + NR - 1) * kSC, (r + NR - 1) % NR);
-                        if (late) {
-                            wait_slots<NR - 2>(cnt);
-                            load_b((r + 1) % NR, 0, cw, ms, mm);
-                        }
+                        if (late) load_next_slot();
                     }
 #pragma unroll
                     for (int h = 0; h < 8; ++h) {
                         const int at = (late && MT > 1) ? 1 + (h * (MT - 1)) / 8 : (h * MT) / 8;
-                        if (at == i) dequant_half(cw, ms, mm, h, bnext);
+                        if (at == i) dequant_half(raw, h, bnext);
                     }
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
@@ -405,53 +571,48 @@ void dq_gemm_kernel(const uint16_t *__restrict__ x, int M, int64_t K, int64_t N,
     }
 
     if (!gvalid || phase != 0) return;
-    // ---- undo the column group's exponent (a power of two: exact)
-    const float gscale = __builtin_amdgcn_ldexpf(1.0f, (int)pm[(int64_t)nchunks * ng * 32 + g]);
+    if constexpr (!CANON) {
+        // ---- undo the column group's exponent (a power of two: exact)
+        const float gscale = __builtin_amdgcn_ldexpf(1.0f, (int)wm[(int64_t)nchunks * ng * 32 + g]);
+#pragma unroll
+        for (int i = 0; i < MT; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[i][j] *= gscale;
+    }
+    // ---- store: lane holds rows 4*(lane/16)+r of each 16x16 tile, MFMA
+    // column lane%16, which is output channel 64g + 16j + lane%16 (packed)
+    // or 64g + 4(lane%16) + j (canonical: four consecutive channels)
+    const int crow = (lane >> 4) * 4, ccol = lane & 15;
+    const int64_t col0 = g * 64 + (CANON ? 4 * ccol : ccol);
+    auto store_row = [&](auto *dst, int i, int r) {
+        using T = std::remove_pointer_t<decltype(dst)>;
+        if constexpr (CANON) {
+            if constexpr (std::is_same_v<T, float>) {
+                *reinterpret_cast<f32x4 *>(dst) = f32x4{acc[i][0][r], acc[i][1][r], acc[i][2][r], acc[i][3][r]};
+            } else {
+                typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+                *reinterpret_cast<f16x4 *>(dst) = f16x4{(_Float16)acc[i][0][r], (_Float16)acc[i][1][r],
+                                                         (_Float16)acc[i][2][r], (_Float16)acc[i][3][r]};
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) dst[j * 16] = (T)acc[i][j][r];
+        }
+    };
+    float *fbase = ksplit > 1 ? part + (int64_t)split * M * N : static_cast<float *>(y);
+    const bool f16out = ksplit == 1 && y_f16;
 #pragma unroll
     for (int i = 0; i < MT; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] *= gscale;
-    // ---- store: lane holds rows 4*(lane/16)+r, column lane%16 of each 16x16 tile
-    const int crow = (lane >> 4) * 4, ccol = lane & 15;
-    const int64_t col0 = g * 64 + ccol;
-    if (ksplit > 1) {
-        float *pbase = part + (int64_t)split * M * N;
-#pragma unroll
-        for (int i = 0; i < MT; ++i)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int row = m0 + i * 16 + crow + r;
-                if (row < M) {
-                    float *prow = pbase + (int64_t)row * N + col0;
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) prow[j * 16] = acc[i][j][r];
-                }
+        for (int r = 0; r < 4; ++r) {
+            const int row = m0 + i * 16 + crow + r;
+            if (row < M) {
+                if (f16out)
+                    store_row(static_cast<_Float16 *>(y) + (int64_t)row * N + col0, i, r);
+                else
+                    store_row(fbase + (int64_t)row * N + col0, i, r);
             }
-    } else if (y_f16) {
-#pragma unroll
-        for (int i = 0; i < MT; ++i)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int row = m0 + i * 16 + crow + r;
-                if (row < M) {
-                    _Float16 *yrow = static_cast<_Float16 *>(y) + (int64_t)row * N + col0;
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) yrow[j * 16] = (_Float16)acc[i][j][r];
-                }
-            }
-    } else {
-#pragma unroll
-        for (int i = 0; i < MT; ++i)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int row = m0 + i * 16 + crow + r;
-                if (row < M) {
-                    float *yrow = static_cast<float *>(y) + (int64_t)row * N + col0;
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) yrow[j * 16] = acc[i][j][r];
-                }
-            }
-    }
+        }
 }
 
 // Y = sum over splits of the partial tiles, in split order.
@@ -472,13 +633,29 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *__restr
     }
 }
 
-template <int MT>
+template <int MT, bool CANON>
 void launch_mt(int kp, dim3 grid, hipStream_t stream, const uint16_t *x, int M, int64_t K, int64_t N,
-               const uint32_t *pc, const uint32_t *pm, int cps, float *part, void *y, int f16, int ksplit) {
+               const void *wc, const uint32_t *wm, int cps, float *part, void *y, int f16, int ksplit) {
     if (kp == 2)
-        dq_gemm_kernel<MT, 2><<<grid, dim3(kThreads), 0, stream>>>(x, M, K, N, pc, pm, cps, part, y, f16, ksplit);
+        dq_gemm_kernel<MT, 2, CANON><<<grid, dim3(kThreads), 0, stream>>>(x, M, K, N, wc, wm, cps, part, y, f16, ksplit);
     else
-        dq_gemm_kernel<MT, 1><<<grid, dim3(kThreads), 0, stream>>>(x, M, K, N, pc, pm, cps, part, y, f16, ksplit);
+        dq_gemm_kernel<MT, 1, CANON><<<grid, dim3(kThreads), 0, stream>>>(x, M, K, N, wc, wm, cps, part, y, f16, ksplit);
+}
+
+template <bool CANON>
+void launch_layout(int mt, int kp, dim3 grid, hipStream_t stream, const uint16_t *x, int M, int64_t K, int64_t N,
+                   const void *wc, const uint32_t *wm, int cps, float *part, void *y, int f16, int ksplit) {
+    switch (mt) {
+        case 1: launch_mt<1, CANON>(kp, grid, stream, x, M, K, N, wc, wm, cps, part, y, f16, ksplit); break;
+        case 2: launch_mt<2, CANON>(kp, grid, stream, x, M, K, N, wc, wm, cps, part, y, f16, ksplit); break;
+        case 3: launch_mt<3, CANON>(kp, grid, stream, x, M, K, N, wc, wm, cps, part, y, f16, ksplit); break;
+        case 4: launch_mt<4, CANON>(kp, grid, stream, x, M, K, N, wc, wm, cps, part, y, f16, ksplit); break;
+        case 5: launch_mt<5, CANON>(kp, grid, stream, x, M, K, N, wc, wm, cps, part, y, f16, ksplit); break;
+        case 6: launch_mt<6, CANON>(kp, grid, stream, x, M, K, N, wc, wm, cps, part, y, f16, ksplit); break;
+        case 7: launch_mt<7, CANON>(kp, grid, stream, x, M, K, N, wc, wm, cps, part, y, f16, ksplit); break;
+        case 8: launch_mt<8, CANON>(kp, grid, stream, x, M, K, N, wc, wm, cps, part, y, f16, ksplit); break;
+        default: launch_mt<9, CANON>(kp, grid, stream, x, M, K, N, wc, wm, cps, part, y, f16, ksplit); break;
+    }
 }
 
 }  // namespace
@@ -541,8 +718,10 @@ size_t gemm_ws_bytes(int64_t M, int64_t K, int64_t N) {
     return (size_t)p.ksplit * (size_t)M * (size_t)N * sizeof(float);
 }
 
-fgq_status launch_dequant_gemm(const void *x, int64_t M, int64_t K, int64_t N, const uint32_t *pc,
-                               const uint32_t *pm, void *y, int32_t y_dtype, void *ws, hipStream_t stream) {
+// canonical: wc = uint8 codes [K][N/2], wm = uint32 meta [K][N/64];
+// otherwise the packed layout of fgq_pack_weight_g64.
+fgq_status launch_dequant_gemm(const void *x, int64_t M, int64_t K, int64_t N, const void *wc, const uint32_t *wm,
+                               bool canonical, void *y, int32_t y_dtype, void *ws, hipStream_t stream) {
     if (M == 0 || N == 0) return FGQ_OK;
     const GemmPlan p = gemm_plan(M, K, N);
     if (p.mblocks > 65535 || (double)p.nblocks * p.ksplit * p.mblocks >= 2147483648.0)
@@ -551,18 +730,12 @@ fgq_status launch_dequant_gemm(const void *x, int64_t M, int64_t K, int64_t N, c
     const dim3 grid((unsigned)p.nblocks, (unsigned)p.ksplit, (unsigned)p.mblocks);
     const uint16_t *xh = static_cast<const uint16_t *>(x);
     float *part = static_cast<float *>(ws);
-    const int cps = p.chunks_per_split, ks = p.ksplit, kp = p.kp;
-    switch (p.mt) {
-        case 1: launch_mt<1>(kp, grid, stream, xh, (int)M, K, N, pc, pm, cps, part, y, f16, ks); break;
-        case 2: launch_mt<2>(kp, grid, stream, xh, (int)M, K, N, pc, pm, cps, part, y, f16, ks); break;
-        case 3: launch_mt<3>(kp, grid, stream, xh, (int)M, K, N, pc, pm, cps, part, y, f16, ks); break;
-        case 4: launch_mt<4>(kp, grid, stream, xh, (int)M, K, N, pc, pm, cps, part, y, f16, ks); break;
-        case 5: launch_mt<5>(kp, grid, stream, xh, (int)M, K, N, pc, pm, cps, part, y, f16, ks); break;
-        case 6: launch_mt<6>(kp, grid, stream, xh, (int)M, K, N, pc, pm, cps, part, y, f16, ks); break;
-        case 7: launch_mt<7>(kp, grid, stream, xh, (int)M, K, N, pc, pm, cps, part, y, f16, ks); break;
-        case 8: launch_mt<8>(kp, grid, stream, xh, (int)M, K, N, pc, pm, cps, part, y, f16, ks); break;
-        default: launch_mt<9>(kp, grid, stream, xh, (int)M, K, N, pc, pm, cps, part, y, f16, ks); break;
-    }
+    if (canonical)
+        launch_layout<true>(p.mt, p.kp, grid, stream, xh, (int)M, K, N, wc, wm, p.chunks_per_split, part, y, f16,
+                            p.ksplit);
+    else
+        launch_layout<false>(p.mt, p.kp, grid, stream, xh, (int)M, K, N, wc, wm, p.chunks_per_split, part, y, f16,
+                             p.ksplit);
     fgq_status s = check_launch("dq_gemm_kernel");
     if (s != FGQ_OK || p.ksplit == 1) return s;
     const int64_t MN = M * N;   // N % 64 == 0, so MN % 4 == 0

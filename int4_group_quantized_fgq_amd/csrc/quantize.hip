@@ -134,7 +134,7 @@ struct AppendPos {
 
 __device__ __forceinline__ AppendPos append_pos(uint32_t g2, const fgq_kv_cache &kv, int lg, const FastDiv &div_n,
                                                 const FastDiv &div_h, const uint16_t *k_new,
-                                                const uint16_t *v_new, int32_t pos, int sub) {
+                                                const uint16_t *v_new, int64_t ld, int32_t pos, int sub) {
     const uint32_t gi = g2 & ((1u << lg) - 1u);
     const uint32_t r1 = g2 >> lg;                  // (which, b, head, i)
     const uint32_t r2 = fastdiv(r1, div_n);        // (which, b, head)
@@ -143,9 +143,8 @@ __device__ __forceinline__ AppendPos append_pos(uint32_t g2, const fgq_kv_cache 
     const uint32_t hd = r2 - r3 * div_h.d;
     const int which = r3 >= (uint32_t)kv.batch ? 1 : 0;
     const uint32_t b = r3 - (which ? (uint32_t)kv.batch : 0u);
-    const int64_t hidden = (int64_t)kv.heads * kv.head_dim;
     AppendPos p;
-    p.src = (which ? v_new : k_new) + ((int64_t)b * div_n.d + i) * hidden + (int64_t)hd * kv.head_dim + gi * 64 +
+    p.src = (which ? v_new : k_new) + ((int64_t)b * div_n.d + i) * ld + (int64_t)hd * kv.head_dim + gi * 64 +
             sub * 8;
     p.slot = ((int64_t)b * kv.heads + hd) * kv.capacity + pos + i;
     p.gi = gi;
@@ -156,7 +155,7 @@ __device__ __forceinline__ AppendPos append_pos(uint32_t g2, const fgq_kv_cache 
 template <int GPT>
 __global__ __launch_bounds__(256) void kv_append_kernel(const uint16_t *__restrict__ k_new,
                                                         const uint16_t *__restrict__ v_new,
-                                                        fgq_kv_cache kv, int32_t pos, uint32_t total,
+                                                        fgq_kv_cache kv, int64_t ld, int32_t pos, uint32_t total,
                                                         FastDiv div_n, FastDiv div_h) {
     const int lg = kv.head_dim == 128 ? 1 : 0;              // log2(groups per head)
     const int sub = threadIdx.x & 7;
@@ -165,7 +164,7 @@ __global__ __launch_bounds__(256) void kv_append_kernel(const uint16_t *__restri
 #pragma unroll
     for (int k = 0; k < GPT; ++k) {
         const uint32_t gid = blockIdx.x * (32u * GPT) + 32u * k + (threadIdx.x >> 3);
-        p[k] = append_pos(gid < total ? gid : 0u, kv, lg, div_n, div_h, k_new, v_new, pos, sub);
+        p[k] = append_pos(gid < total ? gid : 0u, kv, lg, div_n, div_h, k_new, v_new, ld, pos, sub);
         raw[k] = make_uint4(0u, 0u, 0u, 0u);
         if (gid < total) raw[k] = *reinterpret_cast<const uint4 *>(p[k].src);
     }
@@ -295,14 +294,14 @@ fgq_status launch_quantize(const void *x, int64_t rows, int64_t cols, int64_t ld
     return FGQ_OK;
 }
 
-fgq_status launch_kv_append(const fgq_kv_cache *kv, const void *k_new, const void *v_new, int32_t pos,
+// k_new / v_new rows (one per sequence and new token) are ld elements apart.
+fgq_status launch_kv_append(const fgq_kv_cache *kv, const void *k_new, const void *v_new, int64_t ld, int32_t pos,
                             int32_t n_new, hipStream_t stream) {
     const int64_t gph = kv->head_dim / 64;
     const int64_t per_seq = 2LL * n_new * kv->heads * gph;   // groups of one sequence (K and V)
     if (per_seq == 0 || kv->batch == 0) return FGQ_OK;
     const int64_t seq_per = kMaxGroupsPerLaunch / per_seq > 0 ? kMaxGroupsPerLaunch / per_seq : 1;
     const FastDiv div_n = make_fastdiv((uint32_t)n_new), div_h = make_fastdiv((uint32_t)kv->heads);
-    const int64_t hidden = (int64_t)kv->heads * kv->head_dim;
     const int64_t rows = (int64_t)kv->heads * kv->capacity;   // cache rows of one sequence
     for (int64_t b0 = 0; b0 < kv->batch; b0 += seq_per) {
         const int64_t nb = kv->batch - b0 < seq_per ? kv->batch - b0 : seq_per;
@@ -313,15 +312,15 @@ fgq_status launch_kv_append(const fgq_kv_cache *kv, const void *k_new, const voi
         sub.k_meta = kv->k_meta + b0 * rows * gph;
         sub.v_meta = kv->v_meta + b0 * rows * gph;
         const int64_t groups = nb * per_seq;
-        const uint16_t *kn = static_cast<const uint16_t *>(k_new) + b0 * n_new * hidden;
-        const uint16_t *vn = static_cast<const uint16_t *>(v_new) + b0 * n_new * hidden;
+        const uint16_t *kn = static_cast<const uint16_t *>(k_new) + b0 * n_new * ld;
+        const uint16_t *vn = static_cast<const uint16_t *>(v_new) + b0 * n_new * ld;
         if (groups >= kAppendManyGroups) {
             constexpr int G2 = FGQ_APPEND_GPT;
             kv_append_kernel<G2><<<dim3((unsigned)((groups + 32 * G2 - 1) / (32 * G2))), dim3(256), 0, stream>>>(
-                kn, vn, sub, pos, (uint32_t)groups, div_n, div_h);
+                kn, vn, sub, ld, pos, (uint32_t)groups, div_n, div_h);
         } else {
             kv_append_kernel<1><<<dim3((unsigned)((groups + 31) / 32)), dim3(256), 0, stream>>>(
-                kn, vn, sub, pos, (uint32_t)groups, div_n, div_h);
+                kn, vn, sub, ld, pos, (uint32_t)groups, div_n, div_h);
         }
         fgq_status s = check_launch("kv_append_kernel");
         if (s != FGQ_OK) return s;

@@ -139,13 +139,29 @@ def pack(codes_d, meta_d, K, N):
 
 
 def gemm(x16: np.ndarray, g: int, m: int, pc, pm, K: int, N: int, y_f16: bool = False, xd=None):
+    """Block GEMM over the packed layout (fgq_dequant_gemm_packed)."""
     torch = torch_cuda()
     M = g * m
     xd = to_dev(x16) if xd is None else xd
     y = torch.empty((M, N), dtype=torch.float16 if y_f16 else torch.float32, device="cuda")
     wsb = fgq.fgq_dequant_gemm_ws_bytes(M, K, N)
     ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device="cuda")
-    fgq.fgq_dequant_gemm(xd, g, m, K, N, pc, pm, y, fgq.FGQ_DTYPE_F16 if y_f16 else fgq.FGQ_DTYPE_F32, ws, wsb)
+    fgq.fgq_dequant_gemm_packed(xd, g, m, K, N, pc, pm, y, fgq.FGQ_DTYPE_F16 if y_f16 else fgq.FGQ_DTYPE_F32, ws,
+                                wsb)
+    torch.cuda.synchronize()
+    return to_host(y).astype(np.float32)
+
+
+def gemm_canonical(x16: np.ndarray, g: int, m: int, codes_d, meta_d, K: int, N: int, y_f16: bool = False, xd=None):
+    """Block GEMM straight from the quantiser's codes [K][N/2] and meta [K][N/64] (fgq_dequant_gemm)."""
+    torch = torch_cuda()
+    M = g * m
+    xd = to_dev(x16) if xd is None else xd
+    y = torch.empty((M, N), dtype=torch.float16 if y_f16 else torch.float32, device="cuda")
+    wsb = fgq.fgq_dequant_gemm_ws_bytes(M, K, N)
+    ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device="cuda")
+    fgq.fgq_dequant_gemm(xd, g, m, K, N, codes_d, meta_d, y, fgq.FGQ_DTYPE_F16 if y_f16 else fgq.FGQ_DTYPE_F32, ws,
+                         wsb)
     torch.cuda.synchronize()
     return to_host(y).astype(np.float32)
 

@@ -22,7 +22,8 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = fgq.declared_symbols()
-    assert {"fgq_quantize_g64", "fgq_kv_append", "fgq_decode_attn_q4kv", "fgq_dequant_gemm"} <= set(names)
+    assert {"fgq_quantize_g64", "fgq_kv_append", "fgq_decode_attn_q4kv", "fgq_dequant_gemm",
+            "fgq_dequant_gemm_packed", "fgq_kv_append_ld", "fgq_decode_attn_q4kv_ld"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
     out = subprocess.run(["nm", "-D", "--defined-only", fgq.LIB_PATH], stdout=subprocess.PIPE, text=True).stdout
@@ -32,14 +33,14 @@ def test_every_declared_symbol_is_exported(lib):
 
 def test_header_compiles_as_plain_c(tmp_path):
     src = tmp_path / "t.c"
-    src.write_text('#include "fgq.h"\nint main(void){ fgq_kv_cache kv; (void)kv; return fgq_abi_version() != 2; }\n')
+    src.write_text('#include "fgq.h"\nint main(void){ fgq_kv_cache kv; (void)kv; return fgq_abi_version() != 3; }\n')
     inc = os.path.join(os.path.dirname(fgq.HEADER_PATH))
     subprocess.check_call(["gcc", "-std=c99", "-Wall", "-Werror", "-c", str(src), "-I", inc, "-o",
                            str(tmp_path / "t.o")])
 
 
 def test_version_and_status_strings(lib):
-    assert fgq.fgq_abi_version() == 2
+    assert fgq.fgq_abi_version() == 3
     assert fgq.status_string(fgq.FGQ_OK) == "ok"
     codes = [fgq.FGQ_ERR_INVALID_ARG, fgq.FGQ_ERR_SHAPE, fgq.FGQ_ERR_ALIGN, fgq.FGQ_ERR_CAPACITY,
              fgq.FGQ_ERR_WORKSPACE, fgq.FGQ_ERR_DTYPE, fgq.FGQ_ERR_DEVICE, fgq.FGQ_ERR_UNSUPPORTED]
@@ -180,8 +181,59 @@ def test_prefill_attention_validation(lib):
     assert _status(lambda: p(0, 0, 0, 2, 0, 2, 128, 0.0, 0, 0, 0)) == fgq.FGQ_OK     # empty prompt
 
 
-def test_gemm_validation_and_workspace(lib):
+def test_canonical_gemm_signature_matches_the_survey_boundary(lib):
+    """fgq_dequant_gemm takes the quantiser's own layout: uint8 codes
+    [K][N/2] and the metadata words [K][N/64], as const pointers."""
+    import re
+    text = open(fgq.HEADER_PATH).read()
+    m = re.search(r"fgq_status fgq_dequant_gemm\((.*?)\);", text, re.S)
+    params = [p.strip() for p in " ".join(m.group(1).split()).split(",")]
+    assert params == ["const void *x_f16", "int32_t g", "int32_t m", "int64_t K", "int64_t N",
+                      "const uint8_t *w_codes", "const void *w_meta", "void *y", "int32_t y_dtype", "void *ws",
+                      "size_t ws_bytes", "void *stream"]
+
+
+def test_canonical_gemm_validation(lib):
     gm = fgq.fgq_dequant_gemm
+    # the canonical layout takes K in multiples of 64 (the packed one: 32)
+    assert _status(lambda: gm(GOOD, 4, 1, 96, 64, GOOD, GOOD, GOOD, 0, 0, 0, 0)) == fgq.FGQ_ERR_SHAPE
+    assert _status(lambda: gm(GOOD, 4, 1, 64, 96, GOOD, GOOD, GOOD, 0, 0, 0, 0)) == fgq.FGQ_ERR_SHAPE
+    assert _status(lambda: gm(GOOD, 4, 1, 64, 2 ** 28, GOOD, GOOD, GOOD, 0, 0, 0, 0)) == fgq.FGQ_ERR_SHAPE
+    assert _status(lambda: gm(GOOD, 4, 1, 64, 64, GOOD, GOOD, GOOD, 5, 0, 0, 0)) == fgq.FGQ_ERR_DTYPE
+    assert _status(lambda: gm(GOOD, 4, -1, 64, 64, GOOD, GOOD, GOOD, 0, 0, 0, 0)) == fgq.FGQ_ERR_INVALID_ARG
+    assert _status(lambda: gm(GOOD, 4, 1, 64, 64, GOOD, BAD, GOOD, 0, 0, 0, 0)) == fgq.FGQ_ERR_ALIGN
+    assert _status(lambda: gm(GOOD, 4, 1, 64, 64, GOOD, 0, GOOD, 0, 0, 0, 0)) == fgq.FGQ_ERR_INVALID_ARG
+    assert _status(lambda: gm(0, 4, 0, 64, 64, 0, 0, 0, 0, 0, 0, 0)) == fgq.FGQ_OK   # empty block
+    need = fgq.fgq_dequant_gemm_ws_bytes(144, 12288, 12288)
+    assert _status(lambda: gm(GOOD, 36, 4, 12288, 12288, GOOD, GOOD, GOOD, 0, 0, 0, 0)) == fgq.FGQ_ERR_WORKSPACE
+    assert _status(lambda: gm(GOOD, 36, 4, 12288, 12288, GOOD, GOOD, GOOD, 0, BAD, need, 0)) == fgq.FGQ_ERR_ALIGN
+
+
+def test_strided_append_and_attention_validation(lib):
+    a = fgq.fgq_kv_append_ld
+    h = 2 * 128
+    assert _status(lambda: a(_kv(), GOOD, GOOD, h - 8, 0, 1, 0)) == fgq.FGQ_ERR_SHAPE
+    assert _status(lambda: a(_kv(), GOOD, GOOD, 3 * h + 4, 0, 1, 0)) == fgq.FGQ_ERR_ALIGN
+    assert _status(lambda: a(_kv(), GOOD, GOOD, 3 * h, 10, 7, 0)) == fgq.FGQ_ERR_CAPACITY
+    assert _status(lambda: a(_kv(), BAD, GOOD, 3 * h, 0, 1, 0)) == fgq.FGQ_ERR_ALIGN
+    assert _status(lambda: a(_kv(), GOOD, GOOD, 3 * h, 0, 0, 0)) == fgq.FGQ_OK          # nothing to append
+    d = fgq.fgq_decode_attn_q4kv_ld
+    assert _status(lambda: d(_kv(), GOOD, h - 8, 4, 0.0, GOOD, 0, 0, 0, 0)) == fgq.FGQ_ERR_SHAPE
+    assert _status(lambda: d(_kv(), GOOD, 3 * h + 4, 4, 0.0, GOOD, 0, 0, 0, 0)) == fgq.FGQ_ERR_ALIGN
+    assert _status(lambda: d(_kv(), GOOD, 3 * h, 17, 0.0, GOOD, 0, 0, 0, 0)) == fgq.FGQ_ERR_CAPACITY
+    assert _status(lambda: d(_kv(), GOOD, 3 * h, 4, 0.0, GOOD, 3, 0, 0, 0)) == fgq.FGQ_ERR_DTYPE
+
+
+def test_attention_rejects_more_than_2_31_work_items(lib):
+    """batch * heads beyond the kernel's 32-bit item index is a shape error
+    on the host, not a wrapped grid."""
+    d = fgq.fgq_decode_attn_q4kv
+    big = _kv(batch=2 ** 20, heads=2 ** 12, cap=16)
+    assert _status(lambda: d(big, GOOD, 4, 0.0, GOOD, 0, GOOD, 2 ** 40, 0)) == fgq.FGQ_ERR_SHAPE
+
+
+def test_gemm_validation_and_workspace(lib):
+    gm = fgq.fgq_dequant_gemm_packed
     assert _status(lambda: gm(GOOD, 4, 1, 48, 64, GOOD, GOOD, GOOD, 0, 0, 0, 0)) == fgq.FGQ_ERR_SHAPE
     assert _status(lambda: gm(GOOD, 4, 1, 64, 96, GOOD, GOOD, GOOD, 0, 0, 0, 0)) == fgq.FGQ_ERR_SHAPE
     assert _status(lambda: gm(GOOD, 4, 1, 64, 64, GOOD, GOOD, GOOD, 5, 0, 0, 0)) == fgq.FGQ_ERR_DTYPE

@@ -1,0 +1,278 @@
+"""The decode layer as a chain with its real data flow, on the GPU through
+the C ABI, against the same chain of oracle calls.
+
+One decode step of one layer for a block of B = g*m sequences:
+  qkv  = X0 * [Wq | Wk | Wv]                (fp16 out, [B][3h])
+  fgq_kv_append_ld(k = qkv[:, h:2h], v = qkv[:, 2h:3h], ld = 3h)
+  attn = attention(q = qkv[:, :h], ld_q = 3h, over prompt + t positions)  (fp16 out)
+  y1   = attn * Wout,  y2 = y1 * W1,  y3 = y2 * W2                        (fp16 out)
+(paper-graph-ui FlexGen summary, section 3 "Technical Approach", the
+computational graph of Figure 2: each operation's output feeds the next
+one and the layer's K and V persist in the cache.)  The layer's
+normalisations, residual sums and FFN activation are not part of the
+compressed path and are not applied: each product's fp16 output is the next
+one's input.
+
+Checks:
+ * stage by stage: every GPU stage against the oracle applied to the GPU's
+   own input of that stage: cache codes bit-exact; products and attention
+   rerun with fp32 output on the same inputs, to the 1e-2 / 1e-3 bar, and
+   the fp16 output the chain handed on equal, bit for bit, to that fp32
+   output rounded to nearest even (fp16 outputs reach |Y| ~ 20 in the
+   OPT-175B chain, where one fp16 step is already 0.0156).  Without the
+   layer's norms the activations grow 2-4x per product, and the 1e-2
+   absolute bar is the configs' one for N(0, 1) inputs; a product is linear
+   in its input, so each one is compared on its input divided by that
+   input's rms (when above 1), which is the same GEMM at the configs' scale;
+ * end to end: the GPU's last output against the chain computed by oracle
+   calls alone, each hand-off rounded to fp16 (round to nearest even) as the
+   GPU hands it on.  That chain sees its own q, k, v, so its cache differs
+   where a last-digit difference flips a code, and its products restore the
+   weights in fp32 where the GPU restores them in fp16; attention's weighted
+   average turns a relative change of its inputs into a ~10x larger one of
+   its small output.  Two valid chains therefore differ by ~3e-3 rel-L2
+   (tests/test_oracle_chain.py pins this on the CPU), and the end-to-end bar
+   is max-abs 5e-2 and rel-L2 1e-2 (END_ATOL, END_RTOL).
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests import gpu_util as gu
+
+try:
+    import torch
+    _HAS_GPU = torch.cuda.is_available()
+except ImportError:   # pragma: no cover
+    _HAS_GPU = False
+
+pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not _HAS_GPU, reason="needs an MI355X GPU")]
+
+W = synth.WORKLOADS
+F16 = gu.fgq.FGQ_DTYPE_F16
+END_ATOL, END_RTOL = 5e-2, 1e-2     # end-to-end bar against the independent oracle chain (see above)
+
+
+def _layer_weights(w):
+    """fp16 host weights of one layer: Wq|Wk|Wv side by side, Wout, W1, W2."""
+    qkv = np.concatenate([synth.weight(w, i) for i in (0, 1, 2)], axis=1)
+    return [qkv, synth.weight(w, 3), synth.weight(w, 4), synth.weight(w, 5)]
+
+
+def _layer_input(w, t):
+    """The layer input of decode step t: fp16 [B][h] ~ N(0, 1)."""
+    key = synth.stream_key(w.cid, synth.T_GEMM_X, 0, t)
+    return synth.to_f16(synth.normal(key, w.batch * w.hidden)).reshape(w.batch, w.hidden)
+
+
+class GpuChain:
+    """The weights compressed on the GPU (canonical codes, and the packed
+    layout), the cache with the prompt appended, and the chain's buffers."""
+
+    def __init__(self, w, canonical):
+        torch = gu.torch_cuda()
+        self.w, self.canonical = w, canonical
+        B, h = w.batch, w.hidden
+        self.host_w = _layer_weights(w)
+        self.codes, self.meta, self.packed = [], [], []
+        for Wt in self.host_w:
+            K, N = Wt.shape
+            wd = gu.to_dev(Wt)
+            c = torch.empty((K, N // 2), dtype=torch.uint8, device="cuda")
+            m = torch.empty((K, N // 64), dtype=torch.int32, device="cuda")
+            gu.fgq.fgq_quantize_g64(wd, K, N, N, c, m)
+            del wd
+            self.codes.append(c)
+            self.meta.append(m)
+            self.packed.append(gu.pack(c, m, K, N) if not canonical else None)
+        self.kv = gu.DevKV(B, w.heads, w.head_dim, w.capacity)
+        for b0 in range(0, B, 8):
+            nb = min(8, B - b0)
+            sub = gu.fgq.kv_struct(self.kv.k_codes[b0:b0 + nb], self.kv.v_codes[b0:b0 + nb],
+                                   self.kv.k_meta[b0:b0 + nb], self.kv.v_meta[b0:b0 + nb], nb, w.heads,
+                                   w.head_dim, w.capacity)
+            gu.fgq.fgq_kv_append(sub, gu.to_dev(synth.prompt_kv(w, "k", b0=b0, nb=nb)),
+                                 gu.to_dev(synth.prompt_kv(w, "v", b0=b0, nb=nb)), 0, w.prompt)
+        self.qkv = torch.empty((B, 3 * h), dtype=torch.float16, device="cuda")
+        self.attn = torch.empty((B, h), dtype=torch.float16, device="cuda")
+        self.y = [torch.empty((B, Wt.shape[1]), dtype=torch.float16, device="cuda") for Wt in self.host_w[1:]]
+        gws = max(gu.fgq.fgq_dequant_gemm_ws_bytes(B, *Wt.shape) for Wt in self.host_w)
+        self.gws = torch.empty(max(gws, 16), dtype=torch.uint8, device="cuda")
+        aws = max(gu.fgq.fgq_decode_attn_ws_bytes(B, w.heads, w.head_dim, L)
+                  for L in range(w.prompt + 1, w.capacity + 1))
+        self.aws = torch.empty(max(aws, 16), dtype=torch.uint8, device="cuda")
+        torch.cuda.synchronize()
+
+    def gemm(self, i, x, y, dtype=F16):
+        w = self.w
+        K, N = self.host_w[i].shape
+        if self.canonical:
+            gu.fgq.fgq_dequant_gemm(x, w.g, w.m, K, N, self.codes[i], self.meta[i], y, dtype, self.gws,
+                                    self.gws.numel())
+        else:
+            pc, pm = self.packed[i]
+            gu.fgq.fgq_dequant_gemm_packed(x, w.g, w.m, K, N, pc, pm, y, dtype, self.gws, self.gws.numel())
+
+    def step(self, x0_dev, t):
+        """One decode step; returns nothing (outputs stay in the buffers)."""
+        w = self.w
+        h = w.hidden
+        self.x0 = x0_dev
+        self.gemm(0, x0_dev, self.qkv)
+        q, k, v = self.qkv[:, :h], self.qkv[:, h:2 * h], self.qkv[:, 2 * h:]
+        gu.fgq.fgq_kv_append_ld(self.kv.struct, k, v, 3 * h, w.prompt + t - 1, 1)
+        gu.fgq.fgq_decode_attn_q4kv_ld(self.kv.struct, q, 3 * h, w.prompt + t, 0.0, self.attn, F16, self.aws,
+                                       self.aws.numel())
+        self.gemm(1, self.attn, self.y[0])
+        self.gemm(2, self.y[0], self.y[1])
+        self.gemm(3, self.y[1], self.y[2])
+
+
+def _f16(a):
+    return np.asarray(a, np.float32).astype(np.float16)
+
+
+def _stage_checks(ch, x0, t, seqs, col_slices=None):
+    """Every stage of the GPU's step t against the oracle on the GPU's own
+    stage inputs; col_slices=None compares whole products, else those
+    256-column whole-group slices."""
+    w = ch.w
+    B, h = w.batch, w.hidden
+    hc = [gu.to_host(c) for c in ch.codes]
+    hm = [gu.to_host(m, np.uint32) for m in ch.meta]
+    torch = gu.torch_cuda()
+    qkv = gu.to_host(ch.qkv)
+    attn = gu.to_host(ch.attn)
+    ys = [gu.to_host(y) for y in ch.y]
+    ins = [x0, attn, ys[0], ys[1]]
+    ins_dev = [ch.x0, ch.attn, ch.y[0], ch.y[1]]
+    outs = [qkv] + ys
+    for i, Wt in enumerate(ch.host_w):
+        N = Wt.shape[1]
+        y32d = torch.empty((B, N), dtype=torch.float32, device="cuda")
+        ch.gemm(i, ins_dev[i], y32d, gu.fgq.FGQ_DTYPE_F32)
+        torch.cuda.synchronize()
+        y32 = gu.to_host(y32d)
+        assert np.array_equal(outs[i], y32.astype(np.float16)), "fp16 hand-off of gemm %d is not RNE(fp32)" % i
+        for n0 in ([0] if col_slices is None else [s for s in col_slices(N)]):
+            n1 = N if col_slices is None else n0 + 256
+            rc, rm = oracle.quantize_g64(np.ascontiguousarray(Wt[:, n0:n1]))
+            assert np.array_equal(hc[i][:, n0 // 2:n1 // 2], rc) and np.array_equal(hm[i][:, n0 // 64:n1 // 64], rm)
+            exp = oracle.dequant_gemm(ins[i], w.g, w.m, rc, rm)
+            sc = max(1.0, float(np.sqrt(np.mean(ins[i].astype(np.float64) ** 2))))
+            gu.assert_close(y32[:, n0:n1] / sc, exp / sc, "stage gemm %d cols %d.. (input rms %.3g)" % (i, n0, sc))
+    # attention of this step rerun with fp32 output (it reads the cache, writes nothing else)
+    o32d = torch.empty((B, h), dtype=torch.float32, device="cuda")
+    gu.fgq.fgq_decode_attn_q4kv_ld(ch.kv.struct, ch.qkv, 3 * h, w.prompt + t, 0.0, o32d, gu.fgq.FGQ_DTYPE_F32,
+                                   ch.aws, ch.aws.numel())
+    torch.cuda.synchronize()
+    o32 = gu.to_host(o32d)
+    assert np.array_equal(attn, o32.astype(np.float16)), "fp16 attention output is not RNE(fp32)"
+    # the cache rows appended this step, and attention, for the sampled sequences
+    kv = ch.kv.host()
+    for b in seqs:
+        ref = oracle.KVCache(1, w.heads, w.head_dim, w.capacity)
+        oracle.kv_append(ref, synth.prompt_kv(w, "k", b0=b, nb=1), synth.prompt_kv(w, "v", b0=b, nb=1), 0)
+        for a in ("k_codes", "k_meta", "v_codes", "v_meta"):
+            assert np.array_equal(kv[a][b][:, :w.prompt], getattr(ref, a)[0][:, :w.prompt]), (a, b)
+        oracle.kv_append(ref, qkv[b:b + 1, None, h:2 * h], qkv[b:b + 1, None, 2 * h:], w.prompt + t - 1)
+        pos = slice(w.prompt + t - 1, w.prompt + t)
+        for a in ("k_codes", "k_meta", "v_codes", "v_meta"):
+            assert np.array_equal(kv[a][b][:, pos], getattr(ref, a)[0][:, pos]), ("appended", a, b)
+        # positions between the prompt and this step were appended by earlier steps: take the GPU's
+        for a in ("k_codes", "k_meta", "v_codes", "v_meta"):
+            getattr(ref, a)[0][:, w.prompt:w.prompt + t - 1] = kv[a][b][:, w.prompt:w.prompt + t - 1]
+        exp = oracle.decode_attn(ref, qkv[b:b + 1, :h], w.prompt + t)
+        gu.assert_close(o32[b:b + 1], exp, "stage attention seq %d" % b)
+
+
+def _oracle_chain(ch, x0, t_steps, x0s):
+    """The whole chain from oracle calls alone over decode steps 1..t_steps;
+    returns the last step's output (fp32 of the fp16 hand-off)."""
+    w = ch.w
+    B, h = w.batch, w.hidden
+    codes = [oracle.quantize_g64(Wt) for Wt in ch.host_w]
+    ref = oracle.KVCache(B, w.heads, w.head_dim, w.capacity)
+    oracle.kv_append(ref, synth.prompt_kv(w, "k"), synth.prompt_kv(w, "v"), 0)
+    y = None
+    for t in range(1, t_steps + 1):
+        qkv = _f16(oracle.dequant_gemm(x0s[t], w.g, w.m, *codes[0]))
+        oracle.kv_append(ref, qkv[:, None, h:2 * h], qkv[:, None, 2 * h:], w.prompt + t - 1)
+        a = _f16(oracle.decode_attn(ref, qkv[:, :h], w.prompt + t))
+        y1 = _f16(oracle.dequant_gemm(a, w.g, w.m, *codes[1]))
+        y2 = _f16(oracle.dequant_gemm(y1, w.g, w.m, *codes[2]))
+        y = _f16(oracle.dequant_gemm(y2, w.g, w.m, *codes[3]))
+    return y.astype(np.float32)
+
+
+@pytest.mark.parametrize("canonical", [True, False])
+def test_chain_opt67b_stagewise_and_end_to_end(canonical):
+    """OPT-6.7B layer, B = 64: two decode steps of the chain; every stage of
+    step 2 against the oracle on the GPU's stage inputs, and the last output
+    of step 2 against the oracle-only chain."""
+    w = W["opt-6.7b"]
+    gu.note("chain opt-6.7b canonical=%s" % canonical)
+    ch = GpuChain(w, canonical)
+    x0s = {t: _layer_input(w, t) for t in (1, 2)}
+    for t in (1, 2):
+        ch.step(gu.to_dev(x0s[t]), t)
+    torch = gu.torch_cuda()
+    torch.cuda.synchronize()
+    _stage_checks(ch, x0s[2], 2, seqs=(0, 31, 63))
+    exp = _oracle_chain(ch, x0s[2], 2, x0s)
+    got = gu.to_host(ch.y[2]).astype(np.float32)
+    assert np.all(np.isfinite(got))
+    max_abs, rel = gu.metrics(got, exp)
+    gu.note("chain end to end (W2 output): max_abs=%.3e rel_l2=%.3e (bar %.0e / %.0e)" %
+            (max_abs, rel, END_ATOL, END_RTOL))
+    assert max_abs <= END_ATOL and rel <= END_RTOL, (max_abs, rel)
+
+
+def test_chain_opt175b_stagewise_sampled():
+    """OPT-175B layer, B = 144, the bench's launch configuration (packed
+    weights): one decode step of the chain, every stage against the oracle on
+    the GPU's stage inputs, on three sampled sequences and three 256-column
+    slices of every product."""
+    w = W["opt-175b"]
+    gu.note("chain opt-175b sampled")
+    ch = GpuChain(w, canonical=False)
+    x0 = _layer_input(w, 1)
+    ch.step(gu.to_dev(x0), 1)
+    torch = gu.torch_cuda()
+    torch.cuda.synchronize()
+    _stage_checks(ch, x0, 1, seqs=(0, 77, 143), col_slices=lambda N: (0, N // 2 + 64, N - 256))
+
+
+def test_strided_entries_equal_contiguous_ones():
+    """fgq_kv_append_ld and fgq_decode_attn_q4kv_ld over rows 3h apart give
+    the same bytes as the contiguous calls on copies of those rows."""
+    torch = gu.torch_cuda()
+    w = W["opt-6.7b"]
+    nb, h = 3, w.hidden
+    rng = np.random.default_rng(5)
+    buf = rng.standard_normal((nb, 3 * h)).astype(np.float16)
+    gu.note("strided append/attention")
+    a = gu.DevKV(nb, w.heads, w.head_dim, 40)
+    b = gu.DevKV(nb, w.heads, w.head_dim, 40)
+    pk = synth.prompt_kv(w, "k", nb=nb, nt=30)
+    pv = synth.prompt_kv(w, "v", nb=nb, nt=30)
+    a.append(pk, pv, 0)
+    b.append(pk, pv, 0)
+    d = gu.to_dev(buf)
+    gu.fgq.fgq_kv_append_ld(a.struct, d[:, h:2 * h], d[:, 2 * h:], 3 * h, 30, 1)
+    b.append(np.ascontiguousarray(buf[:, None, h:2 * h]), np.ascontiguousarray(buf[:, None, 2 * h:]), 30)
+    ha, hb = a.host(), b.host()
+    for key in ha:
+        assert np.array_equal(ha[key], hb[key]), key
+    out = torch.empty((nb, h), dtype=torch.float32, device="cuda")
+    wsb = gu.fgq.fgq_decode_attn_ws_bytes(nb, w.heads, w.head_dim, 31)
+    ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device="cuda")
+    gu.fgq.fgq_decode_attn_q4kv_ld(a.struct, d, 3 * h, 31, 0.0, out, gu.fgq.FGQ_DTYPE_F32, ws, wsb)
+    torch.cuda.synchronize()
+    got = gu.to_host(out)
+    assert np.array_equal(got, b.attend(np.ascontiguousarray(buf[:, :h]), 31))
+    ref = oracle.KVCache(nb, w.heads, w.head_dim, 40)
+    oracle.kv_append(ref, pk, pv, 0)
+    oracle.kv_append(ref, buf[:, None, h:2 * h], buf[:, None, 2 * h:], 30)
+    gu.assert_close(got, oracle.decode_attn(ref, buf[:, :h], 31), "strided attention vs oracle")

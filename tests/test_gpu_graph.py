@@ -51,7 +51,7 @@ class _Step:
                                     attn_ws.numel(), s)
         for i, (_, K, N) in enumerate(GEMMS):
             pc, pm = self.weights[i]
-            gu.fgq.fgq_dequant_gemm(self.x[i], G, MB, K, N, pc, pm, self.y[i], gu.fgq.FGQ_DTYPE_F32, gemm_ws,
+            gu.fgq.fgq_dequant_gemm_packed(self.x[i], G, MB, K, N, pc, pm, self.y[i], gu.fgq.FGQ_DTYPE_F32, gemm_ws,
                                     gemm_ws.numel(), s)
 
     def outputs(self):

@@ -56,6 +56,16 @@ def test_prefill_fp16_output_and_scale():
     gu.assert_close(_gpu(q, k, v, H, scale=0.3), oracle.prefill_attn(q, k, v, H, scale=0.3), "prefill scale 0.3")
 
 
+def test_prefill_long_launch_fp16_output_and_scale():
+    """The 12-wave launch (prompts of 1024+ tokens, Q staged in LDS) with
+    fp16 output and an explicit softmax scale."""
+    B, s, H, D = 1, 1030, 2, 128
+    q, k, v = _qkv(B, s, H, D, 40)
+    gu.note("prefill 12-wave fp16 out / scale 0.07")
+    exp = oracle.prefill_attn(q, k, v, H, scale=0.07)
+    gu.assert_close(_gpu(q, k, v, H, scale=0.07, out_f16=True), exp, "prefill 12-wave fp16 out scale 0.07")
+
+
 def test_prefill_workload_shape_sampled_rows():
     """OPT-175B attention shape (96 heads of 128, prompt 512) for 8 sequences
     of the prompt's synthetic K and V: the first and last rows of every

@@ -36,7 +36,7 @@ def test_streamed_weights_double_buffered_match_resident():
     ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device="cuda")
 
     def gemm(x, pc, pm, y, s):
-        gu.fgq.fgq_dequant_gemm(x, g, m, K, N, pc, pm, y, gu.fgq.FGQ_DTYPE_F32, ws, wsb, s)
+        gu.fgq.fgq_dequant_gemm_packed(x, g, m, K, N, pc, pm, y, gu.fgq.FGQ_DTYPE_F32, ws, wsb, s)
 
     main = torch.cuda.current_stream()
     resident = []
