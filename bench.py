@@ -862,14 +862,16 @@ def summarize_trace(folder: str, w, steps: int) -> None:
     print("| step (sum) | | %.1f |" % tot)
 
 
-# Unit-utilisation figures from raw counters (per dispatch, summed over the
-# counter's dimensions), with rocprofv3's own derived-metric formulas:
+# Unit-utilisation figures from raw counters.  rocprofv3 reports each counter
+# per dispatch summed over its dimensions; the GRBM counters run once per XCD,
+# so their per-XCD value (rocprof's reduce(..., max)) is the sum / 8 on
+# MI355X.  rocprofv3's own derived-metric formulas:
 #   MfmaUtil  = 100 * SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE * SIMD_NUM)
 #   VALUBusy  = 100 * SQ_ACTIVE_INST_VALU / CU_NUM / GRBM_GUI_ACTIVE
 #   Occupancy = 400 * SQ_WAVE_CYCLES / GRBM_GUI_ACTIVE / CU_NUM / 32   (% of 32 wave slots per CU)
 #   LdsBankConflict (% of LDS-active cycles stalled) = 100 * SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE
 #   LdsUtil   = 100 * SQ_LDS_IDX_ACTIVE / (GRBM_GUI_ACTIVE * CU_NUM)
-CU_NUM, SIMD_NUM = 256, 1024
+CU_NUM, SIMD_NUM, XCD_NUM = 256, 1024, 8
 
 
 def summarize_counters(folders, kernels) -> None:
@@ -908,12 +910,15 @@ def summarize_counters(folders, kernels) -> None:
         def pct(a, b, f=1.0):
             return "%.1f" % (100.0 * f * a / b) if a is not None and b else "-"
         gui = g("GRBM_GUI_ACTIVE")
+        gui = gui / XCD_NUM if gui else gui
         mf = g("SQ_INSTS_MFMA")
         valu = g("SQ_INSTS_VALU")
         row = {
             "dispatches": max(cnt.values()),
             "gui_active": gui,
             "mfma_busy": pct(g("SQ_VALU_MFMA_BUSY_CYCLES"), gui and gui * SIMD_NUM),
+            "mfma_cycles_per_inst": "%.1f" % (g("SQ_VALU_MFMA_BUSY_CYCLES") / mf)
+            if g("SQ_VALU_MFMA_BUSY_CYCLES") is not None and mf else "-",
             "valu_busy": pct(g("SQ_ACTIVE_INST_VALU"), gui and gui * CU_NUM),
             "valu_per_mfma": "%.2f" % ((valu - mf) / mf) if valu is not None and mf else "-",
             "lds_per_mfma": "%.2f" % (g("SQ_INSTS_LDS") / mf) if g("SQ_INSTS_LDS") is not None and mf else "-",
