@@ -46,7 +46,8 @@
  *    thread's last failure.
  *  - Inputs must be finite (precondition; the result is undefined otherwise).
  *  - Calls are reentrant; the library holds no mutable global state besides
- *    the per-thread error text.
+ *    the per-thread error text and, for fgq_decode_attn_q4kv_noalloc only,
+ *    one fixed scratch array per GPU (see there).
  */
 #ifndef FGQ_H
 #define FGQ_H
@@ -173,6 +174,23 @@ fgq_status fgq_decode_attn_q4kv(const fgq_kv_cache *kv, const void *q_f16, int32
 fgq_status fgq_decode_attn_q4kv_ld(const fgq_kv_cache *kv, const void *q_f16, int64_t ld_q, int32_t kv_len,
                                    float softmax_scale, void *out, int32_t out_dtype,
                                    void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * fgq_decode_attn_q4kv_noalloc - fgq_decode_attn_q4kv for callers that cannot
+ * allocate device memory (code under graph capture, tight serving loops,
+ * harnesses that forbid allocation): the same kernels and result, with the
+ * per-split softmax states kept in a fixed scratch array inside the library
+ * (FGQ_NOALLOC_SCRATCH_BYTES per GPU, held until the process ends) instead of
+ * a workspace argument.  It allocates nothing.  The split plan never needs
+ * more than 8,650,224 bytes of states; a call that would is rejected with
+ * FGQ_ERR_WORKSPACE.  Every call on one GPU shares that GPU's scratch: calls
+ * that overlap on one GPU (two streams, or two threads) race and must be
+ * ordered by the caller.  The first call on a device looks up the scratch's
+ * device address (FGQ_ERR_DEVICE if that fails).
+ */
+#define FGQ_NOALLOC_SCRATCH_BYTES ((size_t)9 << 20)
+fgq_status fgq_decode_attn_q4kv_noalloc(const fgq_kv_cache *kv, const void *q_f16, int32_t kv_len,
+                                        float softmax_scale, void *out, int32_t out_dtype, void *stream);
 
 /*
  * fgq_decode_attn_gqa_q4kv - decode attention with grouped K/V heads (GQA) or

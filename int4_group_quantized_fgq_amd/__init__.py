@@ -28,6 +28,7 @@ FGQ_ERR_DEVICE = -7
 FGQ_ERR_UNSUPPORTED = -8
 FGQ_DTYPE_F32 = 0
 FGQ_DTYPE_F16 = 1
+FGQ_NOALLOC_SCRATCH_BYTES = 9 << 20
 
 _lib = None
 
@@ -67,6 +68,7 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
         "fgq_decode_attn_ws_bytes": ([i32, i32, i32, i32], sz),
         "fgq_decode_attn_q4kv": ([kvp, vp, i32, f32, vp, i32, vp, sz, vp], i32),
         "fgq_decode_attn_q4kv_ld": ([kvp, vp, i64, i32, f32, vp, i32, vp, sz, vp], i32),
+        "fgq_decode_attn_q4kv_noalloc": ([kvp, vp, i32, f32, vp, i32, vp], i32),
         "fgq_decode_attn_topk_q4kv": ([kvp, vp, i32, i32, f32, vp, i32, vp, vp], i32),
         "fgq_decode_attn_gqa_ws_bytes": ([i32, i32, i32, i32, i32], sz),
         "fgq_decode_attn_gqa_q4kv": ([kvp, vp, i32, i32, f32, vp, i32, vp, sz, vp], i32),
@@ -162,6 +164,11 @@ def fgq_decode_attn_q4kv_ld(kv: fgq_kv_cache, q, ld_q, kv_len, softmax_scale, ou
                             stream=None) -> None:
     _check(load().fgq_decode_attn_q4kv_ld(ctypes.byref(kv), _ptr(q), ld_q, kv_len, softmax_scale, _ptr(out),
                                           out_dtype, _ptr(ws), ws_bytes, _stream(stream)), "fgq_decode_attn_q4kv_ld")
+
+
+def fgq_decode_attn_q4kv_noalloc(kv: fgq_kv_cache, q, kv_len, softmax_scale, out, out_dtype, stream=None) -> None:
+    _check(load().fgq_decode_attn_q4kv_noalloc(ctypes.byref(kv), _ptr(q), kv_len, softmax_scale, _ptr(out),
+                                               out_dtype, _stream(stream)), "fgq_decode_attn_q4kv_noalloc")
 
 
 def fgq_decode_attn_gqa_ws_bytes(batch, q_heads, kv_heads, head_dim, kv_len) -> int:

@@ -16,6 +16,8 @@ fgq_status launch_kv_append(const fgq_kv_cache *kv, const void *k_new, const voi
 fgq_status launch_pack_weight(const uint8_t *codes, const uint32_t *meta, int64_t K, int64_t N,
                               uint32_t *packed_codes, uint32_t *packed_meta, hipStream_t stream);
 size_t attn_ws_bytes(int32_t batch, int32_t heads, int32_t head_dim, int32_t kv_len);
+size_t attn_scratch_bytes();
+fgq_status attn_scratch_ptr(void **ptr);
 fgq_status launch_decode_attn(const fgq_kv_cache *kv, const void *q, int64_t ld_q, int32_t kv_len, float scale,
                               void *out, int32_t out_dtype, void *ws, hipStream_t stream);
 size_t gqa_ws_bytes(int32_t batch, int32_t q_heads, int32_t kv_heads, int32_t head_dim, int32_t kv_len);
@@ -129,10 +131,11 @@ size_t fgq_decode_attn_ws_bytes(int32_t batch, int32_t heads, int32_t head_dim, 
     return attn_ws_bytes(batch, heads, head_dim, kv_len);
 }
 
-fgq_status fgq_decode_attn_q4kv_ld(const fgq_kv_cache *kv, const void *q_f16, int64_t ld_q, int32_t kv_len,
-                                   float softmax_scale, void *out, int32_t out_dtype, void *ws, size_t ws_bytes,
-                                   void *stream) {
-    g_err[0] = 0;
+// Host validation shared by the dense decode attention entry points (nothing
+// about the workspace); *noop is set when there is nothing to compute.
+static fgq_status check_attn(const fgq_kv_cache *kv, const void *q_f16, int64_t ld_q, int32_t kv_len,
+                             float softmax_scale, const void *out, int32_t out_dtype, bool *noop) {
+    *noop = false;
     fgq_status s = check_kv(kv);
     if (s != FGQ_OK) return s;
     if (out_dtype != FGQ_DTYPE_F32 && out_dtype != FGQ_DTYPE_F16)
@@ -144,10 +147,43 @@ fgq_status fgq_decode_attn_q4kv_ld(const fgq_kv_cache *kv, const void *q_f16, in
     if (ld_q < hidden) return fail(FGQ_ERR_SHAPE, "ld_q %lld < heads * head_dim %lld", (long long)ld_q,
                                    (long long)hidden);
     if ((int64_t)kv->batch * kv->heads > INT32_MAX) return fail(FGQ_ERR_SHAPE, "batch * heads > 2^31 - 1");
-    if (kv->batch == 0 || kv->heads == 0) return FGQ_OK;
+    if (kv->batch == 0 || kv->heads == 0) {
+        *noop = true;
+        return FGQ_OK;
+    }
     if (!q_f16 || !out) return fail(FGQ_ERR_INVALID_ARG, "NULL q or out");
     if (!aligned16(q_f16) || !aligned16(out) || ld_q % 8 != 0)
         return fail(FGQ_ERR_ALIGN, "q (and its rows) and out must be 16-byte aligned");
+    return FGQ_OK;
+}
+
+fgq_status fgq_decode_attn_q4kv_noalloc(const fgq_kv_cache *kv, const void *q_f16, int32_t kv_len,
+                                        float softmax_scale, void *out, int32_t out_dtype, void *stream) {
+    g_err[0] = 0;
+    bool noop = false;
+    const int64_t ld_q = kv ? (int64_t)kv->heads * kv->head_dim : 0;
+    fgq_status s = check_attn(kv, q_f16, ld_q, kv_len, softmax_scale, out, out_dtype, &noop);
+    if (s != FGQ_OK || noop) return s;
+    const size_t need = attn_ws_bytes(kv->batch, kv->heads, kv->head_dim, kv_len);
+    if (need > attn_scratch_bytes())
+        return fail(FGQ_ERR_WORKSPACE, "split states need %zu bytes, more than the library's %zu-byte scratch",
+                    need, attn_scratch_bytes());
+    void *ws = nullptr;
+    if (need > 0) {
+        s = attn_scratch_ptr(&ws);
+        if (s != FGQ_OK) return s;
+    }
+    const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt((float)kv->head_dim);
+    return launch_decode_attn(kv, q_f16, ld_q, kv_len, scale, out, out_dtype, ws, static_cast<hipStream_t>(stream));
+}
+
+fgq_status fgq_decode_attn_q4kv_ld(const fgq_kv_cache *kv, const void *q_f16, int64_t ld_q, int32_t kv_len,
+                                   float softmax_scale, void *out, int32_t out_dtype, void *ws, size_t ws_bytes,
+                                   void *stream) {
+    g_err[0] = 0;
+    bool noop = false;
+    fgq_status s = check_attn(kv, q_f16, ld_q, kv_len, softmax_scale, out, out_dtype, &noop);
+    if (s != FGQ_OK || noop) return s;
     const size_t need = attn_ws_bytes(kv->batch, kv->heads, kv->head_dim, kv_len);
     if (need > 0) {
         if (!ws || ws_bytes < need)

@@ -28,6 +28,7 @@
 //    the wave, then the exponentials and the P.V pass run with that max: the
 //    running accumulators are rescaled once per chunk, not per token.
 #include <climits>
+#include <mutex>
 #include <type_traits>
 
 #include "common.h"
@@ -381,6 +382,42 @@ AttnPlan attn_plan(int32_t batch, int32_t heads, int32_t head_dim, int32_t kv_le
     per = ((per + chunk - 1) / chunk) * chunk;
     n_split = (kv_len + per - 1) / per;   // drop empty splits
     return {n_split, per, ch};
+}
+
+// Scratch of the allocation-free entry point: a file-scope device array, one
+// copy per GPU the library runs on, held until the process ends.  It holds
+// the per-split softmax states, which the split kernel writes in full before
+// the merge kernel reads them, so it needs no clearing between calls.  The
+// split plan keeps batch * heads * splits below 2 * 8192 (a split count is
+// only chosen when batch * heads < 8192 and is then at most
+// ceil(8192 / (batch * heads))), so at most 16383 rows of (head_dim + 4)
+// floats: 8,650,224 bytes at head_dim 128.
+constexpr size_t kAttnScratchBytes = (size_t)9 << 20;
+static __device__ __align__(256) uint8_t scratch[kAttnScratchBytes];
+constexpr int kMaxDevices = 64;
+
+size_t attn_scratch_bytes() { return kAttnScratchBytes; }
+
+// Device address of `scratch` on the current device.  In host code the
+// array's name is only a stand-in for the symbol, so its address is looked
+// up once per device (with that device current) and kept.
+fgq_status attn_scratch_ptr(void **ptr) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(FGQ_ERR_DEVICE, "hipGetDevice: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices) return fail(FGQ_ERR_DEVICE, "device %d beyond %d", dev, kMaxDevices);
+    static std::mutex mu;
+    static void *addr[kMaxDevices];
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return fail(FGQ_ERR_DEVICE, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+        addr[dev] = p;
+    }
+    *ptr = addr[dev];
+    return FGQ_OK;
 }
 
 size_t attn_ws_bytes(int32_t batch, int32_t heads, int32_t head_dim, int32_t kv_len) {

@@ -23,7 +23,8 @@ def lib():
 def test_every_declared_symbol_is_exported(lib):
     names = fgq.declared_symbols()
     assert {"fgq_quantize_g64", "fgq_kv_append", "fgq_decode_attn_q4kv", "fgq_dequant_gemm",
-            "fgq_dequant_gemm_packed", "fgq_kv_append_ld", "fgq_decode_attn_q4kv_ld"} <= set(names)
+            "fgq_dequant_gemm_packed", "fgq_kv_append_ld", "fgq_decode_attn_q4kv_ld",
+            "fgq_decode_attn_q4kv_noalloc"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
     out = subprocess.run(["nm", "-D", "--defined-only", fgq.LIB_PATH], stdout=subprocess.PIPE, text=True).stdout
@@ -222,6 +223,26 @@ def test_strided_append_and_attention_validation(lib):
     assert _status(lambda: d(_kv(), GOOD, 3 * h + 4, 4, 0.0, GOOD, 0, 0, 0, 0)) == fgq.FGQ_ERR_ALIGN
     assert _status(lambda: d(_kv(), GOOD, 3 * h, 17, 0.0, GOOD, 0, 0, 0, 0)) == fgq.FGQ_ERR_CAPACITY
     assert _status(lambda: d(_kv(), GOOD, 3 * h, 4, 0.0, GOOD, 3, 0, 0, 0)) == fgq.FGQ_ERR_DTYPE
+
+
+def test_noalloc_attention_validation_and_scratch_bound(lib):
+    """The allocation-free entry validates like the workspace one, and the
+    split states of every plan fit its fixed scratch: the plan only splits
+    when batch * heads < 8192, into at most ceil(8192 / (batch * heads))
+    parts, so batch * heads * splits * (head_dim + 4) * 4 < 2 * 8192 * 132 * 4."""
+    n = fgq.fgq_decode_attn_q4kv_noalloc
+    assert _status(lambda: n(_kv(), GOOD, 0, 0.0, GOOD, 0, 0)) == fgq.FGQ_ERR_SHAPE
+    assert _status(lambda: n(_kv(), GOOD, 17, 0.0, GOOD, 0, 0)) == fgq.FGQ_ERR_CAPACITY
+    assert _status(lambda: n(_kv(), GOOD, 4, 0.0, GOOD, 9, 0)) == fgq.FGQ_ERR_DTYPE
+    assert _status(lambda: n(_kv(), BAD, 4, 0.0, GOOD, 0, 0)) == fgq.FGQ_ERR_ALIGN
+    assert _status(lambda: n(_kv(), GOOD, 4, float("nan"), GOOD, 0, 0)) == fgq.FGQ_ERR_INVALID_ARG
+    assert _status(lambda: n(_kv(batch=0), 0, 4, 0.0, 0, 0, 0)) == fgq.FGQ_OK
+    worst = 0
+    for bh in list(range(1, 300)) + [511, 512, 1000, 2047, 2048, 4095, 4096, 6000, 8191, 8192, 20000]:
+        for D in (64, 128):
+            for L in (1, 255, 256, 700, 4100, 16416, 100000):
+                worst = max(worst, fgq.fgq_decode_attn_ws_bytes(bh, 1, D, L))
+    assert 0 < worst <= 16383 * 132 * 4 <= fgq.FGQ_NOALLOC_SCRATCH_BYTES
 
 
 def test_attention_rejects_more_than_2_31_work_items(lib):
