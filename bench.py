@@ -95,6 +95,9 @@ def parse():
                     help="only summarise rocprofv3 --pmc folders of this bench (any mix of SQ/GRBM counters) "
                          "into per-kernel unit-utilisation figures")
     ap.add_argument("--kernel", default="dq_gemm_kernel", help="kernel summarised by --summarize-pmc")
+    ap.add_argument("--kernel-variant", default="",
+                    help="regular expression the kernel's full name must also match (e.g. the packed layout's "
+                         "template arguments), for --summarize-pmc")
     ap.add_argument("--summarize-trace", metavar="DIR",
                     help="only summarise a rocprofv3 --kernel-trace --stats output folder of this bench: the "
                          "kernel statistics and the steady-state duration of every launch of a step")
@@ -125,10 +128,10 @@ def source_hash(kernel: str) -> str:
     return h.hexdigest()
 
 
-def committed_traffic(kernel: str, config: str):
+def committed_traffic(kernel: str, config: str, variant: str = ""):
     """HBM bytes per launch measured by rocprofv3 counters (a 'traffic-json:'
     line of a summary under profiles/), or None when there is none for this
-    kernel and workload or the kernel's source has changed since."""
+    kernel, variant and workload or the kernel's source has changed since."""
     import glob
     for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.md"))):
         with open(path) as fh:
@@ -136,7 +139,7 @@ def committed_traffic(kernel: str, config: str):
                 if line.startswith("traffic-json: "):
                     d = json.loads(line[len("traffic-json: "):])
                     if d.get("kernel") == kernel and d.get("config") == config and \
-                            d.get("source_sha256") == source_hash(kernel):
+                            d.get("variant", "") == variant and d.get("source_sha256") == source_hash(kernel):
                         return d
     return None
 
@@ -172,9 +175,11 @@ def summarize_pmc(args):
         per = [v for v in vals if v > 0.5 * big]
         copy_bytes = args.calibrate_copy * 2 ** 20 if args.calibrate_copy else None
         fac[counter] = copy_bytes / (np.mean(per) * 1024.0) if copy_bytes else None
+    import re
     res = {}
     for counter, folder in (("FETCH_SIZE", kf), ("WRITE_SIZE", kw)):
-        vals = [v for name, v in read_pmc(folder, counter).values() if args.kernel in name]
+        vals = [v for name, v in read_pmc(folder, counter).values()
+                if args.kernel in name and re.search(args.kernel_variant, name)]
         res[counter] = (len(vals), float(np.mean(vals)) if vals else 0.0)
     return fac, res
 
@@ -871,6 +876,7 @@ def summarize_trace(folder: str, w, steps: int) -> None:
 #   Occupancy = 400 * SQ_WAVE_CYCLES / GRBM_GUI_ACTIVE / CU_NUM / 32   (% of 32 wave slots per CU)
 #   LdsBankConflict (% of LDS-active cycles stalled) = 100 * SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE
 #   LdsUtil   = 100 * SQ_LDS_IDX_ACTIVE / (GRBM_GUI_ACTIVE * CU_NUM)
+#   SIMD_UTILIZATION = SQ_BUSY_CU_CYCLES / GRBM_COUNT / CU_NUM  (GUI_ACTIVE used when GRBM_COUNT is absent)
 CU_NUM, SIMD_NUM, XCD_NUM = 256, 1024, 8
 
 
@@ -887,10 +893,10 @@ def summarize_counters(folders, kernels) -> None:
             d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
             if "Start_Timestamp" in r and r.get("End_Timestamp"):
                 durs.setdefault(name, {})[key] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
-    print("| kernel | dispatches | GUI_ACTIVE cycles | MFMA busy % | VALU busy % | VALU insts per MFMA | "
+    print("| kernel | dispatches | GUI_ACTIVE cycles | MFMA busy % | CU busy % | VALU busy % | VALU insts per MFMA | "
           "LDS insts per MFMA | occupancy % of 32 slots | LDS util % | LDS bank-conflict % of LDS-active | "
-          "MFMA-VALU co-issue % | waves waiting on LDS % |")
-    print("|---|---|---|---|---|---|---|---|---|---|---|---|")
+          "MFMA-VALU co-issue % | wave-cycles waiting to issue % | waiting on LDS % |")
+    print("|---|---|---|---|---|---|---|---|---|---|---|---|---|---|")
     out = {}
     for name in sorted(per):
         if kernels and not any(k in name for k in kernels):
@@ -926,13 +932,15 @@ def summarize_counters(folders, kernels) -> None:
             "lds_util": pct(g("SQ_LDS_IDX_ACTIVE"), gui and gui * CU_NUM),
             "lds_conflict": pct(g("SQ_LDS_BANK_CONFLICT"), g("SQ_LDS_IDX_ACTIVE")),
             "coexec": pct(g("SQ_VALU_MFMA_COEXEC_CYCLES"), g("SQ_VALU_MFMA_BUSY_CYCLES")),
+            "cu_busy": pct(g("SQ_BUSY_CU_CYCLES"), gui and gui * CU_NUM),
+            "wait_issue": pct(g("SQ_WAIT_INST_ANY"), g("SQ_WAVE_CYCLES")),
             "wait_lds": pct(g("SQ_WAIT_INST_LDS"), g("SQ_WAVE_CYCLES")),
         }
         out[name] = row
-        print("| %s | %d | %s | %s | %s | %s | %s | %s | %s | %s | %s | %s |" % (
-            name, row["dispatches"], "%.4g" % gui if gui else "-", row["mfma_busy"], row["valu_busy"],
+        print("| %s | %d | %s | %s | %s | %s | %s | %s | %s | %s | %s | %s | %s | %s |" % (
+            name, row["dispatches"], "%.4g" % gui if gui else "-", row["mfma_busy"], row["cu_busy"], row["valu_busy"],
             row["valu_per_mfma"], row["lds_per_mfma"], row["occupancy"], row["lds_util"], row["lds_conflict"],
-            row["coexec"], row["wait_lds"]))
+            row["coexec"], row["wait_issue"], row["wait_lds"]))
         dd = durs.get(name)
         if dd and gui:
             mean_us = float(np.mean(list(dd.values())))
@@ -1128,7 +1136,8 @@ def main():
         n_w, write_kib = res["WRITE_SIZE"]
         per_launch = fetch_kib * 1024.0 * fac["FETCH_SIZE"] + write_kib * 1024.0 * fac["WRITE_SIZE"]
         alg = algorithmic_bytes_per_launch(args.kernel, w, args.warmup + args.steps, args.warmup)
-        d = {"kernel": args.kernel, "config": w.name, "source_sha256": source_hash(args.kernel),
+        d = {"kernel": args.kernel, "variant": args.kernel_variant, "config": w.name,
+             "source_sha256": source_hash(args.kernel),
              "dispatches": [n_f, n_w], "fetch_kib_per_dispatch": round(fetch_kib, 1),
              "write_kib_per_dispatch": round(write_kib, 1), "fetch_factor": round(fac["FETCH_SIZE"], 4),
              "write_factor": round(fac["WRITE_SIZE"], 4), "bytes_per_launch": round(per_launch),
@@ -1229,7 +1238,8 @@ def main():
                 "unit": "GB/s", "frac": attn_gbs / HBM_PEAK_GBS, "traffic": None,
                 "algorithmic_per_launch": "1.125*hidden*kv_len bytes per sequence (+q, out); mean %.4g" %
                                           algorithmic_bytes_per_launch(kname, w)}
-    tr = committed_traffic(kname, w.name)
+    tr = committed_traffic(kname, w.name, ("false>" if args.gemm_layout == "packed" else "true>")
+                           if kname == "dq_gemm_kernel" else "")
     if tr is not None:
         roof["traffic"] = tr["bytes_per_launch"]
         roof["traffic_source"] = "rocprofv3 FETCH_SIZE + WRITE_SIZE per launch, copy-calibrated (profiles/)"
