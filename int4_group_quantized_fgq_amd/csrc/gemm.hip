@@ -57,7 +57,7 @@ namespace {
 
 constexpr int kWaves = 8;                  // waves (weight groups) per workgroup
 constexpr int kThreads = 64 * kWaves;
-constexpr int kSC = 2;                     // 32-k chunks per LDS ring slot (one barrier per slot)
+constexpr int kSCMin = 2;                  // 32-k chunks per LDS ring slot at KP <= 2 (one barrier per slot)
 constexpr int kLdsBudget = 152 * 1024;     // LDS bytes the ring may take (of 160 KB)
 
 // LDS byte address of a pointer into a __shared__ array.
@@ -140,15 +140,16 @@ __device__ __forceinline__ int cswz(int row) { return ((row >> 3) & 3) << 1; }
 __device__ __forceinline__ int mswz(int row) { return (row >> 3) & 3; }
 
 // Ring and LDS layout of a workgroup with MT m-tiles and KP k-phases: the
-// 8 waves are CG = 8/KP column groups x KP phases; phase p multiplies the
-// chunks p, p+KP, ... of every slot, and the phases' accumulators are summed
-// through LDS at the end.
+// 8 waves are CG = 8/KP column groups x KP phases; a ring slot holds SC
+// chunks, phase p multiplies the chunks p, p+KP, ... of every slot, and the
+// phases' accumulators are summed through LDS at the end.
 template <int MT, int KP>
 struct Cfg {
+    static constexpr int SC = KP > kSCMin ? KP : kSCMin;   // chunks per slot
     static constexpr int CG = kWaves / KP;             // column groups (64 channels each)
-    static constexpr int LC = kSC / KP;                // chunks per wave and slot
+    static constexpr int LC = SC / KP;                 // chunks per wave and slot
     static constexpr int XCHUNK = MT * 1024;           // MT*16 rows x 64 bytes (one 32-k chunk)
-    static constexpr int XBYTES = kSC * XCHUNK;
+    static constexpr int XBYTES = SC * XCHUNK;
     static constexpr int BBYTES = kWaves * LC * 1024;  // packed codes, 1 KB per wave and chunk
     static constexpr int MBYTES = kWaves * LC * 128;   // packed meta, 128 B per wave and chunk
     static constexpr int SLOT = XBYTES + BBYTES + MBYTES;
@@ -160,7 +161,7 @@ struct Cfg {
     static constexpr int RING = NR * SLOT;
     static constexpr int RED = (KP - 1) * CG * MT * 4 * 64 * 16;   // accumulators of phases 1..KP-1
     static constexpr int LDS = RING > RED ? RING : RED;
-    static_assert(kSC % KP == 0, "every phase takes the same number of chunks of a slot");
+    static_assert(SC % KP == 0, "every phase takes the same number of chunks of a slot");
     static_assert(NR >= 3, "ring too shallow");
     static_assert(LDS <= 160 * 1024, "LDS budget");
 };
@@ -219,12 +220,13 @@ void dq_gemm_kernel(const uint16_t *__restrict__ x, int M, int64_t K, int64_t N,
 
     // X blocks (16 rows x 64 B) of a slot are spread over the waves:
     // block b is loaded by wave b % kWaves.
-    constexpr int XBLK = MT * kSC;
+    constexpr int SC = C::SC;
+    constexpr int XBLK = MT * SC;
     constexpr int XT = (XBLK + kWaves - 1) / kWaves;
     const int nx = XBLK / kWaves + (wv < XBLK % kWaves ? 1 : 0);
-    // Canonical metadata of a slot (kSC chunks x 32 rows x CG groups x 4 B)
+    // Canonical metadata of a slot (SC chunks x 32 rows x CG groups x 4 B)
     // goes in 256-byte instructions, instruction e by wave e.
-    constexpr int NMETA = kSC * 32 * CG * 4 / 256;
+    constexpr int NMETA = SC * 32 * CG * 4 / 256;
     const int nm = CANON ? (wv < NMETA ? 1 : 0) : 1;
     const int cnt = nx + LC + nm;                // load instructions per slot for this wave
 
@@ -253,7 +255,7 @@ void dq_gemm_kernel(const uint16_t *__restrict__ x, int M, int64_t K, int64_t N,
         moff = (uint32_t)((row * ng + grp) * 4);
         mchunk = (wv * RPM) / 32;
     }
-    // Canonical codes: the workgroup's code rows of a slot (kSC chunks x 32
+    // Canonical codes: the workgroup's code rows of a slot (SC chunks x 32
     // rows x CG groups x 32 bytes) are loaded 1 KB per instruction, RPD rows
     // each, instruction d by wave d / LC.  Lane l takes 16-byte piece
     // (l % (2 CG)) ^ cswz(row) of row l / (2 CG), so the pieces land
@@ -287,7 +289,7 @@ void dq_gemm_kernel(const uint16_t *__restrict__ x, int M, int64_t K, int64_t N,
     }
     const int aoff = phase * C::XCHUNK + arow * 64 + ((akq ^ xswz(arow)) * 16);
 
-    // Issue this wave's direct-to-LDS loads for the slot of kSC chunks that
+    // Issue this wave's direct-to-LDS loads for the slot of SC chunks that
     // starts at chunk kc0: its share of the X blocks and the code words and
     // metadata of its own chunks kc0 + phase + lc*KP.  Chunks past c_end (the
     // tail of the ring) are clamped to the last chunk of the split; a chunk
@@ -425,7 +427,7 @@ void dq_gemm_kernel(const uint16_t *__restrict__ x, int M, int64_t K, int64_t N,
     };
 
     const int nmine = c_end - c_begin;           // chunks of this split
-    const int nslots = (nmine + kSC - 1) / kSC;
+    const int nslots = (nmine + SC - 1) / SC;
     // B fragments: bf[n % 2] feeds this wave's n-th chunk of a ring turn
     // while bf[(n+1) % 2] receives the next one's; with an even number of
     // chunks per ring turn the roles swap statically, with no register copy.
@@ -441,7 +443,7 @@ void dq_gemm_kernel(const uint16_t *__restrict__ x, int M, int64_t K, int64_t N,
     f16x8 ap[PD];                                // ap[d]: fragment d m-tiles ahead
     if (nmine > 0) {
 #pragma unroll
-        for (int r = 0; r < NR - 1; ++r) issue(c_begin + r * kSC, r);
+        for (int r = 0; r < NR - 1; ++r) issue(c_begin + r * SC, r);
         wait_slots<NR - 2>(cnt);                 // this wave's loads of the first slot
         lds_barrier();                           // ... and every wave's
         BRaw raw;
@@ -466,7 +468,7 @@ void dq_gemm_kernel(const uint16_t *__restrict__ x, int M, int64_t K, int64_t N,
                 // each half interleaved with the MFMAs so the VALU work runs
                 // in their shadow.  A wave only leaves this loop early in the
                 // last slot, which takes no barrier.
-                if (st * kSC + phase + lc * KP >= nmine) break;
+                if (st * SC + phase + lc * KP >= nmine) break;
                 // The next chunk's B words: in this slot, or (last chunk of
                 // the slot) this wave's own loads of the next slot (packed),
                 // for which its vmcnt is enough.  Slot st+1 is only certain
@@ -521,7 +523,7 @@ void dq_gemm_kernel(const uint16_t *__restrict__ x, int M, int64_t K, int64_t N,
                         acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
                             ap[0], __builtin_bit_cast(f16x8, bcur[j]), acc[i][j], 0, 0, 0);
                     if (lc == 0 && i == 0) {
-                        issue(c_begin + (st + NR - 1) * kSC, (r + NR - 1) % NR);
+                        issue(c_begin + (st + NR - 1) * SC, (r + NR - 1) % NR);
                         if (late) load_next_slot();
                     }
 #pragma unroll
@@ -570,10 +572,11 @@ void dq_gemm_kernel(const uint16_t *__restrict__ x, int M, int64_t K, int64_t N,
         }
     }
 
-    if (!gvalid || phase != 0) return;
+    // Phase 0 of each valid column group holds the workgroup's result.
+    const bool active = gvalid && phase == 0;
     if constexpr (!CANON) {
         // ---- undo the column group's exponent (a power of two: exact)
-        const float gscale = __builtin_amdgcn_ldexpf(1.0f, (int)wm[(int64_t)nchunks * ng * 32 + g]);
+        const float gscale = __builtin_amdgcn_ldexpf(1.0f, active ? (int)wm[(int64_t)nchunks * ng * 32 + g] : 0);
 #pragma unroll
         for (int i = 0; i < MT; ++i)
 #pragma unroll
@@ -584,37 +587,87 @@ void dq_gemm_kernel(const uint16_t *__restrict__ x, int M, int64_t K, int64_t N,
     // or 64g + 4(lane%16) + j (canonical: four consecutive channels)
     const int crow = (lane >> 4) * 4, ccol = lane & 15;
     const int64_t col0 = g * 64 + (CANON ? 4 * ccol : ccol);
-    auto store_row = [&](auto *dst, int i, int r) {
+    auto store_row = [&](auto *dst, const f32x4 *v) {
         using T = std::remove_pointer_t<decltype(dst)>;
         if constexpr (CANON) {
             if constexpr (std::is_same_v<T, float>) {
-                *reinterpret_cast<f32x4 *>(dst) = f32x4{acc[i][0][r], acc[i][1][r], acc[i][2][r], acc[i][3][r]};
+                *reinterpret_cast<f32x4 *>(dst) = f32x4{v[0][0], v[1][0], v[2][0], v[3][0]};
             } else {
                 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
-                *reinterpret_cast<f16x4 *>(dst) = f16x4{(_Float16)acc[i][0][r], (_Float16)acc[i][1][r],
-                                                         (_Float16)acc[i][2][r], (_Float16)acc[i][3][r]};
+                *reinterpret_cast<f16x4 *>(dst) =
+                    f16x4{(_Float16)v[0][0], (_Float16)v[1][0], (_Float16)v[2][0], (_Float16)v[3][0]};
             }
         } else {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) dst[j * 16] = (T)acc[i][j][r];
+            for (int j = 0; j < 4; ++j) dst[j * 16] = (T)v[j][0];
         }
     };
-    float *fbase = ksplit > 1 ? part + (int64_t)split * M * N : static_cast<float *>(y);
-    const bool f16out = ksplit == 1 && y_f16;
+    // value (i, j, r) of this lane as the first component of a vector, so
+    // that store_row takes one row's four values
+    auto row_vals = [&](int i, int r, f32x4 (&v)[4]) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) v[j] = f32x4{acc[i][j][r], 0.f, 0.f, 0.f};
+    };
+    auto store_final = [&]() {
+#pragma unroll
+        for (int i = 0; i < MT; ++i)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = m0 + i * 16 + crow + r;
+                if (row < M) {
+                    f32x4 v[4];
+                    row_vals(i, r, v);
+                    if (y_f16)
+                        store_row(static_cast<_Float16 *>(y) + (int64_t)row * N + col0, v);
+                    else
+                        store_row(static_cast<float *>(y) + (int64_t)row * N + col0, v);
+                }
+            }
+    };
+    if (ksplit == 1) {
+        if (active) store_final();
+        return;
+    }
+    // ---- split-K: this split's partial tile, summed in split order by a
+    // second kernel
+    if (!active) return;
+    float *pbase = part + (int64_t)split * M * N;
 #pragma unroll
     for (int i = 0; i < MT; ++i)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int row = m0 + i * 16 + crow + r;
             if (row < M) {
-                if (f16out)
-                    store_row(static_cast<_Float16 *>(y) + (int64_t)row * N + col0, i, r);
-                else
-                    store_row(fbase + (int64_t)row * N + col0, i, r);
+                f32x4 v[4];
+                row_vals(i, r, v);
+                store_row(pbase + (int64_t)row * N + col0, v);
             }
         }
 }
 
+struct LaunchArgs {
+    dim3 grid;
+    hipStream_t stream;
+    const uint16_t *x;
+    int M;
+    int64_t K, N;
+    const void *wc;
+    const uint32_t *wm;
+    int cps;
+    float *part;
+    void *y;
+    int f16, ksplit;
+};
+
+template <int MT, int KP, bool CANON>
+void launch_one(const LaunchArgs &a) {
+    dq_gemm_kernel<MT, KP, CANON><<<a.grid, dim3(kThreads), 0, a.stream>>>(
+        a.x, a.M, a.K, a.N, a.wc, a.wm, a.cps, a.part, a.y, a.f16, a.ksplit);
+}
+
+// k-phases per workgroup: 1 and 2 for every row count; 4 and 8 (one or two
+// column groups per workgroup, phases summed in LDS) for up to 64 rows with
+// the packed layout.
 // Y = sum over splits of the partial tiles, in split order.
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *__restrict__ part, int ksplit,
                                                             int64_t MN, void *__restrict__ y, int y_f16) {
@@ -634,27 +687,27 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *__restr
 }
 
 template <int MT, bool CANON>
-void launch_mt(int kp, dim3 grid, hipStream_t stream, const uint16_t *x, int M, int64_t K, int64_t N,
-               const void *wc, const uint32_t *wm, int cps, float *part, void *y, int f16, int ksplit) {
-    if (kp == 2)
-        dq_gemm_kernel<MT, 2, CANON><<<grid, dim3(kThreads), 0, stream>>>(x, M, K, N, wc, wm, cps, part, y, f16, ksplit);
-    else
-        dq_gemm_kernel<MT, 1, CANON><<<grid, dim3(kThreads), 0, stream>>>(x, M, K, N, wc, wm, cps, part, y, f16, ksplit);
+void launch_mt(int kp, const LaunchArgs &a) {
+    if constexpr (MT <= 4 && !CANON) {
+        if (kp == 8) return launch_one<MT, 8, CANON>(a);
+        if (kp == 4) return launch_one<MT, 4, CANON>(a);
+    }
+    if (kp == 2) return launch_one<MT, 2, CANON>(a);
+    launch_one<MT, 1, CANON>(a);
 }
 
 template <bool CANON>
-void launch_layout(int mt, int kp, dim3 grid, hipStream_t stream, const uint16_t *x, int M, int64_t K, int64_t N,
-                   const void *wc, const uint32_t *wm, int cps, float *part, void *y, int f16, int ksplit) {
+void launch_layout(int mt, int kp, const LaunchArgs &a) {
     switch (mt) {
-        case 1: launch_mt<1, CANON>(kp, grid, stream, x, M, K, N, wc, wm, cps, part, y, f16, ksplit); break;
-        case 2: launch_mt<2, CANON>(kp, grid, stream, x, M, K, N, wc, wm, cps, part, y, f16, ksplit); break;
-        case 3: launch_mt<3, CANON>(kp, grid, stream, x, M, K, N, wc, wm, cps, part, y, f16, ksplit); break;
-        case 4: launch_mt<4, CANON>(kp, grid, stream, x, M, K, N, wc, wm, cps, part, y, f16, ksplit); break;
-        case 5: launch_mt<5, CANON>(kp, grid, stream, x, M, K, N, wc, wm, cps, part, y, f16, ksplit); break;
-        case 6: launch_mt<6, CANON>(kp, grid, stream, x, M, K, N, wc, wm, cps, part, y, f16, ksplit); break;
-        case 7: launch_mt<7, CANON>(kp, grid, stream, x, M, K, N, wc, wm, cps, part, y, f16, ksplit); break;
-        case 8: launch_mt<8, CANON>(kp, grid, stream, x, M, K, N, wc, wm, cps, part, y, f16, ksplit); break;
-        default: launch_mt<9, CANON>(kp, grid, stream, x, M, K, N, wc, wm, cps, part, y, f16, ksplit); break;
+        case 1: launch_mt<1, CANON>(kp, a); break;
+        case 2: launch_mt<2, CANON>(kp, a); break;
+        case 3: launch_mt<3, CANON>(kp, a); break;
+        case 4: launch_mt<4, CANON>(kp, a); break;
+        case 5: launch_mt<5, CANON>(kp, a); break;
+        case 6: launch_mt<6, CANON>(kp, a); break;
+        case 7: launch_mt<7, CANON>(kp, a); break;
+        case 8: launch_mt<8, CANON>(kp, a); break;
+        default: launch_mt<9, CANON>(kp, a); break;
     }
 }
 
@@ -663,7 +716,7 @@ void launch_layout(int mt, int kp, dim3 grid, hipStream_t stream, const uint16_t
 struct GemmPlan {
     int mt;              // 16-row tiles per M block
     int mblocks;
-    int kp;              // k-phases inside a workgroup (1 or 2)
+    int kp;              // k-phases inside a workgroup (1, 2, 4 or 8)
     int64_t nblocks;     // workgroups along N (each 64 * 8 / kp channels)
     int ksplit;
     int chunks_per_split;
@@ -672,34 +725,37 @@ struct GemmPlan {
 // Work split.  One 8-wave workgroup per CU (the LDS ring takes most of the
 // CU's 160 KB).  K is shared out first between the kp phases of a workgroup
 // (summed in LDS), then between ksplit workgroups (fp32 partial tiles summed
-// by a second kernel).  The time of a plan is modelled as (workgroups per CU)
-// x (chunks per wave x time of one 32-k chunk, ~0.88 us at 144 rows, plus the
-// ring fill, the phase sum and the epilogue) plus writing and re-reading the
-// partial tiles and one extra launch; the constants are fitted to sweeps on
-// MI355X over the OPT-shaped weights.
-GemmPlan gemm_plan(int64_t M, int64_t K, int64_t N) {
+// by a second kernel).  The time of a plan is modelled as, per round of
+// workgroups on the 256 CUs, the chunks of one wave times the time of one
+// 32-k chunk (which grows with the rows), the ring fill and epilogue and the
+// phase sum, plus the partial tiles' traffic; the constants are a
+// least-squares fit to a sweep of forced plans (k-phases 1..8, 1..32 splits)
+// over the OPT-6.7B, OPT-30B and OPT-175B weight shapes at their block sizes
+// on MI355X (median error 7%).
+GemmPlan gemm_plan(int64_t M, int64_t K, int64_t N, bool canonical) {
     GemmPlan p{};
     const int64_t mt_needed = (M + 15) / 16;
     p.mt = (int)(mt_needed < 9 ? (mt_needed < 1 ? 1 : mt_needed) : 9);
     p.mblocks = (int)((M + 16 * p.mt - 1) / (16 * p.mt));
     const int64_t ng = N / 64;
     const int64_t nchunks = K / 32;
-    const double chunk_us = 0.1 + 0.78 * p.mt / 9.0;    // one 32-k chunk of one wave
-    const double ramp_us = 4.0;                          // ring fill and epilogue of a workgroup
-    const double phase_us = 1.5;                         // LDS sum of the phases
-    const double bytes_per_us = 3.0e6;                   // partial tile write + read, ~6 TB/s each
+    const double chunk_us = 0.095 + 0.074 * p.mt;       // one 32-k chunk of one wave
+    const double round_us = 1.87;                        // ring fill and epilogue of a round of workgroups
+    const double partial_us_per_mb = 0.364;              // partial tiles written, re-read and summed
     double best = 1e300;
     int best_ks = 1, best_kp = 1;
-    for (int kp = 1; kp <= 2; ++kp) {
+    const int kp_max = (!canonical && p.mt <= 4) ? 8 : 2;
+    for (int kp = 1; kp <= kp_max; kp *= 2) {
         const int64_t cols = kWaves / kp;
         const int64_t base = ((ng + cols - 1) / cols) * (p.mblocks > 0 ? p.mblocks : 1);
+        const double phase_us = 0.67 * (kp - 1) * p.mt / 4.0;   // LDS sum of the phases
         for (int ks = 1; ks <= 64; ++ks) {
             const int64_t cps = (nchunks + ks - 1) / ks;
             if (ks > 1 && (cps * (ks - 1) >= nchunks || cps < 8 * kp)) break;   // empty or too short splits
-            const double per_cu = std::ceil((double)base * ks / kNumCU);
+            const double rounds = std::ceil((double)base * ks / kNumCU);
             const double per_wave = std::ceil((double)cps / kp);
-            const double t = per_cu * (per_wave * chunk_us + ramp_us + (kp > 1 ? phase_us : 0.0)) +
-                             (ks > 1 ? (double)ks * (double)M * (double)N * 4.0 / bytes_per_us + 3.0 : 0.0);
+            const double t = rounds * (round_us + per_wave * chunk_us + phase_us) +
+                             (ks > 1 ? (double)ks * (double)M * (double)N * 4e-6 * partial_us_per_mb : 0.0);
             if (t < best) { best = t; best_ks = ks; best_kp = kp; }
         }
     }
@@ -712,10 +768,12 @@ GemmPlan gemm_plan(int64_t M, int64_t K, int64_t N) {
     return p;
 }
 
+// The workspace (split-K partial tiles) covers both layouts' plans.
 size_t gemm_ws_bytes(int64_t M, int64_t K, int64_t N) {
-    const GemmPlan p = gemm_plan(M, K, N);
-    if (p.ksplit <= 1) return 0;
-    return (size_t)p.ksplit * (size_t)M * (size_t)N * sizeof(float);
+    const GemmPlan a = gemm_plan(M, K, N, false), b = gemm_plan(M, K, N, true);
+    const int ks = a.ksplit > b.ksplit ? a.ksplit : b.ksplit;
+    if (ks <= 1) return 0;
+    return (size_t)ks * (size_t)M * (size_t)N * sizeof(float);
 }
 
 // canonical: wc = uint8 codes [K][N/2], wm = uint32 meta [K][N/64];
@@ -723,23 +781,32 @@ size_t gemm_ws_bytes(int64_t M, int64_t K, int64_t N) {
 fgq_status launch_dequant_gemm(const void *x, int64_t M, int64_t K, int64_t N, const void *wc, const uint32_t *wm,
                                bool canonical, void *y, int32_t y_dtype, void *ws, hipStream_t stream) {
     if (M == 0 || N == 0) return FGQ_OK;
-    const GemmPlan p = gemm_plan(M, K, N);
+    const GemmPlan p = gemm_plan(M, K, N, canonical);
     if (p.mblocks > 65535 || (double)p.nblocks * p.ksplit * p.mblocks >= 2147483648.0)
         return fail(FGQ_ERR_SHAPE, "dequant GEMM grid too large (M=%lld N=%lld)", (long long)M, (long long)N);
-    const int f16 = y_dtype == FGQ_DTYPE_F16;
-    const dim3 grid((unsigned)p.nblocks, (unsigned)p.ksplit, (unsigned)p.mblocks);
-    const uint16_t *xh = static_cast<const uint16_t *>(x);
-    float *part = static_cast<float *>(ws);
+    LaunchArgs a{};
+    a.grid = dim3((unsigned)p.nblocks, (unsigned)p.ksplit, (unsigned)p.mblocks);
+    a.stream = stream;
+    a.x = static_cast<const uint16_t *>(x);
+    a.M = (int)M;
+    a.K = K;
+    a.N = N;
+    a.wc = wc;
+    a.wm = wm;
+    a.cps = p.chunks_per_split;
+    a.part = static_cast<float *>(ws);
+    a.y = y;
+    a.f16 = y_dtype == FGQ_DTYPE_F16;
+    a.ksplit = p.ksplit;
     if (canonical)
-        launch_layout<true>(p.mt, p.kp, grid, stream, xh, (int)M, K, N, wc, wm, p.chunks_per_split, part, y, f16,
-                            p.ksplit);
+        launch_layout<true>(p.mt, p.kp, a);
     else
-        launch_layout<false>(p.mt, p.kp, grid, stream, xh, (int)M, K, N, wc, wm, p.chunks_per_split, part, y, f16,
-                             p.ksplit);
+        launch_layout<false>(p.mt, p.kp, a);
     fgq_status s = check_launch("dq_gemm_kernel");
     if (s != FGQ_OK || p.ksplit == 1) return s;
     const int64_t MN = M * N;   // N % 64 == 0, so MN % 4 == 0
-    splitk_reduce_kernel<<<dim3((unsigned)((MN / 4 + 255) / 256)), dim3(256), 0, stream>>>(part, p.ksplit, MN, y, f16);
+    splitk_reduce_kernel<<<dim3((unsigned)((MN / 4 + 255) / 256)), dim3(256), 0, stream>>>(
+        a.part, p.ksplit, MN, y, a.f16);
     return check_launch("splitk_reduce_kernel");
 }
 
