@@ -18,12 +18,13 @@
 //    n-tiles) and every row of its M block (up to 9 m-tiles = 144 rows), so
 //    one dequantised B fragment feeds up to 9 MFMAs;
 //  * a workgroup is 8 waves (two per SIMD): 8/KP column groups times KP
-//    k-phases (KP = 1 or 2); the phases multiply alternate chunks of K and
-//    are summed through LDS at the end, and all waves share the X rows of
-//    each K chunk through LDS;
+//    k-phases (KP = 1 or 2; also 4 or 8 with the packed layout for blocks of
+//    at most 4 m-tiles); the phases multiply interleaved chunks of K and are
+//    summed through LDS at the end, and all waves share the X rows of each
+//    K chunk through LDS;
 //  * every operand reaches LDS through gfx950's direct global->LDS loads
 //    (global_load_lds_dword[x4], scalar base + loop-invariant lane offset,
-//    so no vector ALU work) into a ring of two-chunk slots (the X rows, the
+//    so no vector ALU work) into a ring of max(2, KP)-chunk slots (the X rows, the
 //    code words and the group metadata) as deep as the LDS allows, all but
 //    one slot in flight, one barrier per slot;
 //  * packed layout: the 8 k-values of one output channel sit in one 32-bit
