@@ -44,6 +44,8 @@
  *    error nothing is enqueued and outputs are untouched.  A failed launch
  *    returns FGQ_ERR_DEVICE.  fgq_last_error() gives a text for the calling
  *    thread's last failure.
+ *  - Size queries (the *_ws_bytes and *_words functions) return 0 for
+ *    arguments the matching call rejects.
  *  - Inputs must be finite (precondition; the result is undefined otherwise).
  *  - Calls are reentrant; the library holds no mutable global state besides
  *    the per-thread error text and, for fgq_decode_attn_q4kv_noalloc only,
@@ -88,7 +90,8 @@ const char *fgq_last_error(void);
  * For a weight W [K = in][N = out] pass rows=K, cols=N: each group is 64
  * consecutive output channels at one input index.  For KV rows pass
  * [tokens][hidden]: each group is 64 consecutive hidden elements.
- * Requires cols % 64 == 0 and ld_x % 8 == 0, ld_x >= cols.  rows == 0 is a no-op.
+ * Requires cols % 64 == 0 and ld_x % 8 == 0, ld_x >= cols, rows * ld_x <= 2^48
+ * (FGQ_ERR_SHAPE otherwise).  rows == 0 is a no-op.
  * Codes and meta equal, bit for bit, the encoding defined above.
  */
 fgq_status fgq_quantize_g64(const void *x_f16, int64_t rows, int64_t cols, int64_t ld_x,
@@ -101,6 +104,8 @@ fgq_status fgq_quantize_g64(const void *x_f16, int64_t rows, int64_t cols, int64
  * Groups run along the hidden dimension of one token's K (or V) row; with
  * head_dim a multiple of 64 a group never straddles two heads.  The caller
  * allocates the arrays; the library reads and writes them only in calls.
+ * Every call that takes a cache requires capacity <= 2^30 and
+ * batch * heads * capacity * head_dim <= 2^48 (FGQ_ERR_SHAPE otherwise).
  */
 typedef struct fgq_kv_cache {
     uint8_t *k_codes;
@@ -121,7 +126,8 @@ typedef struct fgq_kv_cache {
  * jaehun.me, "Is 4-bit compression ...": KV grouped along hidden).
  *   k_new, v_new  fp16 [batch][n_new][heads*head_dim], token-major.
  * Bit-exact with fgq_quantize_g64 on the same rows.  n_new == 0 or batch == 0
- * is a no-op.  pos + n_new > capacity -> FGQ_ERR_CAPACITY.
+ * is a no-op.  pos + n_new > capacity -> FGQ_ERR_CAPACITY; k_new/v_new of
+ * more than 2^48 elements (batch * n_new * row stride) -> FGQ_ERR_SHAPE.
  */
 fgq_status fgq_kv_append(const fgq_kv_cache *kv, const void *k_new_f16, const void *v_new_f16,
                          int32_t pos, int32_t n_new, void *stream);
@@ -309,7 +315,8 @@ fgq_status fgq_dequant_gemm(const void *x_f16, int32_t g, int32_t m, int64_t K, 
  *     column group g: the smallest e >= 0 with max_k step[k][g] * 2^(24-e)
  *     <= 65504.  (The GEMM multiplies codes placed as q * 2^-24 or q * 2^-20
  *     by these steps, and its result by 2^e_g.)
- * Requires K % 32 == 0, N % 64 == 0.
+ * Requires K % 32 == 0, N % 64 == 0, K <= 2^23 and N <= 2^28 (FGQ_ERR_SHAPE
+ * otherwise; the word count query returns 0 for such sizes).
  */
 size_t fgq_pack_weight_meta_words(int64_t K, int64_t N);
 fgq_status fgq_pack_weight_g64(const uint8_t *codes, const uint32_t *meta, int64_t K, int64_t N,

@@ -35,6 +35,17 @@ fgq_status launch_dequant_gemm(const void *x, int64_t M, int64_t K, int64_t N, c
 
 static thread_local char g_err[512];
 
+// Size limits that keep every host and device offset computation inside
+// 64-bit (host) and the kernels' index types: at most 2^48 elements in any
+// one array, 2^30 cache positions per sequence.
+constexpr double kMaxElems = 281474976710656.0;   // 2^48
+constexpr int32_t kMaxCapacity = 1 << 30;
+// GEMM limits: rows of the block, K, N (packed layout; the canonical layout
+// takes half that N).
+constexpr int64_t kMaxM = (int64_t)1 << 30;
+constexpr int64_t kMaxK = (int64_t)1 << 23;
+constexpr int64_t kMaxNPacked = (int64_t)1 << 28;
+
 fgq_status fail(fgq_status s, const char *fmt, ...) {
     va_list ap;
     va_start(ap, fmt);
@@ -57,6 +68,11 @@ static fgq_status check_kv(const fgq_kv_cache *kv) {
         if (kv->head_dim % 64 != 0) return fail(FGQ_ERR_SHAPE, "head_dim %d is not a multiple of 64", kv->head_dim);
         return fail(FGQ_ERR_UNSUPPORTED, "head_dim %d (64 or 128 supported)", kv->head_dim);
     }
+    if (kv->capacity > kMaxCapacity)
+        return fail(FGQ_ERR_SHAPE, "capacity %d above 2^30 positions", kv->capacity);
+    if ((double)kv->batch * kv->heads * kv->capacity * kv->head_dim > kMaxElems)
+        return fail(FGQ_ERR_SHAPE, "cache of batch %d x heads %d x capacity %d x head_dim %d above 2^48 elements",
+                    kv->batch, kv->heads, kv->capacity, kv->head_dim);
     if (!kv->k_codes || !kv->v_codes || !kv->k_meta || !kv->v_meta)
         return fail(FGQ_ERR_INVALID_ARG, "kv array is NULL");
     if (!aligned16(kv->k_codes) || !aligned16(kv->v_codes) || !aligned16(kv->k_meta) || !aligned16(kv->v_meta))
@@ -95,6 +111,8 @@ fgq_status fgq_quantize_g64(const void *x_f16, int64_t rows, int64_t cols, int64
     if (rows < 0 || cols < 0) return fail(FGQ_ERR_INVALID_ARG, "negative size");
     if (cols % 64 != 0) return fail(FGQ_ERR_SHAPE, "cols %lld is not a multiple of 64", (long long)cols);
     if (ld_x < cols) return fail(FGQ_ERR_SHAPE, "ld_x %lld < cols %lld", (long long)ld_x, (long long)cols);
+    if ((double)rows * ld_x > kMaxElems || cols / 64 > INT32_MAX)
+        return fail(FGQ_ERR_SHAPE, "x of %lld rows x ld %lld above 2^48 elements", (long long)rows, (long long)ld_x);
     if (rows == 0 || cols == 0) return FGQ_OK;
     if (!x_f16 || !codes || !meta) return fail(FGQ_ERR_INVALID_ARG, "NULL array");
     if (ld_x % 8 != 0 || !aligned16(x_f16) || !aligned16(codes) || !aligned16(meta))
@@ -113,6 +131,9 @@ fgq_status fgq_kv_append_ld(const fgq_kv_cache *kv, const void *k_new_f16, const
     const int64_t hidden = (int64_t)kv->heads * kv->head_dim;
     if (ld_new < hidden) return fail(FGQ_ERR_SHAPE, "ld_new %lld < heads * head_dim %lld", (long long)ld_new,
                                      (long long)hidden);
+    if ((double)kv->batch * n_new * ld_new > kMaxElems)
+        return fail(FGQ_ERR_SHAPE, "k_new/v_new of batch %d x n_new %d x ld %lld above 2^48 elements", kv->batch,
+                    n_new, (long long)ld_new);
     if (n_new == 0 || kv->batch == 0 || kv->heads == 0) return FGQ_OK;
     if (!k_new_f16 || !v_new_f16) return fail(FGQ_ERR_INVALID_ARG, "NULL k_new or v_new");
     if (!aligned16(k_new_f16) || !aligned16(v_new_f16) || ld_new % 8 != 0)
@@ -127,7 +148,8 @@ fgq_status fgq_kv_append(const fgq_kv_cache *kv, const void *k_new_f16, const vo
 }
 
 size_t fgq_decode_attn_ws_bytes(int32_t batch, int32_t heads, int32_t head_dim, int32_t kv_len) {
-    if (batch <= 0 || heads <= 0 || (head_dim != 64 && head_dim != 128) || kv_len <= 0) return 0;
+    if (batch <= 0 || heads <= 0 || (head_dim != 64 && head_dim != 128) || kv_len <= 0 || kv_len > kMaxCapacity)
+        return 0;
     return attn_ws_bytes(batch, heads, head_dim, kv_len);
 }
 
@@ -147,6 +169,8 @@ static fgq_status check_attn(const fgq_kv_cache *kv, const void *q_f16, int64_t 
     if (ld_q < hidden) return fail(FGQ_ERR_SHAPE, "ld_q %lld < heads * head_dim %lld", (long long)ld_q,
                                    (long long)hidden);
     if ((int64_t)kv->batch * kv->heads > INT32_MAX) return fail(FGQ_ERR_SHAPE, "batch * heads > 2^31 - 1");
+    if ((double)kv->batch * ld_q > kMaxElems)
+        return fail(FGQ_ERR_SHAPE, "q of batch %d x ld %lld above 2^48 elements", kv->batch, (long long)ld_q);
     if (kv->batch == 0 || kv->heads == 0) {
         *noop = true;
         return FGQ_OK;
@@ -203,7 +227,8 @@ fgq_status fgq_decode_attn_q4kv(const fgq_kv_cache *kv, const void *q_f16, int32
 size_t fgq_decode_attn_gqa_ws_bytes(int32_t batch, int32_t q_heads, int32_t kv_heads, int32_t head_dim,
                                     int32_t kv_len) {
     if (batch <= 0 || kv_heads <= 0 || q_heads < kv_heads || q_heads % kv_heads != 0 ||
-        q_heads / kv_heads > FGQ_GQA_MAX_GROUP || (head_dim != 64 && head_dim != 128) || kv_len <= 0)
+        q_heads / kv_heads > FGQ_GQA_MAX_GROUP || (head_dim != 64 && head_dim != 128) || kv_len <= 0 ||
+        kv_len > kMaxCapacity)
         return 0;
     if (q_heads == kv_heads) return attn_ws_bytes(batch, q_heads, head_dim, kv_len);
     return gqa_ws_bytes(batch, q_heads, kv_heads, head_dim, kv_len);
@@ -261,7 +286,7 @@ fgq_status fgq_decode_attn_topk_q4kv(const fgq_kv_cache *kv, const void *q_f16, 
     if (!std::isfinite(softmax_scale)) return fail(FGQ_ERR_INVALID_ARG, "softmax_scale is not finite");
     const int32_t kept = top_k < kv_len ? top_k : kv_len;
     if (attn_topk_lds_bytes(kv_len, kept) > FGQ_TOPK_MAX_POSITIONS * sizeof(float))
-        return fail(FGQ_ERR_UNSUPPORTED, "kv_len + min(top_k, kv_len) = %d > %d", kv_len + kept,
+        return fail(FGQ_ERR_UNSUPPORTED, "kv_len + min(top_k, kv_len) = %lld > %d", (long long)kv_len + kept,
                     FGQ_TOPK_MAX_POSITIONS);
     if ((int64_t)kv->batch * kv->heads > INT32_MAX) return fail(FGQ_ERR_SHAPE, "batch * heads > 2^31 - 1");
     if (kv->batch == 0 || kv->heads == 0) return FGQ_OK;
@@ -286,7 +311,7 @@ fgq_status fgq_prefill_attn_f16(const void *q_f16, const void *k_f16, const void
         return fail(FGQ_ERR_DTYPE, "out_dtype %d", out_dtype);
     if (!std::isfinite(softmax_scale)) return fail(FGQ_ERR_INVALID_ARG, "softmax_scale is not finite");
     if (batch > 65535 || heads > 65535) return fail(FGQ_ERR_SHAPE, "batch and heads must be <= 65535");
-    if ((int64_t)batch * seq * heads * head_dim > ((int64_t)1 << 40))
+    if ((double)batch * seq * heads * head_dim > (double)((int64_t)1 << 40))
         return fail(FGQ_ERR_SHAPE, "q/k/v larger than 2^40 elements");
     if (batch == 0 || seq == 0 || heads == 0) return FGQ_OK;
     if (!q_f16 || !k_f16 || !v_f16 || !out) return fail(FGQ_ERR_INVALID_ARG, "NULL array");
@@ -298,7 +323,7 @@ fgq_status fgq_prefill_attn_f16(const void *q_f16, const void *k_f16, const void
 }
 
 size_t fgq_pack_weight_meta_words(int64_t K, int64_t N) {
-    if (K <= 0 || N <= 0 || K % 32 != 0 || N % 64 != 0) return 0;
+    if (K <= 0 || N <= 0 || K % 32 != 0 || N % 64 != 0 || K > kMaxK || N > kMaxNPacked) return 0;
     return (size_t)(K * (N / 64) + N / 64);
 }
 
@@ -307,6 +332,7 @@ fgq_status fgq_pack_weight_g64(const uint8_t *codes, const uint32_t *meta, int64
     g_err[0] = 0;
     if (K < 0 || N < 0) return fail(FGQ_ERR_INVALID_ARG, "negative size");
     if (K % 32 != 0 || N % 64 != 0) return fail(FGQ_ERR_SHAPE, "K %% 32 and N %% 64 must be 0");
+    if (K > kMaxK || N > kMaxNPacked) return fail(FGQ_ERR_SHAPE, "K > 2^23 or N > 2^28");
     if (K == 0 || N == 0) return FGQ_OK;
     if (!codes || !meta || !packed_codes || !packed_meta) return fail(FGQ_ERR_INVALID_ARG, "NULL array");
     if (!aligned16(codes) || !aligned16(meta) || !aligned16(packed_codes) || !aligned16(packed_meta))
@@ -315,7 +341,8 @@ fgq_status fgq_pack_weight_g64(const uint8_t *codes, const uint32_t *meta, int64
 }
 
 size_t fgq_dequant_gemm_ws_bytes(int64_t M, int64_t K, int64_t N) {
-    if (M <= 0 || K < 0 || N <= 0 || K % 32 != 0 || N % 64 != 0) return 0;
+    if (M <= 0 || K < 0 || N <= 0 || K % 32 != 0 || N % 64 != 0 || M > kMaxM || K > kMaxK || N > kMaxNPacked)
+        return 0;
     return gemm_ws_bytes(M, K, N);
 }
 
@@ -331,8 +358,8 @@ static fgq_status check_gemm(const void *x_f16, int32_t g, int32_t m, int64_t K,
                     (long long)N);
     if (y_dtype != FGQ_DTYPE_F32 && y_dtype != FGQ_DTYPE_F16) return fail(FGQ_ERR_DTYPE, "y_dtype %d", y_dtype);
     const int64_t M = (int64_t)g * m;
-    if (M > (int64_t)1 << 30) return fail(FGQ_ERR_SHAPE, "g*m too large");
-    if (K > (int64_t)1 << 23 || N > nmax)
+    if (M > kMaxM) return fail(FGQ_ERR_SHAPE, "g*m too large");
+    if (K > kMaxK || N > nmax)
         return fail(FGQ_ERR_SHAPE, "K > 2^23 or N > %lld", (long long)nmax);
     if (M == 0 || N == 0) {
         *noop = true;
@@ -355,7 +382,7 @@ fgq_status fgq_dequant_gemm(const void *x_f16, int32_t g, int32_t m, int64_t K, 
     g_err[0] = 0;
     bool noop = false;
     const fgq_status s = check_gemm(x_f16, g, m, K, N, w_codes, w_meta, y, y_dtype, ws, ws_bytes, 64,
-                                    (int64_t)1 << 27, &noop);
+                                    kMaxNPacked / 2, &noop);
     if (s != FGQ_OK || noop) return s;
     return launch_dequant_gemm(x_f16, (int64_t)g * m, K, N, w_codes, static_cast<const uint32_t *>(w_meta), true, y,
                                y_dtype, ws, static_cast<hipStream_t>(stream));
@@ -367,7 +394,7 @@ fgq_status fgq_dequant_gemm_packed(const void *x_f16, int32_t g, int32_t m, int6
     g_err[0] = 0;
     bool noop = false;
     const fgq_status s = check_gemm(x_f16, g, m, K, N, packed_codes, packed_meta, y, y_dtype, ws, ws_bytes, 32,
-                                    (int64_t)1 << 28, &noop);
+                                    kMaxNPacked, &noop);
     if (s != FGQ_OK || noop) return s;
     return launch_dequant_gemm(x_f16, (int64_t)g * m, K, N, packed_codes, packed_meta, false, y, y_dtype, ws,
                                static_cast<hipStream_t>(stream));

@@ -753,6 +753,7 @@ GemmPlan gemm_plan(int64_t M, int64_t K, int64_t N, bool canonical) {
         for (int ks = 1; ks <= 64; ++ks) {
             const int64_t cps = (nchunks + ks - 1) / ks;
             if (ks > 1 && (cps * (ks - 1) >= nchunks || cps < 8 * kp)) break;   // empty or too short splits
+            if (ks > 1 && (double)ks * (double)M * (double)N * 4.0 > 1099511627776.0) break;   // partials > 1 TiB
             const double rounds = std::ceil((double)base * ks / kNumCU);
             const double per_wave = std::ceil((double)cps / kp);
             const double t = rounds * (round_us + per_wave * chunk_us + phase_us) +

@@ -183,7 +183,7 @@ int oracle_kv_append(const uint16_t *k_new, const uint16_t *v_new,
                      int32_t batch, int32_t heads, int32_t head_dim, int32_t cap,
                      int32_t pos, int32_t n_new,
                      uint8_t *k_codes, uint32_t *k_meta, uint8_t *v_codes, uint32_t *v_meta) {
-    if (head_dim % 64 != 0 || pos < 0 || n_new < 0 || pos + n_new > cap) return ORACLE_ERR_SHAPE;
+    if (head_dim % 64 != 0 || pos < 0 || n_new < 0 || (int64_t)pos + n_new > cap) return ORACLE_ERR_SHAPE;
     int64_t h = (int64_t)heads * head_dim;
     int64_t gph = head_dim / 64;
     for (int64_t i = 0; i < (int64_t)batch * n_new * h; ++i)
