@@ -1105,6 +1105,24 @@ def gqa_attention_line(torch, fgq, stream, steps: int, warmup: int, sweep_heads=
         sweep["kv_heads_%d" % hk] = {"group": Hq // hk, "us_per_launch": us, "GB_per_s": b / us / 1e3,
                                      "frac_hbm_peak": b / us / 1e3 / HBM_PEAK_GBS,
                                      "TFLOP_per_s": acc.gqa_attention_flops(B, Hq, D, cap) / us / 1e6}
+        if hk == Hq:
+            # top-K (a tenth of the positions kept) over the same multi-head cache: the long-context kernel
+            kk = -(-cap // 10)
+            tk_out = torch.empty_like(out)
+            for _ in range(3):
+                fgq.fgq_decode_attn_topk_q4kv(kvs, q, cap, kk, 0.0, tk_out, fgq.FGQ_DTYPE_F32, None, sh)
+            torch.cuda.synchronize()
+            e0.record(stream)
+            for _ in range(reps):
+                fgq.fgq_decode_attn_topk_q4kv(kvs, q, cap, kk, 0.0, tk_out, fgq.FGQ_DTYPE_F32, None, sh)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            tus = 1e3 * e0.elapsed_time(e1) / reps
+            tb = acc.topk_attention_bytes(B, Hq * D, cap, kk)
+            line["topk_attention_at_kv_len_%d" % cap] = {
+                "heads": Hq, "kept": kk, "us_per_launch": tus, "GB_per_s": tb / tus / 1e3,
+                "frac_hbm_peak": tb / tus / 1e3 / HBM_PEAK_GBS, "time_vs_dense_attention": tus / us}
+            del tk_out
         del arrs, kvs
     tr = committed_traffic("attn_gqa_kernel", "gqa")
     if tr is not None:

@@ -245,11 +245,11 @@ fgq_status fgq_decode_attn_gqa_q4kv(const fgq_kv_cache *kv, const void *q_f16, i
  *   every (sequence, head) in ascending order.
  *   softmax_scale <= 0 selects 1/sqrt(head_dim).  Requires top_k >= 1
  *   (FGQ_ERR_INVALID_ARG), 1 <= kv_len <= capacity, and
- *   kv_len + kk <= FGQ_TOPK_MAX_POSITIONS (FGQ_ERR_UNSUPPORTED: the scores
- *   and the kept list of one (sequence, head) live in on-chip memory).
- *   No workspace.
+ *   kv_len <= FGQ_TOPK_MAX_POSITIONS (FGQ_ERR_UNSUPPORTED: the selection
+ *   state of one (sequence, head) lives in on-chip memory, 4 bytes per
+ *   position while kv_len + kk <= 15360, 2.125 bytes beyond).  No workspace.
  */
-#define FGQ_TOPK_MAX_POSITIONS 15360
+#define FGQ_TOPK_MAX_POSITIONS 65536
 fgq_status fgq_decode_attn_topk_q4kv(const fgq_kv_cache *kv, const void *q_f16, int32_t kv_len,
                                      int32_t top_k, float softmax_scale, void *out, int32_t out_dtype,
                                      int32_t *sel, void *stream);

@@ -29,6 +29,8 @@ FGQ_ERR_UNSUPPORTED = -8
 FGQ_DTYPE_F32 = 0
 FGQ_DTYPE_F16 = 1
 FGQ_NOALLOC_SCRATCH_BYTES = 9 << 20
+FGQ_GQA_MAX_GROUP = 32
+FGQ_TOPK_MAX_POSITIONS = 65536
 
 _lib = None
 

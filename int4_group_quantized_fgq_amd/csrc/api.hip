@@ -23,7 +23,6 @@ fgq_status launch_decode_attn(const fgq_kv_cache *kv, const void *q, int64_t ld_
 size_t gqa_ws_bytes(int32_t batch, int32_t q_heads, int32_t kv_heads, int32_t head_dim, int32_t kv_len);
 fgq_status launch_decode_attn_gqa(const fgq_kv_cache *kv, const void *q, int32_t q_heads, int32_t kv_len,
                                   float scale, void *out, int32_t out_dtype, void *ws, hipStream_t stream);
-size_t attn_topk_lds_bytes(int32_t kv_len, int32_t kept);
 fgq_status launch_decode_attn_topk(const fgq_kv_cache *kv, const void *q, int32_t kv_len, int32_t kept,
                                    float scale, void *out, int32_t out_dtype, int32_t *sel, hipStream_t stream);
 fgq_status launch_prefill_attn(const void *q, const void *k, const void *v, int32_t batch, int32_t seq,
@@ -285,9 +284,8 @@ fgq_status fgq_decode_attn_topk_q4kv(const fgq_kv_cache *kv, const void *q_f16, 
     if (top_k < 1) return fail(FGQ_ERR_INVALID_ARG, "top_k %d < 1", top_k);
     if (!std::isfinite(softmax_scale)) return fail(FGQ_ERR_INVALID_ARG, "softmax_scale is not finite");
     const int32_t kept = top_k < kv_len ? top_k : kv_len;
-    if (attn_topk_lds_bytes(kv_len, kept) > FGQ_TOPK_MAX_POSITIONS * sizeof(float))
-        return fail(FGQ_ERR_UNSUPPORTED, "kv_len + min(top_k, kv_len) = %lld > %d", (long long)kv_len + kept,
-                    FGQ_TOPK_MAX_POSITIONS);
+    if (kv_len > FGQ_TOPK_MAX_POSITIONS)
+        return fail(FGQ_ERR_UNSUPPORTED, "kv_len %d > %d", kv_len, FGQ_TOPK_MAX_POSITIONS);
     if ((int64_t)kv->batch * kv->heads > INT32_MAX) return fail(FGQ_ERR_SHAPE, "batch * heads > 2^31 - 1");
     if (kv->batch == 0 || kv->heads == 0) return FGQ_OK;
     if (!q_f16 || !out) return fail(FGQ_ERR_INVALID_ARG, "NULL q or out");

@@ -559,11 +559,415 @@ __global__ __launch_bounds__(256) void attn_topk_wave_kernel(
     }
 }
 
+
+// Long contexts, where the fp32 scores of one (b, h) no longer fit in LDS.
+// The same selection and output, with a 16-bit key per position in LDS:
+//  * the K stream stores the upper 16 bits of each position's order key
+//    and keeps the exact fp32 maximum;
+//  * a radix select over those 16 bits finds the bucket holding the
+//    kk-th largest key; when every candidate left in it is kept, the cut is
+//    found;
+//  * otherwise the candidates (the positions of that one bucket, usually a
+//    few hundred) get their scores recomputed from their K rows, their low
+//    16 key bits replace the stored ones (a bitmap marks them), and two more
+//    radix passes over those bits find the exact cut;
+//  * the ordered compaction (four tiles of positions per barrier round) fills
+//    an LDS buffer of kept positions, and each time it is half full the P.V
+//    pass runs over it, recomputing each kept position's score from its K row
+//    (the same operations as the stream, so the same fp32 value) and reading
+//    its V row.
+// Bytes: every K row once, the kept K and V rows once more (plus the
+// candidates' K rows when the bucket does not settle the cut).
+constexpr int kTkLongThreads = 512;  // 8 waves per (b, h): more K rows in flight
+constexpr int kTkLongUnroll = 8;     // token groups of K loads in flight per wave
+constexpr int kTkLongSub = 4;        // tiles of kTkLongThreads positions per compaction round
+constexpr int kTkLongRound = kTkLongSub * kTkLongThreads;
+constexpr int kTkLongKept = 2 * kTkLongRound;   // kept positions buffered between P.V passes
+
+// Histograms of the long kernel: four copies (lane % 4 picks one) at a
+// stride of 257 words, so the lanes of a wave that share a digit (the first
+// digit of nearby scores is often the same) spread over four addresses in
+// four banks.
+constexpr int kTkHistCopies = 4;
+constexpr int kTkHistStride = 257;
+constexpr int kTkHistWords = kTkHistCopies * kTkHistStride;
+
+__device__ __forceinline__ void tk_hist_clear(uint32_t *hist) {
+    for (int i = threadIdx.x; i < kTkHistWords; i += blockDim.x) hist[i] = 0u;
+}
+
+__device__ __forceinline__ void tk_hist_add(uint32_t *hist, uint32_t bin) {
+    atomicAdd(&hist[(threadIdx.x & (kTkHistCopies - 1)) * kTkHistStride + bin], 1u);
+}
+
+// The bin of the rem-th largest candidate once the histogram is complete:
+// S(t) = candidates with digit >= t; the bin t with S(t) >= rem and
+// S(t + 1) < rem.  Leaves the digit, the rank inside the bin and the bin's
+// count in sh[0..2]; every thread reads them after the barrier at the end.
+template <int NW>
+__device__ __forceinline__ void tk_pick_bin(const uint32_t *hist, uint32_t *wsum, uint32_t *sh, uint32_t rem) {
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    uint32_t hv = 0;
+    if (tid < 256) {
+#pragma unroll
+        for (int c = 0; c < kTkHistCopies; ++c) hv += hist[c * kTkHistStride + tid];
+    }
+    uint32_t x = hv;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t y = __shfl_down(x, off, 64);
+        if (lane + off < 64) x += y;
+    }
+    if (lane == 0) wsum[wv] = x;
+    __syncthreads();
+    uint32_t S = x;
+    for (int w = wv + 1; w < NW; ++w) S += wsum[w];
+    const uint32_t S_above = S - hv;
+    if (S >= rem && S_above < rem) {   // exactly one bin satisfies this
+        sh[0] = (uint32_t)tid;
+        sh[1] = rem - S_above;
+        sh[2] = hv;
+    }
+    __syncthreads();
+}
+
+// The eight waves' counts of one tile (16-byte aligned): the sum over the
+// waves before this one, and the total.
+__device__ __forceinline__ void tk_wave_counts(const uint32_t *c8, uint32_t &before, uint32_t &total) {
+    const int wv = threadIdx.x >> 6;
+    const uint4 a = *reinterpret_cast<const uint4 *>(c8);
+    const uint4 b = *reinterpret_cast<const uint4 *>(c8 + 4);
+    const uint32_t v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+    before = 0;
+    total = 0;
+#pragma unroll
+    for (int w = 0; w < 8; ++w) {
+        before += w < wv ? v[w] : 0u;
+        total += v[w];
+    }
+}
+
+template <int D>
+__global__ __launch_bounds__(kTkLongThreads) void attn_topk_long_kernel(
+    const uint8_t *__restrict__ kc, const uint32_t *__restrict__ km, const uint8_t *__restrict__ vc,
+    const uint32_t *__restrict__ vm, const uint16_t *__restrict__ q, int H, int cap, int L, int kk, float scale,
+    void *__restrict__ out, int out_f16, int32_t *__restrict__ sel) {
+    constexpr int PARTS = D / 32;    // lanes per token row
+    constexpr int TPI = 64 / PARTS;  // tokens per wave per load
+    constexpr int G = D / 64;        // groups per token row
+    constexpr int NW = kTkLongThreads / 64;
+    constexpr int TH = kTkLongThreads;
+    constexpr int SUB = kTkLongSub;
+    static_assert(NW == 8, "tk_wave_counts reads eight wave counts");
+    extern __shared__ uint32_t tk_long_smem[];   // key16 [L] as (L+1)/2 words, then the candidate bitmap
+    __shared__ __align__(16) int32_t kept[kTkLongKept];
+    __shared__ uint32_t hist[kTkHistWords];
+    __shared__ __align__(16) uint32_t cnt[2][SUB][NW];
+    __shared__ float wmax[NW];
+    __shared__ uint32_t sh[3];
+    // the final reduction reuses the kept buffer (no P.V pass reads it then)
+    static_assert((NW * D + NW * PARTS + NW) * 4 <= kTkLongKept * 4, "reduction fits the kept buffer");
+    float(*red_o)[D] = reinterpret_cast<float(*)[D]>(kept);
+    float(*red_m)[PARTS] = reinterpret_cast<float(*)[PARTS]>(reinterpret_cast<float *>(kept) + NW * D);
+    float *red_l = reinterpret_cast<float *>(kept) + NW * D + NW * PARTS;
+
+    uint16_t *key16 = reinterpret_cast<uint16_t *>(tk_long_smem);
+    uint32_t *cbits = tk_long_smem + (L + 1) / 2;
+    const int nwords = (L + 31) / 32;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wv = tid >> 6;
+    const int bh = blockIdx.x;
+    const int slot = lane / PARTS, part = lane % PARTS, grp = part >> 1;
+    const uint64_t lt_mask = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+
+    uint32_t QP[4][4];
+    float qsum;
+    tk_query<D>(q, bh, part, QP, qsum);
+
+    const size_t rowbase = (size_t)bh * cap;
+    const uint8_t *kbase = kc + rowbase * (D / 2) + part * 16;
+    const uint32_t *kmb = km + rowbase * G + grp;
+    const uint8_t *vbase = vc + rowbase * (D / 2) + part * 16;
+    const uint32_t *vmb = vm + rowbase * G + grp;
+
+    tk_hist_clear(hist);
+    for (int w = tid; w < nwords; w += TH) cbits[w] = 0u;
+    __syncthreads();
+
+    // ---- scores of every position: the upper key bits into LDS, the maximum
+    float lmax = -INFINITY;
+    constexpr int BLOCK_TOK = kTkLongUnroll * NW * TPI;
+    for (int base = 0; base < L; base += BLOCK_TOK) {
+        uint4 Kr[kTkLongUnroll];
+        uint32_t Km[kTkLongUnroll];
+#pragma unroll
+        for (int u = 0; u < kTkLongUnroll; ++u) {
+            const int j = base + (u * NW + wv) * TPI + slot;
+            const size_t jc = (size_t)(j < L ? j : L - 1);   // past the end: re-read the last row
+            Kr[u] = tk_stream_load16(kbase + jc * (D / 2));
+            Km[u] = __builtin_nontemporal_load(kmb + jc * G);
+        }
+#pragma unroll
+        for (int u = 0; u < kTkLongUnroll; ++u) {
+            const int j = base + (u * NW + wv) * TPI + slot;
+            const float s = tk_score<PARTS>(Kr[u], Km[u], QP, qsum, scale);
+            if (j < L) {
+                if (part == 0) key16[j] = (uint16_t)(order_key(s) >> 16);
+                lmax = fmaxf(lmax, s);
+            }
+        }
+    }
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) lmax = fmaxf(lmax, __shfl_xor(lmax, off, 64));
+    if (lane == 0) wmax[wv] = lmax;
+    __syncthreads();
+    float m = wmax[0];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) m = fmaxf(m, wmax[w]);
+
+    // ---- radix select over the upper 16 key bits (two 8-bit digits)
+    uint32_t prefix = 0, pmask = 0, rem = (uint32_t)kk;
+    bool settled = false;
+#pragma unroll 1
+    for (int pass = 0; pass < 2; ++pass) {
+        const int shift = 8 - 8 * pass;
+        if (pass > 0) {
+            tk_hist_clear(hist);
+            __syncthreads();
+        }
+        for (int j0 = tid; j0 < L; j0 += 4 * TH) {
+            uint32_t key[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int j = j0 + u * TH;
+                key[u] = key16[j < L ? j : 0];
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                if (j0 + u * TH < L && (key[u] & pmask) == prefix) tk_hist_add(hist, (key[u] >> shift) & 255u);
+        }
+        __syncthreads();
+        tk_pick_bin<NW>(hist, cnt[0][0], sh, rem);
+        prefix |= sh[0] << shift;
+        pmask |= 255u << shift;
+        rem = sh[1];
+        if (rem == sh[2]) {   // every candidate left is kept: the cut is found
+            settled = true;
+            break;
+        }
+    }
+
+    // ---- otherwise refine inside the one 16-bit bucket `prefix`: recompute
+    // its positions' scores, store their low 16 key bits, mark them
+    uint32_t lo_prefix = 0, lo_mask = 0;
+    if (!settled) {
+        uint32_t nbuf = 0;
+        for (int base = 0;; base += kTkLongRound) {
+            const bool more = base < L;
+            if (more) {
+                uint64_t bc[SUB];
+#pragma unroll
+                for (int u = 0; u < SUB; ++u) {
+                    const int j = base + u * TH + tid;
+                    bc[u] = __ballot(j < L && key16[j] == prefix);
+                    if (lane == 0) cnt[0][u][wv] = (uint32_t)__popcll(bc[u]);
+                }
+                __syncthreads();
+                uint32_t run = nbuf;
+#pragma unroll
+                for (int u = 0; u < SUB; ++u) {
+                    const int j = base + u * TH + tid;
+                    uint32_t before, total;
+                    tk_wave_counts(cnt[0][u], before, total);
+                    if ((bc[u] >> lane) & 1ull) kept[run + before + (uint32_t)__popcll(bc[u] & lt_mask)] = j;
+                    run += total;
+                }
+                nbuf = run;
+                __syncthreads();
+            }
+            // recompute the buffered candidates once the buffer is half full, and at the end
+            if (nbuf > 0 && (!more || nbuf + kTkLongRound > (uint32_t)kTkLongKept)) {
+                for (uint32_t i0 = 0; i0 < nbuf; i0 += NW * TPI) {
+                    const uint32_t i = i0 + wv * TPI + slot;
+                    const int j = kept[i < nbuf ? i : nbuf - 1];
+                    const uint4 kr = tk_stream_load16(kbase + (size_t)j * (D / 2));
+                    const uint32_t kmeta = __builtin_nontemporal_load(kmb + (size_t)j * G);
+                    const float s = tk_score<PARTS>(kr, kmeta, QP, qsum, scale);
+                    if (i < nbuf && part == 0) {
+                        key16[j] = (uint16_t)(order_key(s) & 0xffffu);
+                        atomicOr(&cbits[j >> 5], 1u << (j & 31));
+                    }
+                }
+                nbuf = 0;
+                __syncthreads();
+            }
+            if (!more) break;
+        }
+        // two radix passes over the candidates' low 16 bits
+#pragma unroll 1
+        for (int pass = 0; pass < 2; ++pass) {
+            const int shift = 8 - 8 * pass;
+            tk_hist_clear(hist);
+            __syncthreads();
+            for (int j = tid; j < L; j += TH) {
+                if (!((cbits[j >> 5] >> (j & 31)) & 1u)) continue;
+                const uint32_t key = key16[j];
+                if ((key & lo_mask) == lo_prefix) tk_hist_add(hist, (key >> shift) & 255u);
+            }
+            __syncthreads();
+            tk_pick_bin<NW>(hist, cnt[0][0], sh, rem);
+            lo_prefix |= sh[0] << shift;
+            lo_mask |= 255u << shift;
+            rem = sh[1];
+            if (rem == sh[2]) break;
+        }
+    }
+    // Kept: positions whose upper key bits (masked by pmask) exceed prefix;
+    // when settled, every one equal to it; otherwise the candidates whose low
+    // bits (masked by lo_mask) exceed lo_prefix, and the first `rem` by
+    // position of those equal to it.
+
+    // ---- ordered compaction into the LDS buffer, P.V each time it is half full
+    float o[32];
+#pragma unroll
+    for (int e = 0; e < 32; ++e) o[e] = 0.f;
+    float l_acc = 0.f, m_acc = 0.f;
+    const float ml2 = m * kTkLog2e;
+    uint32_t carry_eq = 0, nbuf = 0, flushed = 0;
+    for (int base = 0;; base += kTkLongRound) {
+        const bool more = base < L;
+        if (more) {
+            bool gt[SUB];
+            uint64_t be[SUB];
+#pragma unroll
+            for (int u = 0; u < SUB; ++u) {
+                const int j = base + u * TH + tid;
+                bool g = false, e = false;
+                if (j < L) {
+                    const uint32_t key = key16[j];
+                    if (!settled && ((cbits[j >> 5] >> (j & 31)) & 1u)) {
+                        g = (key & lo_mask) > lo_prefix;
+                        e = (key & lo_mask) == lo_prefix;
+                    } else {
+                        g = (key & pmask) > prefix;
+                        e = settled && (key & pmask) == prefix;
+                    }
+                }
+                gt[u] = g;
+                be[u] = __ballot(e);
+                if (lane == 0) cnt[0][u][wv] = (uint32_t)__popcll(be[u]);
+            }
+            __syncthreads();
+            uint64_t bk[SUB];
+            uint32_t run = carry_eq;
+#pragma unroll
+            for (int u = 0; u < SUB; ++u) {
+                uint32_t before, total;
+                tk_wave_counts(cnt[0][u], before, total);
+                const bool e = (be[u] >> lane) & 1ull;
+                const bool keep = gt[u] || (e && run + before + (uint32_t)__popcll(be[u] & lt_mask) < rem);
+                run += total;
+                bk[u] = __ballot(keep);
+                if (lane == 0) cnt[1][u][wv] = (uint32_t)__popcll(bk[u]);
+            }
+            carry_eq = run;
+            __syncthreads();
+            uint32_t runk = nbuf;
+#pragma unroll
+            for (int u = 0; u < SUB; ++u) {
+                const int j = base + u * TH + tid;
+                uint32_t before, total;
+                tk_wave_counts(cnt[1][u], before, total);
+                const uint32_t pos = runk + before + (uint32_t)__popcll(bk[u] & lt_mask);
+                if (((bk[u] >> lane) & 1ull) && flushed + pos < (uint32_t)kk) {
+                    kept[pos] = j;
+                    if (sel) sel[(size_t)bh * kk + flushed + pos] = j;
+                }
+                runk += total;
+            }
+            nbuf = runk;
+            if (flushed + nbuf > (uint32_t)kk) nbuf = (uint32_t)kk - flushed;   // never more than kk in all
+            __syncthreads();
+        }
+        if (nbuf > 0 && (!more || nbuf + kTkLongRound > (uint32_t)kTkLongKept)) {
+            constexpr int PV_U = 4;
+            for (uint32_t i0 = 0; i0 < nbuf; i0 += PV_U * NW * TPI) {
+                uint4 Kr[PV_U], Vr[PV_U];
+                uint32_t Kmeta[PV_U], Vmeta[PV_U];
+                bool ok[PV_U];
+#pragma unroll
+                for (int u = 0; u < PV_U; ++u) {
+                    const uint32_t i = i0 + (u * NW + wv) * TPI + slot;
+                    ok[u] = i < nbuf;
+                    const size_t j = (size_t)min(max(kept[ok[u] ? i : nbuf - 1], 0), L - 1);
+                    Kr[u] = tk_stream_load16(kbase + j * (D / 2));
+                    Kmeta[u] = __builtin_nontemporal_load(kmb + j * G);
+                    Vr[u] = tk_stream_load16(vbase + j * (D / 2));
+                    Vmeta[u] = __builtin_nontemporal_load(vmb + j * G);
+                }
+#pragma unroll
+                for (int u = 0; u < PV_U; ++u) {
+                    const float s = tk_score<PARTS>(Kr[u], Kmeta[u], QP, qsum, scale);
+                    if (!ok[u]) continue;
+                    const float p = __builtin_amdgcn_exp2f(s * kTkLog2e - ml2);
+                    l_acc += p;
+                    m_acc += p * h2f((uint16_t)(Vmeta[u] & 0xffffu));
+                    tk_pv(o, Vr[u], p * h2f((uint16_t)(Vmeta[u] >> 16)));
+                }
+            }
+            flushed += nbuf;
+            nbuf = 0;
+            __syncthreads();
+        }
+        if (!more) break;
+    }
+
+    // sum over the token slots of the wave (lanes with the same part), then over waves
+#pragma unroll
+    for (int off = PARTS; off < 64; off <<= 1) {
+#pragma unroll
+        for (int e = 0; e < 32; ++e) o[e] += __shfl_xor(o[e], off, 64);
+        l_acc += __shfl_xor(l_acc, off, 64);
+        m_acc += __shfl_xor(m_acc, off, 64);
+    }
+    if (slot == 0) {
+#pragma unroll
+        for (int e = 0; e < 32; ++e) red_o[wv][part * 32 + e] = o[e];
+        red_m[wv][part] = m_acc;
+        if (part == 0) red_l[wv] = l_acc;
+    }
+    __syncthreads();
+    if (tid < D) {
+        float num = 0.f, mins = 0.f, den = 0.f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+            num += red_o[w][tid];
+            mins += red_m[w][tid / 32];
+            den += red_l[w];
+        }
+        const float v = (num + mins) / den;
+        if (out_f16)
+            static_cast<_Float16 *>(out)[(size_t)bh * D + tid] = (_Float16)v;
+        else
+            static_cast<float *>(out)[(size_t)bh * D + tid] = v;
+    }
+}
+
 }  // namespace
 
 size_t attn_topk_lds_bytes(int32_t kv_len, int32_t kept) {
     return ((size_t)kv_len + (size_t)kept) * 4;
 }
+
+// Dynamic LDS of the long-context kernel: 16-bit keys and the candidate bitmap.
+size_t attn_topk_long_lds_bytes(int32_t kv_len) {
+    return (((size_t)kv_len + 1) / 2 + ((size_t)kv_len + 31) / 32) * 4;
+}
+
+// Scores and kept list in fp32 up to this many bytes of LDS (two workgroups
+// per CU); longer contexts take the 16-bit-key kernel.
+constexpr size_t kTopkF32Lds = 15360 * 4;
 
 // Contexts up to this length run one wavefront per (sequence, head); longer
 // ones one workgroup per (sequence, head).
@@ -607,15 +1011,39 @@ fgq_status launch_decode_attn_topk(const fgq_kv_cache *kv, const void *q, int32_
         return check_launch("attn_topk_wave_kernel");
     }
     const size_t lds = attn_topk_lds_bytes(kv_len, kept);
+    if (lds <= kTopkF32Lds) {
+        if (kv->head_dim == 128)
+            attn_topk_kernel<128><<<dim3((unsigned)items), dim3(kTkThreads), lds, stream>>>(
+                kv->k_codes, kv->k_meta, kv->v_codes, kv->v_meta, qh, kv->heads, kv->capacity, kv_len, kept, scale,
+                out, f16, sel);
+        else
+            attn_topk_kernel<64><<<dim3((unsigned)items), dim3(kTkThreads), lds, stream>>>(
+                kv->k_codes, kv->k_meta, kv->v_codes, kv->v_meta, qh, kv->heads, kv->capacity, kv_len, kept, scale,
+                out, f16, sel);
+        return check_launch("attn_topk_kernel");
+    }
+    // long contexts: 16-bit keys and a candidate bitmap in LDS
+    const void *fn = kv->head_dim == 128 ? reinterpret_cast<const void *>(&attn_topk_long_kernel<128>)
+                                         : reinterpret_cast<const void *>(&attn_topk_long_kernel<64>);
+    const size_t lds_long = attn_topk_long_lds_bytes(kv_len);
+    int dev = 0, max_lds = 0;
+    hipFuncAttributes fa{};
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&max_lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev);
+    if (e == hipSuccess) e = hipFuncGetAttributes(&fa, fn);
+    if (e != hipSuccess) return fail(FGQ_ERR_DEVICE, "top-k attention: %s", hipGetErrorString(e));
+    if (lds_long + fa.sharedSizeBytes > (size_t)max_lds)
+        return fail(FGQ_ERR_UNSUPPORTED, "kv_len %d needs %zu bytes of LDS per workgroup (device: %d)", kv_len,
+                    lds_long + fa.sharedSizeBytes, max_lds);
     if (kv->head_dim == 128)
-        attn_topk_kernel<128><<<dim3((unsigned)items), dim3(kTkThreads), lds, stream>>>(
+        attn_topk_long_kernel<128><<<dim3((unsigned)items), dim3(kTkLongThreads), lds_long, stream>>>(
             kv->k_codes, kv->k_meta, kv->v_codes, kv->v_meta, qh, kv->heads, kv->capacity, kv_len, kept, scale, out,
             f16, sel);
     else
-        attn_topk_kernel<64><<<dim3((unsigned)items), dim3(kTkThreads), lds, stream>>>(
+        attn_topk_long_kernel<64><<<dim3((unsigned)items), dim3(kTkLongThreads), lds_long, stream>>>(
             kv->k_codes, kv->k_meta, kv->v_codes, kv->v_meta, qh, kv->heads, kv->capacity, kv_len, kept, scale, out,
             f16, sel);
-    return check_launch("attn_topk_kernel");
+    return check_launch("attn_topk_long_kernel");
 }
 
 }  // namespace fgq

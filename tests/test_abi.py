@@ -161,10 +161,11 @@ def test_topk_attention_validation(lib):
     assert _status(lambda: t(_kv(), GOOD, 4, 2, 0.0, GOOD, 0, BAD, 0)) == fgq.FGQ_ERR_ALIGN
     assert _status(lambda: t(_kv(), 0, 4, 2, 0.0, GOOD, 0, None, 0)) == fgq.FGQ_ERR_INVALID_ARG
     assert _status(lambda: t(_kv(head_dim=96), GOOD, 4, 2, 0.0, GOOD, 0, None, 0)) == fgq.FGQ_ERR_SHAPE
-    # the scores and kept list of one (sequence, head) must fit on chip
-    cap = 20000
-    assert _status(lambda: t(_kv(cap=cap), GOOD, 14000, 1400, 0.0, GOOD, 0, None, 0)) == fgq.FGQ_ERR_UNSUPPORTED
-    assert _status(lambda: t(_kv(cap=cap), GOOD, 8000, 8000, 0.0, GOOD, 0, None, 0)) == fgq.FGQ_ERR_UNSUPPORTED
+    # the selection state of one (sequence, head) must fit on chip: kv_len <= 65536
+    assert fgq.FGQ_TOPK_MAX_POSITIONS == 65536
+    cap = 70000
+    assert _status(lambda: t(_kv(cap=cap), GOOD, 65537, 1, 0.0, GOOD, 0, None, 0)) == fgq.FGQ_ERR_UNSUPPORTED
+    assert _status(lambda: t(_kv(cap=cap), GOOD, 70000, 7000, 0.0, GOOD, 0, None, 0)) == fgq.FGQ_ERR_UNSUPPORTED
     # empty batch: nothing to do, no pointer is touched
     assert _status(lambda: t(_kv(batch=0), 0, 4, 2, 0.0, 0, 0, None, 0)) == fgq.FGQ_OK
 
@@ -279,3 +280,16 @@ def test_gemm_workspace_covers_every_workload():
             need = fgq.fgq_dequant_gemm_ws_bytes(w.batch, K, N)
             assert need % 16 == 0
             assert need <= 64 * w.batch * N * 4        # at most 64 split-K partial tiles
+
+
+def test_binding_constants_match_the_header():
+    import re
+    text = open(fgq.HEADER_PATH).read()
+    defs = dict(re.findall(r"^#define (FGQ_[A-Z0-9_]+) +\(?(-?[0-9]+)\)? *(?:/\*.*)?$", text, re.M))
+    names = ["FGQ_OK", "FGQ_ERR_INVALID_ARG", "FGQ_ERR_SHAPE", "FGQ_ERR_ALIGN", "FGQ_ERR_CAPACITY",
+             "FGQ_ERR_WORKSPACE", "FGQ_ERR_DTYPE", "FGQ_ERR_DEVICE", "FGQ_ERR_UNSUPPORTED", "FGQ_DTYPE_F32",
+             "FGQ_DTYPE_F16", "FGQ_GQA_MAX_GROUP", "FGQ_TOPK_MAX_POSITIONS"]
+    for n in names:
+        assert n in defs, n
+        assert getattr(fgq, n) == int(defs[n]), n
+    assert "FGQ_NOALLOC_SCRATCH_BYTES ((size_t)9 << 20)" in text and fgq.FGQ_NOALLOC_SCRATCH_BYTES == 9 << 20

@@ -247,3 +247,98 @@ def test_topk_repeatable_bitwise():
     a, sa = dev.attend_topk(q, L, 410)
     b, sb = dev.attend_topk(q, L, 410)
     assert np.array_equal(a, b) and np.array_equal(sa, sb)
+
+
+def _random_case(B, H, D, L, seed):
+    rng = np.random.default_rng(seed)
+    k16 = rng.standard_normal((B, L, H * D)).astype(np.float16)
+    v16 = rng.standard_normal((B, L, H * D)).astype(np.float16)
+    q = rng.standard_normal((B, H * D)).astype(np.float16)
+    dev = gu.DevKV(B, H, D, L)
+    ref = oracle.KVCache(B, H, D, L)
+    dev.append(k16, v16, 0)
+    oracle.kv_append(ref, k16, v16, 0)
+    return dev, ref, q
+
+
+@pytest.mark.parametrize("L,D", [(14000, 128), (16416, 128), (40000, 64), (65536, 128)])
+def test_topk_long_contexts(L, D):
+    """Contexts whose fp32 scores and kept list would take more than 60 KB of
+    LDS run the 16-bit-key kernel (candidate refinement inside the cut's
+    bucket, P.V in buffered passes): 10% kept, a few, half, and everything."""
+    dev, ref, q = _random_case(1, 2, D, L, L + D)
+    for k in (math.ceil(L / 10), 3, L // 2):
+        _topk_check(dev, ref, q, L, k, "long L=%d D=%d" % (L, D))
+    got, gsel = _topk_check(dev, ref, q, L, L, "long L=%d D=%d, all kept" % (L, D))
+    gu.assert_close(got, dev.attend(q, L), "long top-k (all kept) vs dense kernel")
+    assert np.array_equal(gsel, np.broadcast_to(np.arange(L, dtype=np.int32), gsel.shape))
+
+
+def test_topk_long_context_exact_ties_span_buffers():
+    """Five distinct K rows per (sequence, head) over 20000 positions: the cut
+    falls inside a run of ~4000 bit-identical scores, more candidates than one
+    LDS buffer holds; the kept set must equal the oracle's (lower positions
+    first)."""
+    B, H, D, L = 1, 2, 128, 20000
+    rng = np.random.default_rng(5)
+    base = rng.standard_normal((B, H, 5, D)).astype(np.float16)
+    pick = rng.integers(0, 5, (B, H, L))
+    k16 = np.take_along_axis(base, pick[..., None].repeat(D, -1), axis=2)
+    k16 = np.ascontiguousarray(k16.transpose(0, 2, 1, 3).reshape(B, L, H * D))
+    v16 = rng.standard_normal((B, L, H * D)).astype(np.float16)
+    q = rng.standard_normal((B, H * D)).astype(np.float16)
+    dev = gu.DevKV(B, H, D, L)
+    ref = oracle.KVCache(B, H, D, L)
+    dev.append(k16, v16, 0)
+    oracle.kv_append(ref, k16, v16, 0)
+    for k in (1, 2000, 6500, L - 1):
+        got, gsel = dev.attend_topk(q, L, k)
+        exp, osel = oracle.decode_attn_topk(ref, q, L, k)
+        gu.note("long exact ties top_k %d" % k)
+        assert np.array_equal(gsel, osel), k
+        gu.assert_close(got, exp, "long exact ties k=%d" % k)
+
+
+def test_topk_long_context_all_scores_equal():
+    """A zero query makes every score 0: the whole context is one candidate
+    bucket; the first kk positions are kept and the output is their mean V."""
+    B, H, D, L = 2, 2, 64, 30000
+    dev, ref, _ = _random_case(B, H, D, L, 9)
+    q = np.zeros((B, H * D), np.float16)
+    kk = 3000
+    got, gsel = dev.attend_topk(q, L, kk)
+    exp, osel = oracle.decode_attn_topk(ref, q, L, kk)
+    assert np.array_equal(gsel, np.broadcast_to(np.arange(kk, dtype=np.int32), gsel.shape))
+    assert np.array_equal(osel, gsel)
+    gu.assert_close(got, exp, "all scores equal")
+
+
+def test_topk_16k_context_full_heads_sampled():
+    """The grouped-query workload's context (16 sequences, 32 heads, 16416
+    positions) as multi-head attention: one launch, three sequences against
+    the oracle at 10% kept."""
+    B, H, D, L = 16, 32, 128, 16416
+    gu.note("top-k 16k context B=%d H=%d L=%d" % (B, H, L))
+    rng = np.random.default_rng(77)
+    dev = gu.DevKV(B, H, D, L)
+    ks, vs = [], []
+    for b in range(B):
+        k16 = rng.standard_normal((1, L, H * D)).astype(np.float16)
+        v16 = rng.standard_normal((1, L, H * D)).astype(np.float16)
+        sub = gu.fgq.kv_struct(dev.k_codes[b:b + 1], dev.v_codes[b:b + 1], dev.k_meta[b:b + 1], dev.v_meta[b:b + 1],
+                               1, H, D, L)
+        gu.fgq.fgq_kv_append(sub, gu.to_dev(k16), gu.to_dev(v16), 0, L)
+        ks.append(k16)
+        vs.append(v16)
+    q = rng.standard_normal((B, H * D)).astype(np.float16)
+    k = math.ceil(L / 10)
+    got, gsel = dev.attend_topk(q, L, k)
+    for b in (0, 7, 15):
+        ref = oracle.KVCache(1, H, D, L)
+        oracle.kv_append(ref, ks[b], vs[b], 0)
+
+        class _One:
+            def attend_topk(self, q_, L_, k_, scale=0.0, out_f16=False):
+                return got[b:b + 1], gsel[b:b + 1]
+
+        _topk_check(_One(), ref, q[b:b + 1], L, k, "16k context seq %d" % b)
