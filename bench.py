@@ -82,6 +82,9 @@ def parse():
     ap.add_argument("--gqa-only", action="store_true",
                     help="only run the grouped-query attention line (for profiling that kernel)")
     ap.add_argument("--no-gqa-sweep", action="store_true", help="skip the K/V-head sweep of the grouped line")
+    ap.add_argument("--prefill-only", action="store_true",
+                    help="only time causal prefill attention (OPT-175B heads: 8 x 512 and 1 x 4096 tokens; "
+                         "for profiling that kernel)")
     ap.add_argument("--summarize-gqa-trace", metavar="DIR",
                     help="only summarise a rocprofv3 --kernel-trace --stats folder of a --gqa-only run")
     ap.add_argument("--cpu-sample-seqs", type=int, default=4)
@@ -701,6 +704,37 @@ def prefill_and_bulk_lines(torch, fgq, w, ch, stream) -> dict:
                                "us_whole_block_estimate": bulk_us * B / nb}}
 
 
+def prefill_only_lines(torch, fgq, stream, reps: int) -> dict:
+    """Causal prefill attention alone at OPT-175B's heads (96 x 128), on the
+    seeded prompt recipe: 8 sequences of 512 tokens (the 8-wave launch) and
+    one of 4096 (the long-prompt launch), reps launches each after a warm-up."""
+    w = synth.WORKLOADS["opt-175b"]
+    H, D, h = w.heads, w.head_dim, w.hidden
+    sh = stream.cuda_stream
+    lines = {}
+    for nb, S in ((8, 512), (1, 4096)):
+        rng = np.random.default_rng(S)
+        qd, kd, vd = (torch.from_numpy(rng.standard_normal((nb, S, h)).astype(np.float16)).to("cuda")
+                      for _ in range(3))
+        out = torch.empty((nb, S, h), dtype=torch.float16, device="cuda")
+
+        def run(_i=0):
+            fgq.fgq_prefill_attn_f16(qd, kd, vd, nb, S, H, D, 0.0, out, fgq.FGQ_DTYPE_F16, sh)
+        warm_up(torch, run, 0, 8, 200.0)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            run()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = 1e3 * e0.elapsed_time(e1) / reps
+        fl = acc.prefill_attention_flops(nb, h, S)
+        lines["%dx%d" % (nb, S)] = {"us_per_launch": us, "TFLOP_per_s": fl / (us * 1e-6) / 1e12,
+                                    "frac_mfma_peak": fl / (us * 1e-6) / 1e12 / MFMA_F16_PEAK_TFLOPS}
+        del qd, kd, vd, out
+    return lines
+
+
 def topk_line(torch, fgq, w, ch, stream, steps, warmup) -> dict:
     """Top-K sparse attention (keep the top tenth of the positions, read only
     their V rows) over the same caches and decode steps, queries drawn per
@@ -1145,7 +1179,8 @@ def main():
         return
     if args.summarize_counters:
         summarize_counters(args.summarize_counters, ("dq_gemm_kernel", "attn_split_kernel", "attn_merge_kernel",
-                                                     "kv_append_kernel", "splitk_reduce_kernel"))
+                                                     "kv_append_kernel", "splitk_reduce_kernel",
+                                                     "prefill_attn_kernel"))
         return
     if args.summarize_pmc:
         w = synth.WORKLOADS[args.config]
@@ -1189,6 +1224,10 @@ def main():
         line = gqa_attention_line(torch, fgq, torch.cuda.current_stream(), args.steps, args.warmup,
                                   () if args.no_gqa_sweep else (32, 16, 8, 4, 2, 1))
         print(json.dumps({"gqa_attention": line}), flush=True)
+        return
+    if args.prefill_only:
+        print(json.dumps({"prefill_attention": prefill_only_lines(torch, fgq, torch.cuda.current_stream(),
+                                                                  args.steps)}), flush=True)
         return
     w = synth.WORKLOADS[args.config]
     B, H, D, h = w.batch, w.heads, w.head_dim, w.hidden
