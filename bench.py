@@ -1207,8 +1207,8 @@ def main():
         print("traffic-json: " + json.dumps(d))
         return
     if args.gpus != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (the kernels shard by "
-              "sequence/head and by weight column; see DESIGN.md). Run with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU: the library has no multi-GPU path (the work would shard by "
+              "sequence and head, and the weights by column group). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
     import torch
     import int4_group_quantized_fgq_amd as fgq

@@ -183,7 +183,7 @@ def test_prefill_attention_validation(lib):
     assert _status(lambda: p(0, 0, 0, 2, 0, 2, 128, 0.0, 0, 0, 0)) == fgq.FGQ_OK     # empty prompt
 
 
-def test_canonical_gemm_signature_matches_the_survey_boundary(lib):
+def test_canonical_gemm_signature_takes_the_quantiser_layout(lib):
     """fgq_dequant_gemm takes the quantiser's own layout: uint8 codes
     [K][N/2] and the metadata words [K][N/64], as const pointers."""
     import re
