@@ -244,6 +244,21 @@ def test_chain_opt175b_stagewise_sampled():
     _stage_checks(ch, x0, 1, seqs=(0, 77, 143), col_slices=lambda N: (0, N // 2 + 64, N - 256))
 
 
+def test_chain_opt30b_stagewise_sampled_canonical():
+    """OPT-30B layer, B = 96 (six 16-row tiles, the row count between the
+    other two chains), straight from the quantiser's codes: one decode step,
+    every stage against the oracle on the GPU's stage inputs, on three
+    sampled sequences and three 256-column slices of every product."""
+    w = W["opt-30b"]
+    gu.note("chain opt-30b sampled, canonical layout")
+    ch = GpuChain(w, canonical=True)
+    x0 = _layer_input(w, 1)
+    ch.step(gu.to_dev(x0), 1)
+    torch = gu.torch_cuda()
+    torch.cuda.synchronize()
+    _stage_checks(ch, x0, 1, seqs=(0, 50, 95), col_slices=lambda N: (0, N // 2 + 64, N - 256))
+
+
 def test_strided_entries_equal_contiguous_ones():
     """fgq_kv_append_ld and fgq_decode_attn_q4kv_ld over rows 3h apart give
     the same bytes as the contiguous calls on copies of those rows."""

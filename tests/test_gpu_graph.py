@@ -33,8 +33,9 @@ def _f16(tag, n, sigma=1.0):
 class _Step:
     """Static device buffers of one layer step (what a graph binds to)."""
 
-    def __init__(self, t, weights):
+    def __init__(self, t, weights, canonical=False):
         self.t = t
+        self.canonical = canonical
         self.k = gu.to_dev(_f16(10 + t, B * HID).reshape(B, 1, HID))
         self.v = gu.to_dev(_f16(20 + t, B * HID).reshape(B, 1, HID))
         self.q = gu.to_dev(_f16(30 + t, B * HID).reshape(B, HID))
@@ -50,9 +51,9 @@ class _Step:
         gu.fgq.fgq_decode_attn_q4kv(kv.struct, self.q, L, 0.0, self.attn, gu.fgq.FGQ_DTYPE_F32, attn_ws,
                                     attn_ws.numel(), s)
         for i, (_, K, N) in enumerate(GEMMS):
-            pc, pm = self.weights[i]
-            gu.fgq.fgq_dequant_gemm_packed(self.x[i], G, MB, K, N, pc, pm, self.y[i], gu.fgq.FGQ_DTYPE_F32, gemm_ws,
-                                    gemm_ws.numel(), s)
+            wc, wm = self.weights[i]
+            gemm = gu.fgq.fgq_dequant_gemm if self.canonical else gu.fgq.fgq_dequant_gemm_packed
+            gemm(self.x[i], G, MB, K, N, wc, wm, self.y[i], gu.fgq.FGQ_DTYPE_F32, gemm_ws, gemm_ws.numel(), s)
 
     def outputs(self):
         return [gu.to_host(self.attn)] + [gu.to_host(y) for y in self.y]
@@ -64,14 +65,16 @@ def _kv_with_prompt(pk, pv):
     return kv
 
 
-def test_graph_layer_step_replays_match_eager():
+@pytest.mark.parametrize("canonical", [False, True])
+def test_graph_layer_step_replays_match_eager(canonical):
     gu.torch_cuda()
-    gu.note("graph layer step: setup")
+    gu.note("graph layer step (canonical GEMM layout: %s): setup" % canonical)
     weights, host_w = [], []
     for i, (_, K, N) in enumerate(GEMMS):
         Wt = _f16(60 + i, K * N, 0.02).reshape(K, N)
         codes, meta = gu.quantize(Wt)
-        weights.append(gu.pack(gu.to_dev(codes), gu.to_dev(meta), K, N))
+        cd, md = gu.to_dev(codes), gu.to_dev(meta)
+        weights.append((cd, md) if canonical else gu.pack(cd, md, K, N))
         host_w.append((codes, meta))
     pk = _f16(1, B * PROMPT * HID).reshape(B, PROMPT, HID)
     pv = _f16(2, B * PROMPT * HID).reshape(B, PROMPT, HID)
@@ -82,8 +85,8 @@ def test_graph_layer_step_replays_match_eager():
     assert attn_wsb > 0 and gemm_wsb > 0
     attn_ws = torch.empty(attn_wsb, dtype=torch.uint8, device="cuda")
     gemm_ws = torch.empty(gemm_wsb, dtype=torch.uint8, device="cuda")
-    steps = [_Step(t, weights) for t in range(1, STEPS + 1)]
-    other = _Step(1, weights)     # eager work between replays, on buffers of its own
+    steps = [_Step(t, weights, canonical) for t in range(1, STEPS + 1)]
+    other = _Step(1, weights, canonical)     # eager work between replays, on buffers of its own
 
     gu.note("graph layer step: eager pass")
     eager = []
