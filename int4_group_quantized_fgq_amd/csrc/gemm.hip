@@ -669,15 +669,25 @@ void launch_one(const LaunchArgs &a) {
 // k-phases per workgroup: 1 and 2 for every row count; 4 and 8 (one or two
 // column groups per workgroup, phases summed in LDS) for up to 64 rows with
 // the packed layout.
-// Y = sum over splits of the partial tiles, in split order.
+// Y = sum over splits of the partial tiles, in split order.  The loads of up
+// to eight splits are in flight together (one memory latency per eight
+// splits, not per split); the sum still runs in split order.
+constexpr int kReduceBatch = 8;
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *__restrict__ part, int ksplit,
                                                             int64_t MN, void *__restrict__ y, int y_f16) {
     const int64_t i4 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
     if (i4 >= MN) return;
     float4 s = *reinterpret_cast<const float4 *>(part + i4);
-    for (int k = 1; k < ksplit; ++k) {
-        const float4 v = *reinterpret_cast<const float4 *>(part + (int64_t)k * MN + i4);
-        s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
+    for (int k = 1; k < ksplit; k += kReduceBatch) {
+        float4 v[kReduceBatch];
+#pragma unroll
+        for (int u = 0; u < kReduceBatch; ++u)
+            if (k + u < ksplit) v[u] = *reinterpret_cast<const float4 *>(part + (int64_t)(k + u) * MN + i4);
+#pragma unroll
+        for (int u = 0; u < kReduceBatch; ++u)
+            if (k + u < ksplit) {
+                s.x += v[u].x; s.y += v[u].y; s.z += v[u].z; s.w += v[u].w;
+            }
     }
     if (y_f16) {
         _Float16 *o = static_cast<_Float16 *>(y) + i4;
