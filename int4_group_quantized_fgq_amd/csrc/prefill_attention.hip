@@ -15,9 +15,9 @@
 //    waves (256 rows, two waves per SIMD) for short prompts, of 12 waves
 //    (384 rows, three per SIMD) for long ones, where the Q fragments move
 //    from registers to LDS to make room for the third wave;
-//    key blocks of 64 are staged in LDS by 8 of the waves: K row-major, V
-//    transposed (d-major), the next block's global loads in flight while the
-//    current one is multiplied;
+//    key blocks of 64 are staged in LDS by 8 of the waves, K and V both
+//    row-major, the next block's global loads in flight while the current
+//    one is multiplied;
 //  * scores are formed transposed, S^T = K Q^T, on v_mfma_f32_16x16x32_f16
 //    (A = K rows from LDS, B = the wave's Q fragments), so
 //    a lane's accumulators all belong to one query: the running max, the
@@ -25,8 +25,9 @@
 //    cross-lane steps for the row max and one pair at the end for the sum;
 //  * P.V is formed transposed too, O^T = V^T P^T, with P^T taken straight
 //    from the score accumulators: the 32 k-slots of an MFMA are mapped to
-//    keys in the order the accumulators hold them, and the V^T rows are read
-//    from LDS in the same order (two 8-byte reads per fragment);
+//    keys in the order the accumulators hold them, and the V^T fragments
+//    come from the row-major V tile through two transposing 8-byte LDS
+//    reads each (ds_read_b64_tr_b16);
 //  * online softmax in the log2 domain (exp2 on the transcendental unit);
 //    the output is rescaled only when some lane's running max moved; blocks
 //    wholly above a wave's diagonal are skipped, blocks that reach it mask
@@ -44,10 +45,9 @@ constexpr int kPfLongPrompt = 1024;          // prompts from which 12-wave workg
 constexpr int kPfKeys = 64;   // keys per block
 constexpr float kPfSlack = 8.0f;   // log2-domain headroom of the lazy rescale
 
-// Global loads of key block kb (K rows by 16-byte column chunks, coalesced
-// along each row; V one key per lane so that its transposed LDS writes hit
-// consecutive halves) into registers, rows past the prompt clamped to its
-// last token.
+// Global loads of key block kb (K and V rows by 16-byte column chunks,
+// coalesced along each row) into registers, rows past the prompt clamped to
+// its last token.
 constexpr int pf_loads(int D) { return kPfKeys * D / 8 / kPfLoadThreads; }   // 16-byte loads per thread per tile
 
 template <int D>
@@ -62,17 +62,15 @@ __device__ __forceinline__ void pf_load_tile(const uint16_t *__restrict__ k, con
         int j = kb * kPfKeys + row;
         j = j < S ? j : S - 1;
         kr[p] = *reinterpret_cast<const u32x4 *>(k + base + (size_t)j * rs + 8 * ch);
-        const int key = tid & 63, vch = (tid >> 6) + kPfLoadWaves * p;
-        int jv = kb * kPfKeys + key;
-        jv = jv < S ? jv : S - 1;
-        vr[p] = *reinterpret_cast<const u32x4 *>(v + base + (size_t)jv * rs + 8 * vch);
+        vr[p] = *reinterpret_cast<const u32x4 *>(v + base + (size_t)j * rs + 8 * ch);
     }
 }
 
-// The registers of pf_load_tile into LDS: K row-major (row stride KS
-// halves), V transposed (d-major, row stride VS halves).
-template <int D, int KS, int VS>
-__device__ __forceinline__ void pf_store_tile(uint16_t *ks, uint16_t *vt, int tid, const u32x4 (&kr)[pf_loads(D)],
+// The registers of pf_load_tile into LDS, K and V both row-major (row
+// stride KS halves: a 16-byte pad, so the 16-byte writes of a wave and the
+// transposing reads of V spread evenly over the banks).
+template <int D, int KS>
+__device__ __forceinline__ void pf_store_tile(uint16_t *ks, uint16_t *vs, int tid, const u32x4 (&kr)[pf_loads(D)],
                                               const u32x4 (&vr)[pf_loads(D)]) {
     constexpr int KCH = D / 8;
 #pragma unroll
@@ -80,17 +78,21 @@ __device__ __forceinline__ void pf_store_tile(uint16_t *ks, uint16_t *vt, int ti
         const int idx = p * kPfLoadThreads + tid;
         const int row = idx / KCH, ch = idx % KCH;
         *reinterpret_cast<u32x4 *>(ks + row * KS + 8 * ch) = kr[p];
-        const int key = tid & 63, vch = (tid >> 6) + kPfLoadWaves * p;
-        uint16_t *col = vt + 8 * vch * VS + key;
-        col[0 * VS] = (uint16_t)(vr[p][0] & 0xffffu);
-        col[1 * VS] = (uint16_t)(vr[p][0] >> 16);
-        col[2 * VS] = (uint16_t)(vr[p][1] & 0xffffu);
-        col[3 * VS] = (uint16_t)(vr[p][1] >> 16);
-        col[4 * VS] = (uint16_t)(vr[p][2] & 0xffffu);
-        col[5 * VS] = (uint16_t)(vr[p][2] >> 16);
-        col[6 * VS] = (uint16_t)(vr[p][3] & 0xffffu);
-        col[7 * VS] = (uint16_t)(vr[p][3] >> 16);
+        *reinterpret_cast<u32x4 *>(vs + row * KS + 8 * ch) = vr[p];
     }
+}
+
+// gfx950's transposing LDS read (ds_read_b64_tr_b16).  In each group of 16
+// lanes, lane j receives element j % 4 of the 8-byte pieces that lanes
+// 4e + j / 4 (e = 0..3) address, as its elements e = 0..3.  With lane
+// 16g + s addressing the four halves (row r0 + s / 4, columns c0 + 4 (s % 4)
+// .. + 3) of a row-major tile, lane 16g + j gets column c0 + j of rows
+// r0 .. r0 + 3.
+typedef short pf_v4s __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint2 pf_read_tr16(const uint16_t *p) {
+    const pf_v4s r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) pf_v4s *)(const __attribute__((address_space(3))) void *)p);
+    return __builtin_bit_cast(uint2, r);
 }
 
 template <int D, int NW>
@@ -99,7 +101,6 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW > kP
                                                            const uint16_t *__restrict__ v, int S, int H,
                                                            float sl2, void *__restrict__ out, int out_f16) {
     constexpr int KS = D + 8;            // K row stride in halves (16-byte pad)
-    constexpr int VS = kPfKeys + 4;      // V^T row stride in halves (8-byte pad)
     constexpr int NP = pf_loads(D);      // 16-byte global loads per thread per tile (K and V each)
     constexpr int KSTEP = D / 32;        // MFMA k-steps over d
     constexpr int NDT = D / 16;          // output d-tiles
@@ -112,7 +113,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW > kP
     constexpr int QS = D + 8;            // Q row stride in halves (16-byte pad)
     __shared__ __attribute__((aligned(16))) uint16_t qs[QLDS ? ROWS * QS : 8];
     __shared__ __attribute__((aligned(16))) uint16_t ks[kPfKeys * KS];
-    __shared__ __attribute__((aligned(16))) uint16_t vt[D * VS];
+    __shared__ __attribute__((aligned(16))) uint16_t vs[kPfKeys * KS];
 
     const int tid = threadIdx.x, lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 4, c = lane & 15;
@@ -170,7 +171,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW > kP
     if (loader) pf_load_tile<D>(k, v, base, rs, S, 0, tid, kr, vr);
     for (int kb = 0; kb <= kb_last; ++kb) {
         __syncthreads();                           // every wave is done with the previous tile
-        if (loader) pf_store_tile<D, KS, VS>(ks, vt, tid, kr, vr);
+        if (loader) pf_store_tile<D, KS>(ks, vs, tid, kr, vr);
         __syncthreads();
         if (kb < kb_last && loader) pf_load_tile<D>(k, v, base, rs, S, kb + 1, tid, kr, vr);   // in flight during the MFMAs
         if (kb * kPfKeys > wave_q_last) continue;  // every key of the block is past this wave's queries
@@ -263,14 +264,18 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW > kP
                     l_run[n] += pv;
                     pb[n][kk][e] = (_Float16)pv;
                 }
-        // ---- O^T += V^T P^T: row d = 16dt + c of V^T, keys in the same k-slot order
+        // ---- O^T += V^T P^T: row d = 16dt + c of V^T, keys in the same
+        // k-slot order, read transposed from the row-major V tile: lane
+        // (g, c) addresses key 32kk + 4g + c / 4 (and 16 keys on), columns
+        // 16dt + 4 (c % 4) .. + 3, and receives column 16dt + c of keys
+        // 32kk + 4g .. + 3 (and 32kk + 16 + 4g .. + 3)
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
             for (int t = 0; t < NDT; ++t) {
-                const uint16_t *vrow = vt + (16 * t + c) * VS + 32 * kk + 4 * g;
-                const uint2 lo = *reinterpret_cast<const uint2 *>(vrow);
-                const uint2 hi = *reinterpret_cast<const uint2 *>(vrow + 16);
+                const uint16_t *vrow = vs + (32 * kk + 4 * g + (c >> 2)) * KS + 16 * t + 4 * (c & 3);
+                const uint2 lo = pf_read_tr16(vrow);
+                const uint2 hi = pf_read_tr16(vrow + 16 * KS);
                 const u32x4 a4 = {lo.x, lo.y, hi.x, hi.y};
                 const f16x8 a = __builtin_bit_cast(f16x8, a4);
 #pragma unroll
