@@ -39,46 +39,69 @@ namespace {
 
 constexpr float kPfLog2e = 1.4426950408889634f;
 constexpr int kPfWaveRows = 32;              // query rows per wave (two 16-row MFMA tiles)
-constexpr int kPfLoadWaves = 8;              // waves that stage the K/V tiles
-constexpr int kPfLoadThreads = 64 * kPfLoadWaves;
+constexpr int kPfQRegWaves = 8;              // up to this many waves per workgroup keep Q in registers
 constexpr int kPfLongPrompt = 1024;          // prompts from which 12-wave workgroups are used
 constexpr int kPfKeys = 64;   // keys per block
 constexpr float kPfSlack = 8.0f;   // log2-domain headroom of the lazy rescale
 
-// Global loads of key block kb (K and V rows by 16-byte column chunks,
-// coalesced along each row) into registers, rows past the prompt clamped to
-// its last token.
-constexpr int pf_loads(int D) { return kPfKeys * D / 8 / kPfLoadThreads; }   // 16-byte loads per thread per tile
-
+// LDS tiles are unpadded row-major [rows][D] with the 16-byte chunks of a
+// row XOR-swizzled: chunk ch of row r sits at chunk position ch ^ (r % CH)
+// (CH = D / 8 chunks per row), so the fragment reads of 16 rows, the
+// 16-byte row writes and the transposing V reads spread over the banks.
 template <int D>
-__device__ __forceinline__ void pf_load_tile(const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
-                                             size_t base, size_t rs, int S, int kb, int tid,
-                                             u32x4 (&kr)[pf_loads(D)], u32x4 (&vr)[pf_loads(D)]) {
-    constexpr int KCH = D / 8;                     // 16-byte chunks per row
-#pragma unroll
-    for (int p = 0; p < pf_loads(D); ++p) {
-        const int idx = p * kPfLoadThreads + tid;
-        const int row = idx / KCH, ch = idx % KCH;
-        int j = kb * kPfKeys + row;
-        j = j < S ? j : S - 1;
-        kr[p] = *reinterpret_cast<const u32x4 *>(k + base + (size_t)j * rs + 8 * ch);
-        vr[p] = *reinterpret_cast<const u32x4 *>(v + base + (size_t)j * rs + 8 * ch);
-    }
+__device__ __forceinline__ int pf_pos(int row, int ch) {
+    return ch ^ (row & (D / 8 - 1));
 }
 
-// The registers of pf_load_tile into LDS, K and V both row-major (row
-// stride KS halves: a 16-byte pad, so the 16-byte writes of a wave and the
-// transposing reads of V spread evenly over the banks).
-template <int D, int KS>
-__device__ __forceinline__ void pf_store_tile(uint16_t *ks, uint16_t *vs, int tid, const u32x4 (&kr)[pf_loads(D)],
-                                              const u32x4 (&vr)[pf_loads(D)]) {
-    constexpr int KCH = D / 8;
+// LDS byte address of a pointer into a __shared__ array.
+__device__ __forceinline__ uint32_t pf_lds_addr(const void *p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
+}
+
+// Direct global->LDS load of 16 bytes per lane (gfx950's
+// global_load_lds_dwordx4): lane i's bytes land at LDS address lds + 16 i
+// (lds wave-uniform, passed in M0).  Written as inline assembly so the
+// compiler does not count it as an LDS store; the kernel waits for it with
+// an explicit vmcnt before the barrier that publishes the tile.  M0 is used
+// by nothing else in this kernel.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void pf_dma16(const void *gptr, uint32_t lds) {
+    const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds);
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "s"(m0v) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// Every load of this wave's loads has landed (vmcnt 0).
+__device__ __forceinline__ void pf_wait_loads() {
+    // simm16: vmcnt[3:0] = 0 | expcnt[6:4] = 7 | lgkmcnt[11:8] = 15 | vmcnt[5:4] = 0
+    __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
+}
+
+// Issue the direct-to-LDS loads of key block kb (K and V, 64 rows each,
+// rows past the prompt clamped to its last token): load instruction i fills
+// bytes [1024 i, 1024 i + 1024) of a tile, i.e. rows RPI*i .. RPI*i + RPI-1,
+// lane L taking row RPI*i + L / CH at chunk position L % CH, so it reads the
+// swizzled chunk (L % CH) ^ (row % CH).  Instructions are dealt to the
+// waves round-robin.
+template <int D, int NW>
+__device__ __forceinline__ void pf_issue_tile(const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
+                                              size_t base, size_t rs, int S, int kb, int wv, int lane,
+                                              uint16_t *kt, uint16_t *vt) {
+    constexpr int CH = D / 8;               // 16-byte chunks per row
+    constexpr int RPI = 64 / CH;            // rows per load instruction
+    constexpr int NI = kPfKeys / RPI;       // load instructions per tile
+    const int rl = lane / CH, pl = lane % CH;
 #pragma unroll
-    for (int p = 0; p < pf_loads(D); ++p) {
-        const int idx = p * kPfLoadThreads + tid;
-        const int row = idx / KCH, ch = idx % KCH;
-        *reinterpret_cast<u32x4 *>(ks + row * KS + 8 * ch) = kr[p];
-        *reinterpret_cast<u32x4 *>(vs + row * KS + 8 * ch) = vr[p];
+    for (int i0 = 0; i0 < NI; i0 += NW) {
+        const int i = i0 + wv;
+        if (NI % NW != 0 && i >= NI) break;
+        const int row = RPI * i + rl;
+        int j = kb * kPfKeys + row;
+        j = j < S ? j : S - 1;
+        const size_t off = base + (size_t)j * rs + 8 * (pl ^ (row & (CH - 1)));
+        pf_dma16(k + off, pf_lds_addr(kt) + 1024 * i);
+        pf_dma16(v + off, pf_lds_addr(vt) + 1024 * i);
     }
 }
 
@@ -96,12 +119,10 @@ __device__ __forceinline__ uint2 pf_read_tr16(const uint16_t *p) {
 }
 
 template <int D, int NW>
-__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW > kPfLoadWaves ? 3 : 2))) void prefill_attn_kernel(const uint16_t *__restrict__ q,
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW > kPfQRegWaves ? 3 : 2))) void prefill_attn_kernel(const uint16_t *__restrict__ q,
                                                            const uint16_t *__restrict__ k,
                                                            const uint16_t *__restrict__ v, int S, int H,
                                                            float sl2, void *__restrict__ out, int out_f16) {
-    constexpr int KS = D + 8;            // K row stride in halves (16-byte pad)
-    constexpr int NP = pf_loads(D);      // 16-byte global loads per thread per tile (K and V each)
     constexpr int KSTEP = D / 32;        // MFMA k-steps over d
     constexpr int NDT = D / 16;          // output d-tiles
     constexpr int QT = kPfWaveRows / 16; // query tiles per wave
@@ -109,11 +130,13 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW > kP
     constexpr int ROWS = NW * kPfWaveRows;   // query rows per workgroup
     // Above 8 waves the Q fragments live in LDS (read per k-step) instead of
     // registers, which brings a wave under 168 VGPRs: three waves per SIMD
-    constexpr bool QLDS = NW > kPfLoadWaves;
-    constexpr int QS = D + 8;            // Q row stride in halves (16-byte pad)
-    __shared__ __attribute__((aligned(16))) uint16_t qs[QLDS ? ROWS * QS : 8];
-    __shared__ __attribute__((aligned(16))) uint16_t ks[kPfKeys * KS];
-    __shared__ __attribute__((aligned(16))) uint16_t vs[kPfKeys * KS];
+    constexpr bool QLDS = NW > kPfQRegWaves;
+    // Q rows (QLDS), and two K and two V tiles: key block kb is multiplied
+    // from buffer kb % 2 while block kb + 1 loads into the other; all
+    // unpadded with swizzled chunks (pf_pos)
+    __shared__ __attribute__((aligned(1024))) uint16_t ktile[2][kPfKeys * D];
+    __shared__ __attribute__((aligned(1024))) uint16_t vtile[2][kPfKeys * D];
+    __shared__ __attribute__((aligned(16))) uint16_t qs[QLDS ? ROWS * D : 8];
 
     const int tid = threadIdx.x, lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 4, c = lane & 15;
@@ -136,7 +159,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW > kP
             const int row = idx / QCH, ch = idx % QCH;
             int qr = qb * ROWS + row;
             qr = qr < S ? qr : S - 1;
-            *reinterpret_cast<u32x4 *>(qs + row * QS + 8 * ch) =
+            *reinterpret_cast<u32x4 *>(qs + row * D + 8 * pf_pos<D>(row, ch)) =
                 *reinterpret_cast<const u32x4 *>(q + base + (size_t)qr * rs + 8 * ch);
         }
     } else {
@@ -148,9 +171,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW > kP
                 qf[n][s] = *reinterpret_cast<const f16x8 *>(q + base + (size_t)qic * rs + 32 * s + 8 * g);
         }
     }
-    const uint16_t *qw = qs + (wv * kPfWaveRows + c) * QS + 8 * g;   // this lane's Q in LDS (QLDS)
-
-    u32x4 kr[NP], vr[NP];
+    const int qrow = wv * kPfWaveRows + c;      // this lane's first Q row in LDS (QLDS)
     f32x4 o[NDT][QT];
 #pragma unroll
     for (int t = 0; t < NDT; ++t)
@@ -167,14 +188,17 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW > kP
     const int q_last = min(qb * ROWS + ROWS, S) - 1;
     const int kb_last = q_last / kPfKeys;
     const int wave_q_last = q0 + kPfWaveRows - 1;
-    const bool loader = NW == kPfLoadWaves || wv < kPfLoadWaves;   // this wave stages K/V tiles
-    if (loader) pf_load_tile<D>(k, v, base, rs, S, 0, tid, kr, vr);
+    pf_issue_tile<D, NW>(k, v, base, rs, S, 0, wv, lane, ktile[0], vtile[0]);
     for (int kb = 0; kb <= kb_last; ++kb) {
-        __syncthreads();                           // every wave is done with the previous tile
-        if (loader) pf_store_tile<D, KS>(ks, vs, tid, kr, vr);
+        // block kb has landed (this wave's loads, then every wave's), and
+        // every wave is done with block kb - 1, whose buffer block kb + 1
+        // now fills while block kb is multiplied
+        pf_wait_loads();
         __syncthreads();
-        if (kb < kb_last && loader) pf_load_tile<D>(k, v, base, rs, S, kb + 1, tid, kr, vr);   // in flight during the MFMAs
+        if (kb < kb_last) pf_issue_tile<D, NW>(k, v, base, rs, S, kb + 1, wv, lane, ktile[(kb + 1) & 1], vtile[(kb + 1) & 1]);
         if (kb * kPfKeys > wave_q_last) continue;  // every key of the block is past this wave's queries
+        const uint16_t *ks = ktile[kb & 1];
+        const uint16_t *vs = vtile[kb & 1];
 
         // ---- S^T = K Q^T: st[t][n] holds keys 16t + 4g + r (r = 0..3) of query tile n
         f32x4 st[4][QT];
@@ -188,10 +212,11 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW > kP
             for (int s = 0; s < KSTEP; ++s) {
                 f16x8 qs_s[QT];
 #pragma unroll
-                for (int n = 0; n < QT; ++n) qs_s[n] = *reinterpret_cast<const f16x8 *>(qw + 16 * n * QS + 32 * s);
+                for (int n = 0; n < QT; ++n)
+                    qs_s[n] = *reinterpret_cast<const f16x8 *>(qs + (qrow + 16 * n) * D + 8 * pf_pos<D>(qrow + 16 * n, 4 * s + g));
 #pragma unroll
                 for (int t = 0; t < 4; ++t) {
-                    const f16x8 a = *reinterpret_cast<const f16x8 *>(ks + (16 * t + c) * KS + 32 * s + 8 * g);
+                    const f16x8 a = *reinterpret_cast<const f16x8 *>(ks + (16 * t + c) * D + 8 * pf_pos<D>(16 * t + c, 4 * s + g));
 #pragma unroll
                     for (int n = 0; n < QT; ++n)
                         st[t][n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, qs_s[n], st[t][n], 0, 0, 0);
@@ -202,7 +227,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW > kP
             for (int t = 0; t < 4; ++t)
 #pragma unroll
                 for (int s = 0; s < KSTEP; ++s) {
-                    const f16x8 a = *reinterpret_cast<const f16x8 *>(ks + (16 * t + c) * KS + 32 * s + 8 * g);
+                    const f16x8 a = *reinterpret_cast<const f16x8 *>(ks + (16 * t + c) * D + 8 * pf_pos<D>(16 * t + c, 4 * s + g));
 #pragma unroll
                     for (int n = 0; n < QT; ++n)
                         st[t][n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, qf[QLDS ? 0 : n][s], st[t][n], 0, 0, 0);
@@ -273,9 +298,9 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW > kP
         for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
             for (int t = 0; t < NDT; ++t) {
-                const uint16_t *vrow = vs + (32 * kk + 4 * g + (c >> 2)) * KS + 16 * t + 4 * (c & 3);
-                const uint2 lo = pf_read_tr16(vrow);
-                const uint2 hi = pf_read_tr16(vrow + 16 * KS);
+                const int vr0 = 32 * kk + 4 * g + (c >> 2), vch = 2 * t + ((c >> 1) & 1), vsub = 4 * (c & 1);
+                const uint2 lo = pf_read_tr16(vs + vr0 * D + 8 * pf_pos<D>(vr0, vch) + vsub);
+                const uint2 hi = pf_read_tr16(vs + (vr0 + 16) * D + 8 * pf_pos<D>(vr0 + 16, vch) + vsub);
                 const u32x4 a4 = {lo.x, lo.y, hi.x, hi.y};
                 const f16x8 a = __builtin_bit_cast(f16x8, a4);
 #pragma unroll
