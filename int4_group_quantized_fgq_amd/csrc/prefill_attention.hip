@@ -45,12 +45,24 @@ constexpr int kPfKeys = 64;   // keys per block
 constexpr float kPfSlack = 8.0f;   // log2-domain headroom of the lazy rescale
 
 // LDS tiles are unpadded row-major [rows][D] with the 16-byte chunks of a
-// row XOR-swizzled: chunk ch of row r sits at chunk position ch ^ (r % CH)
-// (CH = D / 8 chunks per row), so the fragment reads of 16 rows, the
-// 16-byte row writes and the transposing V reads spread over the banks.
+// row XOR-swizzled (CH = D / 8 chunks per row).  Q and K: chunk ch of row r
+// sits at chunk position ch ^ (r % CH), so the 16-byte fragment reads of 16
+// consecutive rows (one chunk each) hit 16 distinct positions.  V: at
+// ch ^ pf_vsw(r), so the transposing reads of half a wave (8 consecutive
+// rows, two adjacent chunks each) hit distinct banks: with 256-byte rows
+// (D = 128) an even offset 2r per row; with 128-byte rows (two rows per
+// bank cycle) 2 * (r / 2).
 template <int D>
 __device__ __forceinline__ int pf_pos(int row, int ch) {
     return ch ^ (row & (D / 8 - 1));
+}
+template <int D>
+__device__ __forceinline__ int pf_vsw(int row) {
+    return (D == 128 ? 2 * row : 2 * (row >> 1)) & (D / 8 - 1);
+}
+template <int D>
+__device__ __forceinline__ int pf_vpos(int row, int ch) {
+    return ch ^ pf_vsw<D>(row);
 }
 
 // LDS byte address of a pointer into a __shared__ array.
@@ -82,7 +94,7 @@ __device__ __forceinline__ void pf_wait_loads() {
 // rows past the prompt clamped to its last token): load instruction i fills
 // bytes [1024 i, 1024 i + 1024) of a tile, i.e. rows RPI*i .. RPI*i + RPI-1,
 // lane L taking row RPI*i + L / CH at chunk position L % CH, so it reads the
-// swizzled chunk (L % CH) ^ (row % CH).  Instructions are dealt to the
+// chunk that the tile's swizzle puts there.  Instructions are dealt to the
 // waves round-robin.
 template <int D, int NW>
 __device__ __forceinline__ void pf_issue_tile(const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
@@ -99,9 +111,9 @@ __device__ __forceinline__ void pf_issue_tile(const uint16_t *__restrict__ k, co
         const int row = RPI * i + rl;
         int j = kb * kPfKeys + row;
         j = j < S ? j : S - 1;
-        const size_t off = base + (size_t)j * rs + 8 * (pl ^ (row & (CH - 1)));
-        pf_dma16(k + off, pf_lds_addr(kt) + 1024 * i);
-        pf_dma16(v + off, pf_lds_addr(vt) + 1024 * i);
+        const size_t rowoff = base + (size_t)j * rs;
+        pf_dma16(k + rowoff + 8 * pf_pos<D>(row, pl), pf_lds_addr(kt) + 1024 * i);
+        pf_dma16(v + rowoff + 8 * pf_vpos<D>(row, pl), pf_lds_addr(vt) + 1024 * i);
     }
 }
 
@@ -299,8 +311,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW > kP
 #pragma unroll
             for (int t = 0; t < NDT; ++t) {
                 const int vr0 = 32 * kk + 4 * g + (c >> 2), vch = 2 * t + ((c >> 1) & 1), vsub = 4 * (c & 1);
-                const uint2 lo = pf_read_tr16(vs + vr0 * D + 8 * pf_pos<D>(vr0, vch) + vsub);
-                const uint2 hi = pf_read_tr16(vs + (vr0 + 16) * D + 8 * pf_pos<D>(vr0 + 16, vch) + vsub);
+                const uint2 lo = pf_read_tr16(vs + vr0 * D + 8 * pf_vpos<D>(vr0, vch) + vsub);
+                const uint2 hi = pf_read_tr16(vs + (vr0 + 16) * D + 8 * pf_vpos<D>(vr0 + 16, vch) + vsub);
                 const u32x4 a4 = {lo.x, lo.y, hi.x, hi.y};
                 const f16x8 a = __builtin_bit_cast(f16x8, a4);
 #pragma unroll
