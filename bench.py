@@ -1140,7 +1140,8 @@ def gqa_attention_line(torch, fgq, stream, steps: int, warmup: int, sweep_heads=
                                      "frac_hbm_peak": b / us / 1e3 / HBM_PEAK_GBS,
                                      "TFLOP_per_s": acc.gqa_attention_flops(B, Hq, D, cap) / us / 1e6}
         if hk == Hq:
-            # top-K (a tenth of the positions kept) over the same multi-head cache: the long-context kernel
+            # top-K (a tenth of the positions kept) over the same multi-head cache: 16416 + 1642 positions of
+            # fp32 scores and kept list fit the workgroup kernel's LDS bound (19840)
             kk = -(-cap // 10)
             tk_out = torch.empty_like(out)
             for _ in range(3):

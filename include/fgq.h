@@ -247,7 +247,7 @@ fgq_status fgq_decode_attn_gqa_q4kv(const fgq_kv_cache *kv, const void *q_f16, i
  *   (FGQ_ERR_INVALID_ARG), 1 <= kv_len <= capacity, and
  *   kv_len <= FGQ_TOPK_MAX_POSITIONS (FGQ_ERR_UNSUPPORTED: the selection
  *   state of one (sequence, head) lives in on-chip memory, 4 bytes per
- *   position while kv_len + kk <= 15360, 2.125 bytes beyond).  No workspace.
+ *   position while kv_len + kk <= 19840, 2.125 bytes beyond).  No workspace.
  */
 #define FGQ_TOPK_MAX_POSITIONS 65536
 fgq_status fgq_decode_attn_topk_q4kv(const fgq_kv_cache *kv, const void *q_f16, int32_t kv_len,

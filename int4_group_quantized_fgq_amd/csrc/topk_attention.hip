@@ -965,9 +965,13 @@ size_t attn_topk_long_lds_bytes(int32_t kv_len) {
     return (((size_t)kv_len + 1) / 2 + ((size_t)kv_len + 31) / 32) * 4;
 }
 
-// Scores and kept list in fp32 up to this many bytes of LDS (two workgroups
-// per CU); longer contexts take the 16-bit-key kernel.
-constexpr size_t kTopkF32Lds = 15360 * 4;
+// Scores and kept list in fp32 up to this many bytes of LDS: with the
+// kernel's ~2.1 KB of static LDS, two workgroups still share a CU's 160 KB
+// (kv_len + kk <= 19840 positions); longer contexts take the 16-bit-key
+// kernel.  At 16416 positions the fp32 kernel took 6-7% less time than the
+// 16-bit-key kernel for kk from 16 to 3200 (it re-reads no K rows and needs
+// no refinement).
+constexpr size_t kTopkF32Lds = 19840 * 4;
 
 // Contexts up to this length run one wavefront per (sequence, head); longer
 // ones one workgroup per (sequence, head).

@@ -263,9 +263,11 @@ def _random_case(B, H, D, L, seed):
 
 @pytest.mark.parametrize("L,D", [(14000, 128), (16416, 128), (40000, 64), (65536, 128)])
 def test_topk_long_contexts(L, D):
-    """Contexts whose fp32 scores and kept list would take more than 60 KB of
-    LDS run the 16-bit-key kernel (candidate refinement inside the cut's
-    bucket, P.V in buffered passes): 10% kept, a few, half, and everything."""
+    """Long contexts at 10% kept, a few, half, and everything: while the fp32
+    scores and kept list fit 19840 positions (77.5 KB of LDS) the fp32
+    workgroup kernel runs (above 64 KB of dynamic LDS at 14000 and 16416
+    positions), beyond that the 16-bit-key kernel (candidate refinement
+    inside the cut's bucket, P.V in buffered passes)."""
     dev, ref, q = _random_case(1, 2, D, L, L + D)
     for k in (math.ceil(L / 10), 3, L // 2):
         _topk_check(dev, ref, q, L, k, "long L=%d D=%d" % (L, D))
