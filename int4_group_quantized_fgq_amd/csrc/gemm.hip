@@ -24,9 +24,10 @@
 //    K chunk through LDS;
 //  * every operand reaches LDS through gfx950's direct global->LDS loads
 //    (global_load_lds_dword[x4], scalar base + loop-invariant lane offset,
-//    so no vector ALU work) into a ring of max(2, KP)-chunk slots (the X rows, the
-//    code words and the group metadata) as deep as the LDS allows, all but
-//    one slot in flight, one barrier per slot;
+//    so no vector ALU work) into a ring of slots of max(2, KP) chunks, twice
+//    that for k-phased workgroups where three slots still fit (the X rows,
+//    the code words and the group metadata), as deep as the LDS allows, all
+//    but one slot in flight, one barrier per slot;
 //  * packed layout: the 8 k-values of one output channel sit in one 32-bit
 //    word, in a nibble order where one AND leaves two codes in the mantissas
 //    of two fp16 subnormals (q * 2^-24 or q * 2^-20); the packed metadata
@@ -146,7 +147,12 @@ __device__ __forceinline__ int mswz(int row) { return (row >> 3) & 3; }
 // phases' accumulators are summed through LDS at the end.
 template <int MT, int KP>
 struct Cfg {
-    static constexpr int SC = KP > kSCMin ? KP : kSCMin;   // chunks per slot
+    // Chunks per slot: at least kSCMin and one per phase; doubled (two of a
+    // wave's own chunks per slot, half the barriers per chunk) for k-phased
+    // workgroups whenever the ring still holds three slots.
+    static constexpr int SC0 = KP > kSCMin ? KP : kSCMin;
+    static constexpr int slot_bytes(int sc) { return sc * MT * 1024 + kWaves * (sc / KP) * (1024 + 128); }
+    static constexpr int SC = (KP >= 2 && kLdsBudget / slot_bytes(2 * SC0) >= 3) ? 2 * SC0 : SC0;
     static constexpr int CG = kWaves / KP;             // column groups (64 channels each)
     static constexpr int LC = SC / KP;                 // chunks per wave and slot
     static constexpr int XCHUNK = MT * 1024;           // MT*16 rows x 64 bytes (one 32-k chunk)
