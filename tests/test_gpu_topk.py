@@ -301,6 +301,32 @@ def test_topk_long_context_exact_ties_span_buffers():
         gu.assert_close(got, exp, "long exact ties k=%d" % k)
 
 
+@pytest.mark.parametrize("kk", [1840, 1841])
+def test_topk_exact_ties_at_the_fp32_bound(kk):
+    """kv_len + kk = 19840 is the largest selection the fp32 workgroup kernel
+    holds (77.5 KB of dynamic LDS); one more kept position takes the
+    16-bit-key kernel.  Five distinct K rows per (sequence, head) make runs of
+    bit-identical scores at the cut; on both sides of the bound the kept
+    positions must be the oracle's (ties to the lower position)."""
+    B, H, D, L = 1, 2, 128, 18000
+    gu.note("fp32 bound L=%d kk=%d" % (L, kk))
+    rng = np.random.default_rng(kk)
+    base = rng.standard_normal((B, H, 5, D)).astype(np.float16)
+    pick = rng.integers(0, 5, (B, H, L))
+    k16 = np.take_along_axis(base, pick[..., None].repeat(D, -1), axis=2)
+    k16 = np.ascontiguousarray(k16.transpose(0, 2, 1, 3).reshape(B, L, H * D))
+    v16 = rng.standard_normal((B, L, H * D)).astype(np.float16)
+    q = rng.standard_normal((B, H * D)).astype(np.float16)
+    dev = gu.DevKV(B, H, D, L)
+    ref = oracle.KVCache(B, H, D, L)
+    dev.append(k16, v16, 0)
+    oracle.kv_append(ref, k16, v16, 0)
+    got, gsel = dev.attend_topk(q, L, kk)
+    exp, osel = oracle.decode_attn_topk(ref, q, L, kk)
+    assert np.array_equal(gsel, osel)
+    gu.assert_close(got, exp, "fp32 bound exact ties kk=%d" % kk)
+
+
 def test_topk_long_context_all_scores_equal():
     """A zero query makes every score 0: the whole context is one candidate
     bucket; the first kk positions are kept and the output is their mean V."""
