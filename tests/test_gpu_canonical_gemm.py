@@ -55,6 +55,22 @@ def test_canonical_gemm_ragged_shapes(M, K, N):
     gu.assert_close(y, oracle.dequant_gemm(X, M, 1, rc, rm), "canonical gemm %dx%dx%d" % (M, K, N))
 
 
+@pytest.mark.parametrize("M", [8, 40, 72, 104, 136])
+def test_canonical_gemm_row_tile_counts(M):
+    """Row-tile counts 1, 3, 5, 7 and 9 with several ring turns, a split plan
+    and a ragged last column block: two-phase workgroups of up to 8 m-tiles
+    take slots of two chunks per wave, 9 m-tiles one."""
+    K, N = 8192, 640
+    rng = np.random.default_rng(M + 23)
+    Wt = (rng.standard_normal((K, N)) * 0.02).astype(np.float16)
+    X = rng.standard_normal((M, K)).astype(np.float16)
+    gu.note("canonical gemm row tiles M=%d" % M)
+    codes, meta = _quantized(Wt)
+    rc, rm = oracle.quantize_g64(Wt)
+    y = gu.gemm_canonical(X, M, 1, codes, meta, K, N)
+    gu.assert_close(y, oracle.dequant_gemm(X, M, 1, rc, rm), "canonical gemm %dx%dx%d" % (M, K, N))
+
+
 def test_canonical_gemm_empty_k_is_zero():
     torch = gu.torch_cuda()
     M, N = 4, 64

@@ -335,6 +335,22 @@ def test_gemm_ragged_shapes(M, K, N):
     gu.assert_close(y, oracle.dequant_gemm(X, M, 1, rc, rm), "gemm %dx%dx%d" % (M, K, N))
 
 
+# Every row-tile count (1..9 m-tiles) with a K long enough for several ring
+# turns and a split plan: k-phased workgroups of up to 8 m-tiles take slots
+# of two of a wave's chunks where three slots fit in LDS, so this covers both
+# slot sizes, the ring's tail and a ragged last column block (N = 640).
+@pytest.mark.parametrize("M", [8, 24, 40, 56, 72, 88, 104, 120, 136])
+def test_gemm_every_row_tile_count(M):
+    K, N = 8192, 640
+    rng = np.random.default_rng(M + 11)
+    Wt = (rng.standard_normal((K, N)) * 0.02).astype(np.float16)
+    X = rng.standard_normal((M, K)).astype(np.float16)
+    gu.note("gemm row tiles M=%d K=%d N=%d" % (M, K, N))
+    rc, rm, pc, pm = _gemm_case(X, M, 1, Wt)
+    y = gu.gemm(X, M, 1, pc, pm, K, N)
+    gu.assert_close(y, oracle.dequant_gemm(X, M, 1, rc, rm), "gemm %dx%dx%d" % (M, K, N))
+
+
 @pytest.mark.parametrize("name,idx", [("tiny", 0), ("opt-6.7b", 0), ("opt-6.7b", 4), ("opt-6.7b", 5),
                                       ("opt-30b", 0)])
 def test_gemm_workload_full(name, idx):
