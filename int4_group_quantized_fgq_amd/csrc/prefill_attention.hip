@@ -15,9 +15,11 @@
 //    waves (256 rows, two waves per SIMD) for short prompts, of 12 waves
 //    (384 rows, three per SIMD) for long ones, where the Q fragments move
 //    from registers to LDS to make room for the third wave;
-//    key blocks of 64 are staged in LDS by 8 of the waves, K and V both
-//    row-major, the next block's global loads in flight while the current
-//    one is multiplied;
+//    key blocks of 64 reach LDS through gfx950's direct global->LDS loads
+//    (no registers, no LDS write instructions), dealt to all the waves, into
+//    two buffers: block kb + 1 lands in one while block kb is multiplied
+//    from the other, with one barrier per block; K and V sit row-major and
+//    unpadded, their 16-byte chunks XOR-swizzled per row;
 //  * scores are formed transposed, S^T = K Q^T, on v_mfma_f32_16x16x32_f16
 //    (A = K rows from LDS, B = the wave's Q fragments), so
 //    a lane's accumulators all belong to one query: the running max, the
@@ -145,7 +147,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW > kP
     constexpr bool QLDS = NW > kPfQRegWaves;
     // Q rows (QLDS), and two K and two V tiles: key block kb is multiplied
     // from buffer kb % 2 while block kb + 1 loads into the other; all
-    // unpadded with swizzled chunks (pf_pos)
+    // unpadded with swizzled chunks (pf_pos for Q and K, pf_vpos for V)
     __shared__ __attribute__((aligned(1024))) uint16_t ktile[2][kPfKeys * D];
     __shared__ __attribute__((aligned(1024))) uint16_t vtile[2][kPfKeys * D];
     __shared__ __attribute__((aligned(16))) uint16_t qs[QLDS ? ROWS * D : 8];
