@@ -11,7 +11,11 @@
 // Design (HBM-bound: 1.125 bytes per cached hidden element, ~4 flops):
 //  * One wavefront owns one (b, h, split) work item; the sequence is split
 //    into n_split ranges when b*h alone would not fill the 256 CUs, and the
-//    partial softmax states (m, l, o) are merged by a second kernel.
+//    partial softmax states (m, l, o) are merged by a second kernel.  Long
+//    sequences with fewer pairs than that give each item the four waves of a
+//    workgroup instead: wave w takes every fourth chunk from chunk w, and the
+//    four softmax states are merged in LDS, in wave order (fewer splits, so
+//    fewer or no merge launches, and every wave still streams a long run).
 //  * Lane = (token slot, part): a token's 64-byte row of codes (head_dim 128)
 //    is read by 4 lanes with one 16-byte load each, so a wave streams 16
 //    tokens per load instruction, fully coalesced.
@@ -91,7 +95,9 @@ __device__ __forceinline__ uint4 stream_load16(const uint8_t *p) {
 // D = head_dim (64 or 128); CH = token iterations per chunk (even).  Short
 // chunks leave registers for four waves per SIMD (many short sequences);
 // long chunks keep more bytes in flight per wave at two (long sequences).
-template <int D, int CH>
+// WPI = waves per work item: 1 (four items per workgroup) or 4 (one item per
+// workgroup, its chunks dealt to the waves round-robin).
+template <int D, int CH, int WPI>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(CH <= 2 ? 4 : (CH >= 6 ? 2 : 3))))
 void attn_split_kernel(
     const uint8_t *__restrict__ kc, const uint32_t *__restrict__ km, const uint8_t *__restrict__ vc,
@@ -103,12 +109,17 @@ void attn_split_kernel(
     constexpr int G = D / 64;       // groups per token row
     constexpr int EPL = 32 / TPI;   // output elements per lane in the final reduction
     static_assert(CH % 2 == 0, "P.V pairs token iteration it with it + CH/2");
+    static_assert(WPI == 1 || WPI == 4, "one item per wave or per workgroup");
     __shared__ float red[4][64 * 33];
+    __shared__ float mrg_o[WPI][D];         // WPI > 1: the waves' partial states
+    __shared__ float mrg_m[WPI], mrg_l[WPI];
 
     const int lane = threadIdx.x & 63;
     const int wv = threadIdx.x >> 6;
-    const int item = blockIdx.x * 4 + wv;
-    if (item >= total_items) return;   // wave-uniform
+    const int item = WPI > 1 ? (int)blockIdx.x : (int)blockIdx.x * 4 + wv;
+    const int sub = WPI > 1 ? wv : 0;       // this wave's share of the item
+    // wave-uniform; with one item per workgroup the grid is exactly the items
+    if (WPI == 1 && item >= total_items) return;
 
     const int split = item % n_split;
     const int bh = item / n_split;
@@ -256,30 +267,32 @@ void attn_split_kernel(
         }
     };
 
-    // Two register buffers: the loads of the next chunk are in flight while
-    // the current one is processed.
+    // Two register buffers: the loads of the wave's next chunk are in flight
+    // while the current one is processed.  A chunk with a next one is whole
+    // (body); the wave's last chunk may reach past the end (tail).
     constexpr int STEP = CH * TPI;
+    constexpr int STRIDE = WPI * STEP;   // the waves of an item take every WPI-th chunk
     Chunk bufA, bufB;
-    int c0 = j0;
+    int c0 = j0 + sub * STEP;
     if (c0 < j1) load(c0, bufA);
     const std::true_type tail;
     const std::false_type body;
     while (c0 < j1) {
-        if (c0 + STEP < j1) {
-            load(c0 + STEP, bufB);
+        if (c0 + STRIDE < j1) {
+            load(c0 + STRIDE, bufB);
             process(c0, bufA, body);
         } else {
             process(c0, bufA, tail);
         }
-        c0 += STEP;
+        c0 += STRIDE;
         if (c0 >= j1) break;
-        if (c0 + STEP < j1) {
-            load(c0 + STEP, bufA);
+        if (c0 + STRIDE < j1) {
+            load(c0 + STRIDE, bufA);
             process(c0, bufB, body);
         } else {
             process(c0, bufB, tail);
         }
-        c0 += STEP;
+        c0 += STRIDE;
     }
 
     // ---- reduce the token slots: o (per element) through LDS, l and macc by shuffles
@@ -300,8 +313,40 @@ void attn_split_kernel(
         val[k] = acc * ((e & 1) ? 1048576.0f : 16777216.0f) + m_tot;
     }
     const int d0 = part * 32 + slot * EPL;
+    float m_out = m_run, l_out = l_tot;
+    if constexpr (WPI > 1) {
+        // merge the waves' states in wave order: m = max m_w, each wave's o
+        // and l scaled by 2^(m_w - m); a wave that took no chunk has
+        // m_w = -inf and o = l = 0, and adds nothing
+#pragma unroll
+        for (int k = 0; k < EPL; ++k) mrg_o[sub][d0 + k] = val[k];
+        if (lane == 0) {
+            mrg_m[sub] = m_run;
+            mrg_l[sub] = l_tot;
+        }
+        __syncthreads();
+        float mx = mrg_m[0];
+#pragma unroll
+        for (int w = 1; w < WPI; ++w) mx = fmaxf(mx, mrg_m[w]);
+        float fw[WPI];
+        l_out = 0.f;
+#pragma unroll
+        for (int w = 0; w < WPI; ++w) {
+            fw[w] = mrg_m[w] == -INFINITY ? 0.f : fast_exp2(mrg_m[w] - mx);
+            l_out += fw[w] * mrg_l[w];
+        }
+#pragma unroll
+        for (int k = 0; k < EPL; ++k) {
+            float acc = 0.f;
+#pragma unroll
+            for (int w = 0; w < WPI; ++w) acc += fw[w] * mrg_o[w][d0 + k];
+            val[k] = acc;
+        }
+        m_out = mx;
+        if (sub != 0) return;   // wave 0 writes the item's result
+    }
     if (n_split == 1) {
-        const float inv = 1.0f / l_tot;
+        const float inv = 1.0f / l_out;
         const size_t ob = ((size_t)b * H + hh) * D + d0;
 #pragma unroll
         for (int k = 0; k < EPL; ++k) {
@@ -315,8 +360,8 @@ void attn_split_kernel(
 #pragma unroll
         for (int k = 0; k < EPL; ++k) wrow[d0 + k] = val[k];
         if (lane == 0) {
-            wrow[D] = m_run;
-            wrow[D + 1] = l_tot;
+            wrow[D] = m_out;
+            wrow[D + 1] = l_out;
         }
     }
 }
@@ -352,6 +397,12 @@ __global__ __launch_bounds__(128) void attn_merge_kernel(const float *__restrict
 // mostly load masked positions past the end.
 constexpr int kChunkShort = 4, kChunkLong = 6;
 constexpr int kLongChunkTokens = 256;   // tokens per wave from which the long chunk is used
+// Sequences from this length take four waves per item when the pairs alone
+// would not give ~8 waves per SIMD (each wave then streams >= 512 tokens).
+// Measured: 32 sequences x 96 heads x 4100 positions 290 -> 277 us (no split
+// and no merge launch instead of 3 splits), 16 x 32 x 16416 203 -> 193 us;
+// at 530 positions (2048 pairs) the quarter runs were slower (32 -> 34 us).
+constexpr int kQuadWaveMinTokens = 2048;
 
 }  // namespace
 
@@ -359,29 +410,32 @@ struct AttnPlan {
     int n_split;
     int tok_per_split;
     int chunk_iters;
+    int wpi;    // waves per work item: 1 or 4
 };
 
 AttnPlan attn_plan(int32_t batch, int32_t heads, int32_t head_dim, int32_t kv_len) {
     const int tpi = 64 / (head_dim / 32);
-    const int64_t bh = (int64_t)batch * heads;
     const int64_t target_waves = 8LL * 4 * kNumCU;     // ~8 waves per SIMD in flight
     const int64_t slots = 2LL * 4 * kNumCU;            // one wave per slot at two waves per SIMD
+    const int64_t pairs = (int64_t)batch * heads;
+    const int wpi = (pairs < target_waves && kv_len >= kQuadWaveMinTokens) ? 4 : 1;
+    const int64_t bh = pairs * wpi;                    // waves per split
     int n_split = 1;
     if (bh > 0 && bh < target_waves) {
         n_split = (int)((target_waves + bh - 1) / bh);
-        // Once the pairs alone occupy every wave slot, a split pays only if each
-        // part still streams a long run (it adds a merge and a wave's setup);
-        // with fewer pairs than slots, shorter parts are worth the occupancy.
-        const int min_tok = bh >= slots ? 768 : 256;
+        // Once the waves alone occupy every wave slot, a split pays only if each
+        // wave still streams a long run (it adds a merge and a wave's setup);
+        // with fewer waves than slots, shorter runs are worth the occupancy.
+        const int min_tok = (bh >= slots ? 768 : 256) * wpi;
         const int max_split = kv_len / min_tok > 1 ? kv_len / min_tok : 1;
         if (n_split > max_split) n_split = max_split;
     }
     int per = (kv_len + n_split - 1) / n_split;
-    const int ch = per >= kLongChunkTokens ? kChunkLong : kChunkShort;
+    const int ch = per / wpi >= kLongChunkTokens ? kChunkLong : kChunkShort;   // wpi 4: always long
     const int chunk = ch * tpi;
     per = ((per + chunk - 1) / chunk) * chunk;
     n_split = (kv_len + per - 1) / per;   // drop empty splits
-    return {n_split, per, ch};
+    return {n_split, per, ch, wpi};
 }
 
 // Scratch of the allocation-free entry point: a file-scope device array, one
@@ -436,18 +490,24 @@ fgq_status launch_decode_attn(const fgq_kv_cache *kv, const void *q, int64_t ld_
     const int total = (int)total64;
     const float sl2 = scale * kLog2e;
     const int f16 = out_dtype == FGQ_DTYPE_F16;
-    const dim3 grid((unsigned)((total + 3) / 4)), block(256);
-#define FGQ_ATTN_LAUNCH(D, CH)                                                                                  \
-    attn_split_kernel<D, CH><<<grid, block, 0, stream>>>(kv->k_codes, kv->k_meta, kv->v_codes, kv->v_meta,      \
+    const dim3 grid((unsigned)(p.wpi > 1 ? total : (total + 3) / 4)), block(256);
+#define FGQ_ATTN_LAUNCH_W(D, CH, WPI)                                                                          \
+    attn_split_kernel<D, CH, WPI><<<grid, block, 0, stream>>>(kv->k_codes, kv->k_meta, kv->v_codes, kv->v_meta,      \
                                                          static_cast<const uint16_t *>(q), ld_q, kv->heads, kv->capacity, \
                                                          kv_len, p.n_split, p.tok_per_split, total, sl2,        \
                                                          static_cast<float *>(ws), out, f16)
+    // Four waves per item only come with splits of >= 4 x 256 tokens, so
+    // always with the long chunk.
     if (kv->head_dim == 128) {
-        if (p.chunk_iters == kChunkLong) FGQ_ATTN_LAUNCH(128, kChunkLong); else FGQ_ATTN_LAUNCH(128, kChunkShort);
+        if (p.wpi > 1) FGQ_ATTN_LAUNCH_W(128, kChunkLong, 4);
+        else if (p.chunk_iters == kChunkLong) FGQ_ATTN_LAUNCH_W(128, kChunkLong, 1);
+        else FGQ_ATTN_LAUNCH_W(128, kChunkShort, 1);
     } else {
-        if (p.chunk_iters == kChunkLong) FGQ_ATTN_LAUNCH(64, kChunkLong); else FGQ_ATTN_LAUNCH(64, kChunkShort);
+        if (p.wpi > 1) FGQ_ATTN_LAUNCH_W(64, kChunkLong, 4);
+        else if (p.chunk_iters == kChunkLong) FGQ_ATTN_LAUNCH_W(64, kChunkLong, 1);
+        else FGQ_ATTN_LAUNCH_W(64, kChunkShort, 1);
     }
-#undef FGQ_ATTN_LAUNCH
+#undef FGQ_ATTN_LAUNCH_W
     fgq_status s = check_launch("attn_split_kernel");
     if (s != FGQ_OK || p.n_split == 1) return s;
     const dim3 mgrid((unsigned)(kv->batch * kv->heads));

@@ -207,9 +207,10 @@ def test_attention_full_size_sampled(name, t, samples):
 
 @pytest.mark.parametrize("B,H,D,L", [(8, 256, 64, 3100), (16, 128, 128, 4100)])
 def test_attention_long_chunk_plan_sampled(B, H, D, L):
-    """2048 (sequence, head) pairs over 3-4K positions: four splits of 775-1025
-    tokens, the long-chunk launch (ragged last chunk of every split); sampled
-    sequences against the oracle on the same codes."""
+    """2048 (sequence, head) pairs over 3-4K positions: one workgroup of four
+    waves per pair (each wave takes every fourth chunk), no split, the
+    long-chunk launch with a ragged last chunk; sampled sequences against the
+    oracle on the same codes."""
     import dataclasses
     w = dataclasses.replace(W["long-t3"], g=B, m=1, heads=H, head_dim=D, prompt=L, steps=1)
     gu.note("long-chunk plan B=%d H=%d D=%d L=%d" % (B, H, D, L))
@@ -226,6 +227,59 @@ def test_attention_long_chunk_plan_sampled(B, H, D, L):
         ref = oracle.KVCache(1, H, D, L)
         oracle.kv_append(ref, synth.prompt_kv(w, "k", b0=b, nb=1), synth.prompt_kv(w, "v", b0=b, nb=1), 0)
         gu.assert_close(got[b:b + 1], oracle.decode_attn(ref, q[b:b + 1], L), "long-chunk seq %d" % b)
+
+
+def _small_long_cache(B, H, D, L):
+    import dataclasses
+    w = dataclasses.replace(W["long-t3"], g=B, m=1, heads=H, head_dim=D, prompt=L, steps=1)
+    dev = gu.DevKV(B, H, D, L)
+    ref = oracle.KVCache(B, H, D, L)
+    k = synth.prompt_kv(w, "k", nb=B)
+    v = synth.prompt_kv(w, "v", nb=B)
+    dev.append(k, v, 0)
+    oracle.kv_append(ref, k, v, 0)
+    return w, dev, ref
+
+
+@pytest.mark.parametrize("B,H,D,L,splits", [
+    (2, 3, 64, 8065, 7),      # last split: 1 token, so waves 1-3 of its items stream nothing
+    (2, 3, 128, 12673, 12),   # the same at head_dim 128
+    (1, 2, 128, 10563, 10),   # last split: 2 whole chunks + 3 tokens, wave 3 idle
+    (1, 2, 128, 2048, 2),     # the shortest sequence that takes four waves per pair
+    (3, 32, 64, 5000, 4),     # 7 chunks per split (wave 3 takes one fewer), last 5 + 8 tokens
+])
+def test_attention_four_waves_per_item(B, H, D, L, splits):
+    """Few (sequence, head) pairs over >= 2048 positions: one workgroup of four
+    waves per work item, merged in LDS, combined with a split of the sequence
+    (the split count is read back from the workspace size).  Every sequence
+    against the oracle on the same codes, and bitwise repeatable."""
+    assert gu.fgq.fgq_decode_attn_ws_bytes(B, H, D, L) == B * H * splits * (D + 4) * 4
+    gu.note("four waves per item B=%d H=%d D=%d L=%d splits=%d" % (B, H, D, L, splits))
+    w, dev, ref = _small_long_cache(B, H, D, L)
+    q = synth.step_q(w, 1)
+    got = dev.attend(q, L)
+    gu.assert_close(got, oracle.decode_attn(ref, q, L), "four-wave items")
+    assert np.array_equal(got, dev.attend(q, L))
+
+
+def test_attention_one_wave_and_four_wave_items_agree():
+    """32 x 96 pairs: at 2047 positions a pair is one wave's item (two splits
+    of 1056 and 991 tokens), at 2048 one workgroup's with no split; both
+    against the oracle on the same cache."""
+    B, H, D = 32, 96, 128
+    assert gu.fgq.fgq_decode_attn_ws_bytes(B, H, D, 2047) == B * H * 2 * (D + 4) * 4
+    assert gu.fgq.fgq_decode_attn_ws_bytes(B, H, D, 2048) == 0
+    nb = 2
+    w, dev, ref = _small_long_cache(nb, H, D, 2048)
+    q = synth.step_q(w, 1)
+    wide = gu.DevKV(B, H, D, 2048)
+    for a in ("k_codes", "k_meta", "v_codes", "v_meta"):
+        getattr(wide, a)[:nb].copy_(getattr(dev, a))
+        getattr(wide, a)[nb:].copy_(getattr(dev, a)[:1].expand(B - nb, -1, -1, -1))
+    qw = np.concatenate([q, np.repeat(q[:1], B - nb, axis=0)])
+    for L in (2047, 2048):
+        gu.note("one- vs four-wave items at L=%d" % L)
+        gu.assert_close(wide.attend(qw, L)[:nb], oracle.decode_attn(ref, q, L), "L=%d" % L)
 
 
 def test_attention_result_does_not_depend_on_batch_split_plan():

@@ -1,8 +1,9 @@
 """fgq_decode_attn_q4kv_noalloc (the allocation-free entry: split states in a
 fixed scratch array inside the library) against fgq_decode_attn_q4kv with a
-caller workspace, on two calls in a row, the second with a smaller input:
-outputs equal bit for bit (same kernels, same plan), and both within the
-attention bar of the oracle.  Runs last: a failure here hides nothing."""
+caller workspace, on calls in a row, each with a smaller input than the one
+before (the first with four waves per item): outputs equal bit for bit (same
+kernels, same plan), and each within the attention bar of the oracle.  Runs
+last: a failure here hides nothing."""
 import numpy as np
 import pytest
 
@@ -42,7 +43,9 @@ def _noalloc(dev, q, L):
 
 
 def test_noalloc_attention_two_calls_second_smaller():
-    cases = [(3, 1300, 0), (1, 600, 5)]     # the second call is smaller (fewer sequences, shorter)
+    # each call smaller than the one before; the first (>= 2048 positions, few
+    # pairs) gives each (pair, split) item the four waves of a workgroup
+    cases = [(3, 2600, 7), (3, 1300, 0), (1, 600, 5)]
     for nb, L, tag in cases:
         gu.note("noalloc attention nb=%d L=%d" % (nb, L))
         dev, ref, q = _case(nb, L, tag)
