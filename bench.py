@@ -187,6 +187,36 @@ def summarize_pmc(args):
     return fac, res
 
 
+def library_gemm_same_shapes(torch, M: int, shapes) -> dict:
+    """The library's plain fp16 GEMM (torch matmul, hipBLASLt) on the step's
+    own weight shapes with uncompressed fp16 weights: X [M][K] @ W [K][N],
+    fp16 out.  It reads 2 bytes per weight element against 0.5625 for the
+    compressed ones, so it is a same-shape yardstick, not a ceiling."""
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    out, tot_us, tot_fl = {}, 0.0, 0.0
+    for name, K, N in shapes:
+        x = torch.randn(M, K, device="cuda").half()
+        wt = (torch.randn(K, N, device="cuda") * 0.02).half()
+        for _ in range(3):
+            y = x @ wt
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(20):
+            y = x @ wt
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / 20
+        fl = 2.0 * M * K * N
+        out["%s %dx%d" % (name, K, N)] = {"us_per_launch": round(us, 1), "TFLOP_per_s": round(fl / us * 1e-6, 1),
+                                          "GB_per_s": round((2.0 * K * N + 2.0 * M * (K + N)) / us * 1e-3, 1)}
+        tot_us += us
+        tot_fl += fl
+        del x, wt, y
+    torch.cuda.empty_cache()
+    out["all"] = {"us": round(tot_us, 1), "TFLOP_per_s": round(tot_fl / tot_us * 1e-6, 1), "rows": M}
+    return out
+
+
 def measured_ceilings(torch) -> dict:
     """Achievable rates on this GPU next to the spec peaks: a 1 GiB device
     copy (HBM read + write) and a library fp16 GEMM (hipBLASLt, 8192^3)."""
@@ -1347,6 +1377,9 @@ def main():
                    "(all 96 layers, prefill included) - not comparable to this per-layer in-HBM rate",
     }
     result["measured_ceilings"] = measured_ceilings(torch)
+    if w.weights:
+        result["measured_ceilings"]["library_f16_gemm_same_shapes"] = library_gemm_same_shapes(
+            torch, B, [(p[0], p[1], p[2]) for p in launch_plan(w)])
     if not args.no_cpu_baseline and w.weights:
         t0 = time.time()
         result["cpu_baseline"] = cpu_baseline(w, args)

@@ -75,6 +75,26 @@ def test_gqa_split_plans(B, Hkv, R, L):
         _check(dev, ref, w, Lq, "split")
 
 
+@pytest.mark.parametrize("B,Hkv,R,D,L,Ls", [
+    (2, 1, 16, 64, 600, (1, 33, 255, 256, 257, 600)),   # ragged splits; waves 1..3 empty at L = 1
+    (2, 2, 12, 128, 300, (31, 224, 256, 300)),          # padding columns (12 of 16 heads)
+    (1, 1, 16, 128, 3000, (3000, 2923, 513)),           # several splits
+    (1, 3, 10, 64, 5000, (5000, 4097)),                 # head_dim 64, padding columns
+])
+def test_gqa_wide_groups_few_pairs(B, Hkv, R, D, L, Ls):
+    """9..16 query heads per K/V head with few pairs: one workgroup per
+    (sequence, K/V head, split), lengths that leave some of its waves without
+    a block, padding columns, head_dim 64, several splits; bitwise repeatable."""
+    w = _shape(W["gqa"], B, Hkv, R, D, L)
+    if L >= 3000:
+        assert gu.fgq.fgq_decode_attn_gqa_ws_bytes(B, Hkv * R, Hkv, D, L) > 0
+    dev, ref = _case(w)
+    for Lq in Ls:
+        _check(dev, ref, w, Lq, "wide group R=%d" % R)
+    q = synth.step_q(w, 1)
+    assert np.array_equal(dev.attend_gqa(q, w.heads, L), dev.attend_gqa(q, w.heads, L))
+
+
 def test_gqa_long_context_outliers_and_constant_groups():
     w = dataclasses.replace(W["long-t3"], g=2, heads=96, kv_heads=12, prompt=4096, steps=1)
     dev, ref = _case(w)
