@@ -28,9 +28,11 @@
 //    two tokens share a dot2 (a byte permute interleaves their codes) and the
 //    fp16 weight p_j*step_j is split into a high and a low fp16 part so the
 //    product keeps ~22 bits.
-//  * Scores of a 64-token chunk are formed first, the chunk max is taken over
-//    the wave, then the exponentials and the P.V pass run with that max: the
-//    running accumulators are rescaled once per chunk, not per token.
+//  * Scores of a chunk (CH token iterations of 64 / (head_dim / 32) tokens:
+//    96 tokens at head_dim 128 with CH = 6) are formed first, the chunk max is
+//    taken over the wave, then the exponentials and the P.V pass run with
+//    that max: the running accumulators are rescaled at most once per chunk,
+//    not per token.
 #include <climits>
 #include <mutex>
 #include <type_traits>
