@@ -154,9 +154,15 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW > kP
 
     const int tid = threadIdx.x, lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 4, c = lane & 15;
-    const int nqb = gridDim.x;
-    const int qb = nqb - 1 - (int)blockIdx.x;      // the longest rows first
-    const int h = blockIdx.y, b = blockIdx.z;
+    // Longest rows first across the whole launch: the workgroups are taken in
+    // dispatch order (x fastest), and that order visits the last row block of
+    // every (sequence, head) before any earlier one, so the short causal
+    // blocks fill the tail.  nqb * heads * batch < 2^26 (the entry's limits).
+    const int nqb = gridDim.x, nbh = gridDim.y * gridDim.z;
+    const int lin = (int)blockIdx.x + nqb * ((int)blockIdx.y + (int)gridDim.y * (int)blockIdx.z);
+    const int qb = nqb - 1 - lin / nbh;
+    const int bh = lin - (lin / nbh) * nbh;
+    const int h = bh % (int)gridDim.y, b = bh / (int)gridDim.y;
     const size_t rs = (size_t)H * D;               // token stride in halves
     const size_t base = (size_t)b * S * rs + (size_t)h * D;
 
