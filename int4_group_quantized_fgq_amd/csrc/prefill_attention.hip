@@ -34,6 +34,8 @@
 //    the output is rescaled only when some lane's running max moved; blocks
 //    wholly above a wave's diagonal are skipped, blocks that reach it mask
 //    j > i.
+#include <type_traits>
+
 #include "common.h"
 
 namespace fgq {
@@ -209,16 +211,20 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW > kP
     const int kb_last = q_last / kPfKeys;
     const int wave_q_last = q0 + kPfWaveRows - 1;
     pf_issue_tile<D, NW>(k, v, base, rs, S, 0, wv, lane, ktile[0], vtile[0]);
-    for (int kb = 0; kb <= kb_last; ++kb) {
+    // One key block; BUF = kb % 2 is a compile-time constant (the loop below
+    // takes blocks in pairs), so every LDS fragment address is a per-lane
+    // base fixed for the whole kernel plus an immediate offset.
+    auto key_block = [&](const int kb, auto bufc) {
+        constexpr int BUF = decltype(bufc)::value;
         // block kb has landed (this wave's loads, then every wave's), and
         // every wave is done with block kb - 1, whose buffer block kb + 1
         // now fills while block kb is multiplied
         pf_wait_loads();
         __syncthreads();
-        if (kb < kb_last) pf_issue_tile<D, NW>(k, v, base, rs, S, kb + 1, wv, lane, ktile[(kb + 1) & 1], vtile[(kb + 1) & 1]);
-        if (kb * kPfKeys > wave_q_last) continue;  // every key of the block is past this wave's queries
-        const uint16_t *ks = ktile[kb & 1];
-        const uint16_t *vs = vtile[kb & 1];
+        if (kb < kb_last) pf_issue_tile<D, NW>(k, v, base, rs, S, kb + 1, wv, lane, ktile[BUF ^ 1], vtile[BUF ^ 1]);
+        if (kb * kPfKeys > wave_q_last) return;   // every key of the block is past this wave's queries
+        const uint16_t *ks = ktile[BUF];
+        const uint16_t *vs = vtile[BUF];
 
         // ---- S^T = K Q^T: st[t][n] holds keys 16t + 4g + r (r = 0..3) of query tile n
         f32x4 st[4][QT];
@@ -327,6 +333,11 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW > kP
                 for (int n = 0; n < QT; ++n)
                     o[t][n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, pb[n][kk], o[t][n], 0, 0, 0);
             }
+    };
+    for (int kb = 0; kb <= kb_last; kb += 2) {
+        key_block(kb, std::integral_constant<int, 0>{});
+        if (kb + 1 > kb_last) break;
+        key_block(kb + 1, std::integral_constant<int, 1>{});
     }
 
     // ---- normalise and store: lane holds d = 16dt + 4g + r of query qi[n]
