@@ -94,13 +94,15 @@ __device__ __forceinline__ uint4 stream_load16(const uint8_t *p) {
     return make_uint4(v[0], v[1], v[2], v[3]);
 }
 
-// D = head_dim (64 or 128); CH = token iterations per chunk (even).  Short
-// chunks leave registers for four waves per SIMD (many short sequences);
-// long chunks keep more bytes in flight per wave at two (long sequences).
+// D = head_dim (64 or 128); CH = token iterations per chunk (even): 6 for
+// runs of at least 256 tokens per wave (more bytes in flight per wave), 4
+// for shorter ones (a deep chunk would mostly load masked positions).  Both
+// run at two waves per SIMD: at three the 4-iteration variant spilled 8 to 11
+// registers to scratch and was 4-15% slower.
 // WPI = waves per work item: 1 (four items per workgroup) or 4 (one item per
 // workgroup, its chunks dealt to the waves round-robin).
 template <int D, int CH, int WPI>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(CH <= 2 ? 4 : (CH >= 6 ? 2 : 3))))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
 void attn_split_kernel(
     const uint8_t *__restrict__ kc, const uint32_t *__restrict__ km, const uint8_t *__restrict__ vc,
     const uint32_t *__restrict__ vm, const uint16_t *__restrict__ q, int64_t ld_q, int H, int cap, int L, int n_split,
