@@ -402,11 +402,14 @@ __global__ __launch_bounds__(128) void attn_merge_kernel(const float *__restrict
 constexpr int kChunkShort = 4, kChunkLong = 6;
 constexpr int kLongChunkTokens = 256;   // tokens per wave from which the long chunk is used
 // Sequences from this length take four waves per item when the pairs alone
-// would not give ~8 waves per SIMD (each wave then streams >= 512 tokens).
-// Measured: 32 sequences x 96 heads x 4100 positions 290 -> 277 us (no split
-// and no merge launch instead of 3 splits), 16 x 32 x 16416 203 -> 193 us;
-// at 530 positions (2048 pairs) the quarter runs were slower (32 -> 34 us).
-constexpr int kQuadWaveMinTokens = 2048;
+// would not give ~8 waves per SIMD.  Each wave then streams >= 256 tokens (a
+// split is never shorter than 4 x 256 tokens), so these items always take
+// the long chunk.  Measured: 32 sequences x 96 heads x 4100 positions
+// 290 -> 277 us (no split and no merge launch instead of 3 splits),
+// 16 x 32 x 16416 203 -> 193 us, 96 x 56 x 1040 138 -> 125 us (a finer last
+// round of waves); at 530 positions (2048 pairs) the quarter runs were
+// slower (32 -> 34 us).
+constexpr int kQuadWaveMinTokens = 1024;
 
 }  // namespace
 

@@ -109,14 +109,15 @@ def test_attention_validation_and_workspace(lib):
     assert fgq.fgq_decode_attn_ws_bytes(0, 96, 128, 544) == 0
     # the split rule: once the waves cover every wave slot (2048 on 256 CUs at
     # two waves per SIMD), a sequence is split only into parts of >= 768
-    # tokens per wave; with fewer waves, >= 256 tokens per wave.  From 2048
+    # tokens per wave; with fewer waves, >= 256 tokens per wave.  From 1024
     # positions, fewer than 8192 pairs take four waves per pair (one
     # workgroup), which counts four times towards the 8192-wave target.
     ws = lambda B, H, L, n: B * H * n * (128 + 4) * 4
     assert fgq.fgq_decode_attn_ws_bytes(64, 32, 128, 530) == 0               # 2048 pairs: none
     assert fgq.fgq_decode_attn_ws_bytes(60, 32, 128, 530) == ws(60, 32, 530, 2)
-    assert fgq.fgq_decode_attn_ws_bytes(32, 96, 128, 2047) == ws(32, 96, 2047, 2)
-    assert fgq.fgq_decode_attn_ws_bytes(32, 96, 128, 2048) == 0              # 3072 pairs x 4 waves
+    assert fgq.fgq_decode_attn_ws_bytes(8, 32, 128, 1023) == ws(8, 32, 1023, 3)  # one wave per item
+    assert fgq.fgq_decode_attn_ws_bytes(8, 32, 128, 1024) == 0               # 256 pairs x 4 waves, one split
+    assert fgq.fgq_decode_attn_ws_bytes(32, 96, 128, 2047) == 0              # 3072 pairs x 4 waves
     assert fgq.fgq_decode_attn_ws_bytes(32, 96, 128, 4128) == 0
     assert fgq.fgq_decode_attn_ws_bytes(16, 32, 128, 16416) == ws(16, 32, 16416, 4)  # 512 x 4 waves x 4
     assert fgq.fgq_decode_attn_ws_bytes(96, 56, 128, 1040) == 0              # 5376 pairs, 1040 tokens

@@ -245,7 +245,8 @@ def _small_long_cache(B, H, D, L):
     (2, 3, 64, 8065, 7),      # last split: 1 token, so waves 1-3 of its items stream nothing
     (2, 3, 128, 12673, 12),   # the same at head_dim 128
     (1, 2, 128, 10563, 10),   # last split: 2 whole chunks + 3 tokens, wave 3 idle
-    (1, 2, 128, 2048, 2),     # the shortest sequence that takes four waves per pair
+    (1, 2, 128, 1024, 1),     # the shortest sequence that takes four waves per pair: no split
+    (1, 2, 128, 2048, 2),     # two splits of 1056 and 992 positions
     (3, 32, 64, 5000, 4),     # 7 chunks per split (wave 3 takes one fewer), last 5 + 8 tokens
 ])
 def test_attention_four_waves_per_item(B, H, D, L, splits):
@@ -253,7 +254,7 @@ def test_attention_four_waves_per_item(B, H, D, L, splits):
     waves per work item, merged in LDS, combined with a split of the sequence
     (the split count is read back from the workspace size).  Every sequence
     against the oracle on the same codes, and bitwise repeatable."""
-    assert gu.fgq.fgq_decode_attn_ws_bytes(B, H, D, L) == B * H * splits * (D + 4) * 4
+    assert gu.fgq.fgq_decode_attn_ws_bytes(B, H, D, L) == (B * H * splits * (D + 4) * 4 if splits > 1 else 0)
     gu.note("four waves per item B=%d H=%d D=%d L=%d splits=%d" % (B, H, D, L, splits))
     w, dev, ref = _small_long_cache(B, H, D, L)
     q = synth.step_q(w, 1)
@@ -263,21 +264,21 @@ def test_attention_four_waves_per_item(B, H, D, L, splits):
 
 
 def test_attention_one_wave_and_four_wave_items_agree():
-    """32 x 96 pairs: at 2047 positions a pair is one wave's item (two splits
-    of 1056 and 991 tokens), at 2048 one workgroup's with no split; both
+    """8 x 32 pairs: at 1023 positions a pair is one wave's item (three splits
+    of 384, 384 and 255 tokens), at 1024 one workgroup's with no split; both
     against the oracle on the same cache."""
-    B, H, D = 32, 96, 128
-    assert gu.fgq.fgq_decode_attn_ws_bytes(B, H, D, 2047) == B * H * 2 * (D + 4) * 4
-    assert gu.fgq.fgq_decode_attn_ws_bytes(B, H, D, 2048) == 0
+    B, H, D = 8, 32, 128
+    assert gu.fgq.fgq_decode_attn_ws_bytes(B, H, D, 1023) == B * H * 3 * (D + 4) * 4
+    assert gu.fgq.fgq_decode_attn_ws_bytes(B, H, D, 1024) == 0
     nb = 2
-    w, dev, ref = _small_long_cache(nb, H, D, 2048)
+    w, dev, ref = _small_long_cache(nb, H, D, 1024)
     q = synth.step_q(w, 1)
-    wide = gu.DevKV(B, H, D, 2048)
+    wide = gu.DevKV(B, H, D, 1024)
     for a in ("k_codes", "k_meta", "v_codes", "v_meta"):
         getattr(wide, a)[:nb].copy_(getattr(dev, a))
         getattr(wide, a)[nb:].copy_(getattr(dev, a)[:1].expand(B - nb, -1, -1, -1))
     qw = np.concatenate([q, np.repeat(q[:1], B - nb, axis=0)])
-    for L in (2047, 2048):
+    for L in (1023, 1024):
         gu.note("one- vs four-wave items at L=%d" % L)
         gu.assert_close(wide.attend(qw, L)[:nb], oracle.decode_attn(ref, q, L), "L=%d" % L)
 

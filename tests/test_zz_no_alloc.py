@@ -43,13 +43,14 @@ def _noalloc(dev, q, L):
 
 
 def test_noalloc_attention_two_calls_second_smaller():
-    # each call smaller than the one before; the first (>= 2048 positions, few
-    # pairs) gives each (pair, split) item the four waves of a workgroup
-    cases = [(3, 2600, 7), (3, 1300, 0), (1, 600, 5)]
+    # each call smaller than the one before; the first (>= 1024 positions, few
+    # pairs) gives each (pair, split) item the four waves of a workgroup, the
+    # others one wave per item
+    cases = [(3, 2600, 7), (3, 1000, 0), (1, 600, 5)]
     for nb, L, tag in cases:
         gu.note("noalloc attention nb=%d L=%d" % (nb, L))
         dev, ref, q = _case(nb, L, tag)
-        # both plans split the sequence, so the scratch really holds split states
+        # every plan splits the sequence, so the scratch really holds split states
         assert gu.fgq.fgq_decode_attn_ws_bytes(nb, dev.heads, dev.head_dim, L) > 0
         got = _noalloc(dev, q, L)
         exp_ws = dev.attend(q, L)
