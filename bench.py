@@ -793,17 +793,16 @@ def topk_line(torch, fgq, w, ch, stream, steps, warmup) -> dict:
         fgq.fgq_decode_attn_topk_q4kv(ch.caches[i % ch.R][1], qs[t - 1], L_t, -(-L_t // 10), 0.0, tk_out,
                                       fgq.FGQ_DTYPE_F32, None, sh)
 
-    for i in range(min(warmup, 8)):
-        launch(i)
+    nw, _ = warm_up(torch, launch, 0, min(warmup, 8), 100.0)   # >= 100 ms: the clock of a short burst runs lower
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     torch.cuda.synchronize()
     for i in range(steps):
         ev[i][0].record(stream)
-        launch(min(warmup, 8) + i)
+        launch(nw + i)
         ev[i][1].record(stream)
     torch.cuda.synchronize()
     ms = sum(a.elapsed_time(b) for a, b in ev)
-    ts = [(min(warmup, 8) + i) % w.steps + 1 for i in range(steps)]
+    ts = [(nw + i) % w.steps + 1 for i in range(steps)]
     by = sum(acc.topk_attention_bytes(B, h, w.kv_len(t), -(-w.kv_len(t) // 10)) for t in ts)
     line = {"kept": "ceil(kv_len/10)", "us_per_launch": 1e3 * ms / steps, "GB_per_s": by / (ms * 1e-3) / 1e9,
             "frac_hbm_peak": by / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
@@ -1139,15 +1138,16 @@ def gqa_attention_line(torch, fgq, stream, steps: int, warmup: int, sweep_heads=
         if ev is not None:
             ev[1].record(stream)
 
-    for i in range(warmup):
-        step(i)
+    # at least `warmup` steps and 100 ms of them, as for the sweep below: the
+    # clock of a short burst runs lower
+    nw, _ = warm_up(torch, step, 0, warmup, 100.0)
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     torch.cuda.synchronize()
     for i in range(steps):
-        step(warmup + i, evs[i])
+        step(nw + i, evs[i])
     torch.cuda.synchronize()
     ms = sum(a.elapsed_time(b) for a, b in evs)
-    ts = [(warmup + i) % w.steps + 1 for i in range(steps)]
+    ts = [(nw + i) % w.steps + 1 for i in range(steps)]
     byts = sum(acc.gqa_attention_bytes(B, Hq, Hkv, D, w.kv_len(t)) for t in ts)
     fl = sum(acc.gqa_attention_flops(B, Hq, D, w.kv_len(t)) for t in ts)
     line = {"workload": "gqa: %d sequences, %d query heads over %d K/V heads x %d, prompt %d + %d decode steps"
