@@ -40,7 +40,10 @@ def _gpu(q, k, v, H, scale=0.0, out_f16=False):
 
 @pytest.mark.parametrize("B,s,H,D", [(1, 1, 1, 64), (2, 37, 3, 64), (2, 64, 2, 128), (1, 65, 2, 128),
                                      (2, 200, 3, 128), (1, 513, 2, 128), (3, 130, 4, 64),
-                                     (1, 1024, 1, 64), (1, 1100, 2, 128)])
+                                     (1, 1024, 1, 64), (1, 1100, 2, 128),
+                                     # several sequences, heads and row blocks in one launch: the
+                                     # flattened longest-rows-first workgroup order, both launches
+                                     (2, 600, 3, 128), (2, 1100, 3, 64)])
 def test_prefill_against_oracle(B, s, H, D):
     q, k, v = _qkv(B, s, H, D, 0)
     gu.note("prefill B=%d s=%d H=%d D=%d" % (B, s, H, D))
