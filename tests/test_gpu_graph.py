@@ -185,3 +185,84 @@ def test_graph_gqa_step_replays_match_eager(B2, Hkv, R, L):
     h_e, h_g = kv_e.host(), kv_g.host()
     for a in h_e:
         assert np.array_equal(h_e[a], h_g[a]), a
+
+
+def test_graph_chained_step_replays_match_eager():
+    """The chained layer step (the one the bench replays): the Q|K|V product
+    feeds the append (K and V read at a row stride) and the attention (q at
+    a row stride), attention feeds Wout, Wout feeds W1 and W1 feeds W2, every
+    hand-off in fp16.  Each decode step is captured as one graph and replayed
+    three times with eager work in between: every replay equals the eager
+    step bit for bit, so no launch of the graph runs ahead of one it reads."""
+    gu.torch_cuda()
+    gu.note("graph chained step: setup")
+    weights = []
+    for i, (_, K, N) in enumerate(GEMMS):
+        codes, meta = gu.quantize(_f16(160 + i, K * N, 0.02).reshape(K, N))
+        weights.append(gu.pack(gu.to_dev(codes), gu.to_dev(meta), K, N))
+    pk = _f16(101, B * PROMPT * HID).reshape(B, PROMPT, HID)
+    pv = _f16(102, B * PROMPT * HID).reshape(B, PROMPT, HID)
+    eager_kv, graph_kv = _kv_with_prompt(pk, pv), _kv_with_prompt(pk, pv)
+    f16 = gu.fgq.FGQ_DTYPE_F16
+    x0 = [gu.to_dev(_f16(120 + t, B * HID).reshape(B, HID)) for t in range(1, STEPS + 1)]
+    qkv = torch.empty((B, 3 * HID), dtype=torch.float16, device="cuda")
+    attn = torch.empty((B, HID), dtype=torch.float16, device="cuda")
+    ys = [torch.empty((B, N), dtype=torch.float16, device="cuda") for _, _, N in GEMMS[1:]]
+    attn_wsb = max(gu.fgq.fgq_decode_attn_ws_bytes(B, H, D, PROMPT + t) for t in range(1, STEPS + 1))
+    gemm_wsb = max(gu.fgq.fgq_dequant_gemm_ws_bytes(B, K, N) for _, K, N in GEMMS)
+    assert attn_wsb > 0 and gemm_wsb > 0     # the split merge and a split-K reduction are in the graph
+    attn_ws = torch.empty(attn_wsb, dtype=torch.uint8, device="cuda")
+    gemm_ws = torch.empty(gemm_wsb, dtype=torch.uint8, device="cuda")
+
+    def enqueue(kv, t):
+        s = torch.cuda.current_stream().cuda_stream
+        gemm = gu.fgq.fgq_dequant_gemm_packed
+
+        def mm(i, x, y):
+            _, K, N = GEMMS[i]
+            gemm(x, G, MB, K, N, weights[i][0], weights[i][1], y, f16, gemm_ws, gemm_ws.numel(), s)
+
+        mm(0, x0[t - 1], qkv)
+        gu.fgq.fgq_kv_append_ld(kv.struct, qkv[:, HID:2 * HID], qkv[:, 2 * HID:], 3 * HID, PROMPT + t - 1, 1, s)
+        gu.fgq.fgq_decode_attn_q4kv_ld(kv.struct, qkv[:, :HID], 3 * HID, PROMPT + t, 0.0, attn, f16, attn_ws,
+                                       attn_ws.numel(), s)
+        mm(1, attn, ys[0])
+        mm(2, ys[0], ys[1])
+        mm(3, ys[1], ys[2])
+
+    def outputs():
+        return [gu.to_host(a) for a in [qkv, attn] + ys]
+
+    gu.note("graph chained step: eager pass")
+    eager = []
+    for t in range(1, STEPS + 1):
+        enqueue(eager_kv, t)
+        torch.cuda.synchronize()
+        eager.append(outputs())
+    eager_cache = eager_kv.host()
+    assert all(np.all(np.isfinite(a.astype(np.float32))) for a in eager[-1])
+
+    gu.note("graph chained step: capture %d graphs" % STEPS)
+    graphs = []
+    for t in range(1, STEPS + 1):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            enqueue(graph_kv, t)
+        graphs.append(g)
+    torch.cuda.synchronize()
+
+    for rep in range(3):
+        gu.note("graph chained step: replay round %d" % rep)
+        for i, g in enumerate(graphs):
+            for a in [qkv, attn] + ys:
+                a.fill_(float("nan"))        # a replay must rewrite every output
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            for j, (a, b) in enumerate(zip(outputs(), eager[i])):
+                assert np.array_equal(a.view(np.uint16), b.view(np.uint16)), ("replay", rep, "step", i + 1, "output", j)
+            enqueue(eager_kv, 1)             # eager work on the same stream between replays
+            torch.cuda.synchronize()
+        h = graph_kv.host()
+        for a in h:
+            assert np.array_equal(h[a], eager_cache[a]), ("cache", a, rep)
