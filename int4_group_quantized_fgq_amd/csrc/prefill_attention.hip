@@ -199,11 +199,17 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW > kP
     for (int t = 0; t < NDT; ++t)
 #pragma unroll
         for (int n = 0; n < QT; ++n) o[t][n] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float m_run[QT], l_run[QT];
+    float m_run[QT];
+    // Row sums of P on the matrix cores: an all-ones A operand times the same
+    // P^T fragments as P.V, so every row of lsum[n] holds the sum over keys of
+    // query tile n's column (the fp16 probabilities that P.V also uses).
+    f32x4 lsum[QT];
+    const f16x8 ones = {(_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f,
+                        (_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f};
 #pragma unroll
     for (int n = 0; n < QT; ++n) {
         m_run[n] = -INFINITY;
-        l_run[n] = 0.f;
+        lsum[n] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 
     // key blocks holding a key <= the workgroup's last query (and < S)
@@ -293,9 +299,10 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW > kP
             moved |= up;
             m_run[n] = m_new;
             msc[n] = m_new * sl2;
-            l_run[n] *= corr[n];
         }
         if (__ballot(moved)) {
+#pragma unroll
+            for (int n = 0; n < QT; ++n) lsum[n] *= corr[n];
 #pragma unroll
             for (int t = 0; t < NDT; ++t)
 #pragma unroll
@@ -312,7 +319,6 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW > kP
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
                     const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(st[2 * kk + (e >> 2)][n][e & 3], sl2, -msc[n]));
-                    l_run[n] += pv;
                     pb[n][kk][e] = (_Float16)pv;
                 }
         // ---- O^T += V^T P^T: row d = 16dt + c of V^T, keys in the same
@@ -333,6 +339,11 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW > kP
                 for (int n = 0; n < QT; ++n)
                     o[t][n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, pb[n][kk], o[t][n], 0, 0, 0);
             }
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+            for (int n = 0; n < QT; ++n)
+                lsum[n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, pb[n][kk], lsum[n], 0, 0, 0);
     };
     for (int kb = 0; kb <= kb_last; kb += 2) {
         key_block(kb, std::integral_constant<int, 0>{});
@@ -343,9 +354,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW > kP
     // ---- normalise and store: lane holds d = 16dt + 4g + r of query qi[n]
 #pragma unroll
     for (int n = 0; n < QT; ++n) {
-        float l = l_run[n];
-        l += __shfl_xor(l, 16, 64);
-        l += __shfl_xor(l, 32, 64);
+        const float l = lsum[n][0];   // every row of the tile holds the column's sum
         if (qi[n] >= S) continue;
         const float inv = 1.0f / l;
         const size_t ob = base + (size_t)qi[n] * rs + 4 * g;
