@@ -24,7 +24,8 @@
 //    (A = K rows from LDS, B = the wave's Q fragments), so
 //    a lane's accumulators all belong to one query: the running max, the
 //    rescale of the output and the exponentials stay in the lane, with two
-//    cross-lane steps for the row max and one pair at the end for the sum;
+//    cross-lane steps for the row max; the row sums of P come from the matrix
+//    cores too (an all-ones A operand times the same P^T fragments);
 //  * P.V is formed transposed too, O^T = V^T P^T, with P^T taken straight
 //    from the score accumulators: the 32 k-slots of an MFMA are mapped to
 //    keys in the order the accumulators hold them, and the V^T fragments
@@ -33,7 +34,10 @@
 //  * online softmax in the log2 domain (exp2 on the transcendental unit);
 //    the output is rescaled only when some lane's running max moved; blocks
 //    wholly above a wave's diagonal are skipped, blocks that reach it mask
-//    j > i.
+//    j > i;
+//  * the causal row blocks differ in length, so the workgroups are numbered
+//    to dispatch the last (longest) row block of every (b, h) first, and the
+//    short ones fill the tail of the launch.
 #include <type_traits>
 
 #include "common.h"
