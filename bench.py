@@ -1222,7 +1222,8 @@ def main():
     if args.summarize_counters:
         summarize_counters(args.summarize_counters, ("dq_gemm_kernel", "attn_split_kernel", "attn_merge_kernel",
                                                      "kv_append_kernel", "splitk_reduce_kernel",
-                                                     "prefill_attn_kernel"))
+                                                     "prefill_attn_kernel", "attn_gqa_kernel",
+                                                     "attn_gqa_merge_kernel"))
         return
     if args.summarize_pmc:
         w = synth.WORKLOADS[args.config]

@@ -118,7 +118,8 @@ __attribute__((amdgpu_waves_per_eu(NT == 1 ? FGQ_GQA_WAVES_PER_EU : 1))) void at
     __shared__ float s_o[kGqWaves * NDT * NT * 4][64];
     __shared__ float s_m[kGqWaves][NT][16], s_l[kGqWaves][NT][16], s_mc[kGqWaves][G][NT][16];
     __shared__ __attribute__((aligned(16))) uint8_t s_v[kGqWaves][kGqBlock * VS];
-    __shared__ __attribute__((aligned(16))) uint32_t s_meta[kGqWaves][2][kGqBlock * G];
+    // the block's metadata converted once, as fp32 pairs: K {step * c2, min}, V {step, min}
+    __shared__ __attribute__((aligned(16))) float2 s_meta[kGqWaves][2][kGqBlock * G];
 
     const int lane = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
@@ -167,6 +168,11 @@ __attribute__((amdgpu_waves_per_eu(NT == 1 ? FGQ_GQA_WAVES_PER_EU : 1))) void at
         }
     }
     const float c2 = sl2 * 16777216.0f;   // log2-domain scale times 2^24
+    float qsc[G][NT];                     // the query sums in the scores' scale
+#pragma unroll
+    for (int grp = 0; grp < G; ++grp)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) qsc[grp][nt] = qs[grp][nt] * c2;
 
     // (sequence, kv head) bases; offsets inside one head's rows fit in 32 bits
     const size_t rowbase = (size_t)bk * cap;
@@ -208,7 +214,7 @@ __attribute__((amdgpu_waves_per_eu(NT == 1 ? FGQ_GQA_WAVES_PER_EU : 1))) void at
     }
 
     uint8_t *sv = s_v[wv];
-    uint32_t *smk = s_meta[wv][0], *smv = s_meta[wv][1];
+    const float2 *smk = s_meta[wv][0], *smv = s_meta[wv][1];
 
     // TAIL: the block reaches past the end of the split (the last one)
     auto process = [&](int jb, const GqBlock<G> &d, auto tail) {
@@ -223,7 +229,10 @@ __attribute__((amdgpu_waves_per_eu(NT == 1 ? FGQ_GQA_WAVES_PER_EU : 1))) void at
             *reinterpret_cast<u32x2 *>(dst + 8) = u32x2{d.vr[i][2], d.vr[i][3]};
         }
 #pragma unroll
-        for (int grp = 0; grp < G; ++grp) s_meta[wv][lane >> 5][(lane & 31) * G + grp] = d.mt[grp];
+        for (int grp = 0; grp < G; ++grp) {
+            const float step = hi_f(d.mt[grp]);
+            s_meta[wv][lane >> 5][(lane & 31) * G + grp] = make_float2(lane < 32 ? step * c2 : step, lo_f(d.mt[grp]));
+        }
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -244,11 +253,11 @@ __attribute__((amdgpu_waves_per_eu(NT == 1 ? FGQ_GQA_WAVES_PER_EU : 1))) void at
                 }
             }
         // ---- the lane's meta (tokens 16t + 4g + r) and V codes from the stage
-        uint32_t kmw[2][4][G], vmw[2][4][G];
+        float2 kmw[2][4][G], vmw[2][4][G];
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
-            const uint32_t *pk = smk + (16 * t + 4 * g) * G;
-            const uint32_t *pv = smv + (16 * t + 4 * g) * G;
+            const float2 *pk = smk + (16 * t + 4 * g) * G;
+            const float2 *pv = smv + (16 * t + 4 * g) * G;
 #pragma unroll
             for (int r = 0; r < 4; ++r)
 #pragma unroll
@@ -282,11 +291,11 @@ __attribute__((amdgpu_waves_per_eu(NT == 1 ? FGQ_GQA_WAVES_PER_EU : 1))) void at
                     float v = 0.f;
 #pragma unroll
                     for (int grp = 0; grp < G; ++grp) {
-                        const uint32_t mw = kmw[t][r][grp];
-                        v = __builtin_fmaf(hi_f(mw), acc[t][grp][nt][r], v);
-                        v = __builtin_fmaf(lo_f(mw), qs[grp][nt], v);
+                        const float2 mw = kmw[t][r][grp];
+                        v = __builtin_fmaf(mw.x, acc[t][grp][nt][r], v);
+                        v = __builtin_fmaf(mw.y, qsc[grp][nt], v);
                     }
-                    s[nt][t][r] = v * c2;
+                    s[nt][t][r] = v;
                     if (TAIL && jb + 16 * t + 4 * g + r >= j1) s[nt][t][r] = -INFINITY;
                 }
         // ---- running max per head column: the block max over the lane's 8
@@ -327,9 +336,9 @@ __attribute__((amdgpu_waves_per_eu(NT == 1 ? FGQ_GQA_WAVES_PER_EU : 1))) void at
                     l_run[nt] += p;
 #pragma unroll
                     for (int grp = 0; grp < G; ++grp) {
-                        const uint32_t mw = vmw[t][r][grp];
-                        mc[grp][nt] = __builtin_fmaf(p, lo_f(mw), mc[grp][nt]);
-                        wb[grp][nt][4 * t + r] = (_Float16)__builtin_fmaf(p, hi_f(mw), 0.0f);
+                        const float2 mw = vmw[t][r][grp];
+                        mc[grp][nt] = __builtin_fmaf(p, mw.y, mc[grp][nt]);
+                        wb[grp][nt][4 * t + r] = (_Float16)(p * mw.x);
                     }
                 }
         // ---- O^T += V^T W^T: tile n = 4 grp + qn holds d = 64 grp + 4 row + qn;
