@@ -265,7 +265,8 @@ fgq_status fgq_decode_attn_topk_q4kv(const fgq_kv_cache *kv, const void *q_f16, 
  *   q, k, v fp16 [batch][seq][heads*head_dim] (token-major, as the QKV
  *   projection emits them); out [batch][seq][heads*head_dim] in out_dtype.
  *   softmax_scale <= 0 selects 1/sqrt(head_dim).  head_dim 64 or 128;
- *   batch, heads <= 65535 (FGQ_ERR_SHAPE).  Fp16 matrix cores with fp32
+ *   batch, heads <= 65535 and batch*heads*ceil(seq/128) < 2^31
+ *   (FGQ_ERR_SHAPE).  Fp16 matrix cores with fp32
  *   accumulation; the probabilities enter P.V rounded to fp16.  No workspace.
  */
 fgq_status fgq_prefill_attn_f16(const void *q_f16, const void *k_f16, const void *v_f16, int32_t batch,

@@ -311,6 +311,10 @@ fgq_status fgq_prefill_attn_f16(const void *q_f16, const void *k_f16, const void
     if (batch > 65535 || heads > 65535) return fail(FGQ_ERR_SHAPE, "batch and heads must be <= 65535");
     if ((double)batch * seq * heads * head_dim > (double)((int64_t)1 << 40))
         return fail(FGQ_ERR_SHAPE, "q/k/v larger than 2^40 elements");
+    // the kernel numbers its workgroups (row blocks of at least 128 tokens x
+    // heads x batch) in 32-bit ints
+    if ((int64_t)batch * heads * ((seq + 127) / 128) > INT32_MAX)
+        return fail(FGQ_ERR_SHAPE, "batch * heads * ceil(seq / 128) must be < 2^31");
     if (batch == 0 || seq == 0 || heads == 0) return FGQ_OK;
     if (!q_f16 || !k_f16 || !v_f16 || !out) return fail(FGQ_ERR_INVALID_ARG, "NULL array");
     if (!aligned16(q_f16) || !aligned16(k_f16) || !aligned16(v_f16) || !aligned16(out))

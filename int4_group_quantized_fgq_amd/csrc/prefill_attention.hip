@@ -14,7 +14,10 @@
 //    every K and V fragment read from LDS feeds two MFMAs); a workgroup of 8
 //    waves (256 rows, two waves per SIMD) for short prompts, of 12 waves
 //    (384 rows, three per SIMD) for long ones, where the Q fragments move
-//    from registers to LDS to make room for the third wave;
+//    from registers to LDS to make room for the third wave; and of 4 waves
+//    (128 rows, two workgroups per CU) for prompts up to 640 tokens whose
+//    256-row blocks would leave more rows empty, or that are multiples of 256,
+//    where the shorter causal blocks also even out the waves' work;
 //    key blocks of 64 reach LDS through gfx950's direct global->LDS loads
 //    (no registers, no LDS write instructions), dealt to all the waves, into
 //    two buffers: block kb + 1 lands in one while block kb is multiplied
@@ -49,6 +52,7 @@ constexpr float kPfLog2e = 1.4426950408889634f;
 constexpr int kPfWaveRows = 32;              // query rows per wave (two 16-row MFMA tiles)
 constexpr int kPfQRegWaves = 8;              // up to this many waves per workgroup keep Q in registers
 constexpr int kPfLongPrompt = 1024;          // prompts from which 12-wave workgroups are used
+constexpr int kPfNarrowMax = 640;            // longest prompt that may take 4-wave workgroups
 constexpr int kPfKeys = 64;   // keys per block
 constexpr float kPfSlack = 8.0f;   // log2-domain headroom of the lazy rescale
 
@@ -163,7 +167,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW > kP
     // Longest rows first across the whole launch: the workgroups are taken in
     // dispatch order (x fastest), and that order visits the last row block of
     // every (sequence, head) before any earlier one, so the short causal
-    // blocks fill the tail.  nqb * heads * batch < 2^26 (the entry's limits).
+    // blocks fill the tail.  nqb * heads * batch < 2^31 (checked by the entry).
     const int nqb = gridDim.x, nbh = gridDim.y * gridDim.z;
     const int lin = (int)blockIdx.x + nqb * ((int)blockIdx.y + (int)gridDim.y * (int)blockIdx.z);
     const int qb = nqb - 1 - lin / nbh;
@@ -219,7 +223,9 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW > kP
     // key blocks holding a key <= the workgroup's last query (and < S)
     const int q_last = min(qb * ROWS + ROWS, S) - 1;
     const int kb_last = q_last / kPfKeys;
-    const int wave_q_last = q0 + kPfWaveRows - 1;
+    // a wave whose rows all lie past the prompt multiplies nothing (it still
+    // issues its share of every tile's loads and meets every barrier)
+    const int wave_q_last = q0 < S ? q0 + kPfWaveRows - 1 : -1;
     pf_issue_tile<D, NW>(k, v, base, rs, S, 0, wv, lane, ktile[0], vtile[0]);
     // One key block; BUF = kb % 2 is a compile-time constant (the loop below
     // takes blocks in pairs), so every LDS fragment address is a per-lane
@@ -387,16 +393,21 @@ fgq_status launch_prefill_attn(const void *q, const void *k, const void *v, int3
                    *vh = static_cast<const uint16_t *>(v);
     // 12-wave workgroups (384 rows, three waves per SIMD) once the prompt is
     // long enough that the last, partly filled block of rows costs little;
-    // 8 waves (256 rows, two per SIMD) below
-    const bool wide = seq >= kPfLongPrompt;
-    const int rows = (wide ? 12 : 8) * kPfWaveRows;
+    // 8 waves (256 rows, two per SIMD) below, except that prompts up to
+    // kPfNarrowMax tokens whose last 256-row block would be full or at most
+    // half full take 4 waves (128 rows, two workgroups per CU): fewer empty
+    // rows, or (multiples of 256) shorter causal blocks whose waves' work is
+    // more even; from 768 tokens the doubled K/V tile loads cost more.
+    const int tail = seq % 256;
+    const int nw = seq >= kPfLongPrompt ? 12 : (seq <= kPfNarrowMax && tail <= 128) ? 4 : 8;
+    const int rows = nw * kPfWaveRows;
     const dim3 grid((unsigned)((seq + rows - 1) / rows), (unsigned)heads, (unsigned)batch);
 #define FGQ_PF_LAUNCH(D, NW) \
     prefill_attn_kernel<D, NW><<<grid, dim3(64 * NW), 0, stream>>>(qh, kh, vh, seq, heads, sl2, out, f16)
     if (head_dim == 128) {
-        if (wide) FGQ_PF_LAUNCH(128, 12); else FGQ_PF_LAUNCH(128, 8);
+        if (nw == 12) FGQ_PF_LAUNCH(128, 12); else if (nw == 8) FGQ_PF_LAUNCH(128, 8); else FGQ_PF_LAUNCH(128, 4);
     } else {
-        if (wide) FGQ_PF_LAUNCH(64, 12); else FGQ_PF_LAUNCH(64, 8);
+        if (nw == 12) FGQ_PF_LAUNCH(64, 12); else if (nw == 8) FGQ_PF_LAUNCH(64, 8); else FGQ_PF_LAUNCH(64, 4);
     }
 #undef FGQ_PF_LAUNCH
     return check_launch("prefill_attn_kernel");

@@ -184,6 +184,8 @@ def test_prefill_attention_validation(lib):
     assert _status(lambda: p(GOOD, GOOD, GOOD, 2, 16, 2, 128, 0.0, GOOD, 5, 0)) == fgq.FGQ_ERR_DTYPE
     assert _status(lambda: p(GOOD, GOOD, GOOD, 2, 16, 2, 128, float("nan"), GOOD, 0, 0)) == fgq.FGQ_ERR_INVALID_ARG
     assert _status(lambda: p(GOOD, GOOD, GOOD, 70000, 16, 2, 128, 0.0, GOOD, 0, 0)) == fgq.FGQ_ERR_SHAPE
+    # within 2^40 elements, but 65535 x 65535 workgroups of one row block overflow the 32-bit numbering
+    assert _status(lambda: p(GOOD, GOOD, GOOD, 65535, 1, 65535, 64, 0.0, GOOD, 0, 0)) == fgq.FGQ_ERR_SHAPE
     assert _status(lambda: p(GOOD, BAD, GOOD, 2, 16, 2, 128, 0.0, GOOD, 0, 0)) == fgq.FGQ_ERR_ALIGN
     assert _status(lambda: p(GOOD, GOOD, 0, 2, 16, 2, 128, 0.0, GOOD, 0, 0)) == fgq.FGQ_ERR_INVALID_ARG
     assert _status(lambda: p(0, 0, 0, 2, 0, 2, 128, 0.0, 0, 0, 0)) == fgq.FGQ_OK     # empty prompt

@@ -43,7 +43,11 @@ def _gpu(q, k, v, H, scale=0.0, out_f16=False):
                                      (1, 1024, 1, 64), (1, 1100, 2, 128),
                                      # several sequences, heads and row blocks in one launch: the
                                      # flattened longest-rows-first workgroup order, both launches
-                                     (2, 600, 3, 128), (2, 1100, 3, 64)])
+                                     (2, 600, 3, 128), (2, 1100, 3, 64),
+                                     # 4-wave launch (prompts <= 640 whose last 256-row block is full
+                                     # or at most half full): ragged, the longest, head_dim 64;
+                                     # 8-wave launch past 640 and with a more than half full block
+                                     (2, 300, 3, 64), (1, 640, 2, 128), (1, 250, 2, 64), (2, 700, 2, 128)])
 def test_prefill_against_oracle(B, s, H, D):
     q, k, v = _qkv(B, s, H, D, 0)
     gu.note("prefill B=%d s=%d H=%d D=%d" % (B, s, H, D))
@@ -51,10 +55,11 @@ def test_prefill_against_oracle(B, s, H, D):
     gu.assert_close(got, oracle.prefill_attn(q, k, v, H), "prefill %dx%dx%dx%d" % (B, s, H, D))
 
 
-def test_prefill_fp16_output_and_scale():
-    B, s, H, D = 2, 150, 2, 128
+@pytest.mark.parametrize("s", [150, 100])   # the 8-wave and the 4-wave launch
+def test_prefill_fp16_output_and_scale(s):
+    B, H, D = 2, 2, 128
     q, k, v = _qkv(B, s, H, D, 10)
-    gu.note("prefill fp16 out / scale")
+    gu.note("prefill fp16 out / scale, s=%d" % s)
     gu.assert_close(_gpu(q, k, v, H, out_f16=True), oracle.prefill_attn(q, k, v, H), "prefill fp16 out")
     gu.assert_close(_gpu(q, k, v, H, scale=0.3), oracle.prefill_attn(q, k, v, H, scale=0.3), "prefill scale 0.3")
 
