@@ -749,7 +749,7 @@ def prefill_and_bulk_lines(torch, fgq, w, ch, stream) -> dict:
 
 def prefill_only_lines(torch, fgq, stream, reps: int) -> dict:
     """Causal prefill attention alone at OPT-175B's heads (96 x 128), on the
-    seeded prompt recipe: 8 sequences of 512 tokens (the 8-wave launch) and
+    seeded prompt recipe: 8 sequences of 512 tokens (the short-prompt launch) and
     one of 4096 (the long-prompt launch), reps launches each after a warm-up."""
     w = synth.WORKLOADS["opt-175b"]
     H, D, h = w.heads, w.head_dim, w.hidden
