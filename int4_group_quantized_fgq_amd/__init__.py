@@ -57,7 +57,14 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     if not os.path.exists(path):
         raise RuntimeError("libfgq.so is not built (%s); run __graft_entry__.build() or "
                            "python int4_group_quantized_fgq_amd/build.py" % path)
-    lib = ctypes.CDLL(path)
+    lib = declare(ctypes.CDLL(path))
+    _lib = lib
+    return lib
+
+
+def declare(lib: ctypes.CDLL) -> ctypes.CDLL:
+    """Set the argument and result types of every entry point on a loaded
+    copy of the library."""
     vp, i32, i64, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
     kvp = ctypes.POINTER(fgq_kv_cache)
     sig = {
@@ -85,7 +92,6 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
         f = getattr(lib, name)
         f.argtypes = args
         f.restype = res
-    _lib = lib
     return lib
 
 
